@@ -1,0 +1,456 @@
+"""Seeded synthetic inputs for paged-attention decode.
+
+This module builds host-side input tensors only: queries, paged K/V caches in
+the packed/plain/transposed layouts, block tables, context lengths, dequant
+scales and sink logits.  It holds none of the attention arithmetic; both the
+GPU path and the CPU oracle consume what it produces.
+
+Shapes follow the problem statement of the FlyDSL paged-attention decode pages
+(aiter PR #4332 "Add paged-attention Tile kernel", host wrapper fragments;
+aiter PR #6617 "Extend packed D256 PA decode pipe", summary):
+
+* query ``[rows, Hq, D]`` with ``rows = num_seqs * query_len`` (BF16/FP16);
+* packed K ``[pages, Hkv, D/x, page, x]`` with ``x = 16 / elem_bytes``;
+* plain V ``[pages, Hkv, D, page]``; transposed V ``[pages, Hkv, page/x, D, x]``;
+* int32 ``block_tables [num_seqs, table_stride]`` and ``context_lens [num_seqs]``;
+* FP32 scales: one per tensor, or per token ``[pages, Hkv, page]``;
+* FP32 sink logits ``[Hq]``.
+
+Quantisation to FP8 e4m3fn uses torch's round-to-nearest-even cast after
+clamping to +-448 (the format's largest finite value).  BF16 rounding is
+torch's round-to-nearest-even.
+
+Positions that no query row can see (tail slots of a sequence's last page,
+slots before a sliding window, pages that are never referenced) are filled
+with poison when ``poison=True``: FP8 byte 0x7F and BF16 0x7FC0 (both NaN),
+and per-token scales of 1e30.  A correct decode never lets them reach the
+output.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+FP8_MAX = 448.0
+FP8_POISON = 0x7F
+BF16_POISON = 0x7FC0
+SCALE_POISON = 1.0e30
+
+KV_FP8 = "fp8"
+KV_BF16 = "bf16"
+SCALE_NONE = "none"
+SCALE_TENSOR = "tensor"
+SCALE_TOKEN = "token"
+
+
+@dataclasses.dataclass
+class Problem:
+    num_seqs: int
+    query_len: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    num_pages: int
+    table_stride: int
+    q_dtype: str = "bf16"  # "bf16" | "fp16"
+    kv_dtype: str = KV_FP8  # "fp8" | "bf16"
+    v_transposed: bool = False
+    scale_mode: str = SCALE_TENSOR  # "none" | "tensor" | "token"
+    causal: bool = True
+    sliding_window: int = 0
+    has_sinks: bool = False
+    token_table: bool = False
+    softmax_scale: float = 0.0  # <= 0 means 1/sqrt(head_dim)
+
+    @property
+    def rows(self) -> int:
+        return self.num_seqs * self.query_len
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def scale(self) -> float:
+        return self.softmax_scale if self.softmax_scale > 0 else 1.0 / math.sqrt(self.head_dim)
+
+
+@dataclasses.dataclass
+class Inputs:
+    problem: Problem
+    q: torch.Tensor  # [rows, Hq, D] bf16/fp16
+    k_cache: torch.Tensor  # uint8 (fp8) or bf16, packed layout
+    v_cache: torch.Tensor  # uint8 (fp8) or bf16, plain or transposed layout
+    block_tables: torch.Tensor  # int32 [num_seqs, table_stride]
+    context_lens: torch.Tensor  # int32 [num_seqs]
+    k_scale: Optional[torch.Tensor]  # float32 [1] or [pages, Hkv, page]
+    v_scale: Optional[torch.Tensor]
+    sinks: Optional[torch.Tensor]  # float32 [Hq]
+    name: str = ""
+
+
+def _streams(seed: int, n: int):
+    return [np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence(seed).spawn(n)]
+
+
+def config_seed(config_id: int) -> int:
+    return 0x5EED0000 + config_id
+
+
+def to_bf16(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+
+
+def to_fp8_bytes(x: torch.Tensor) -> torch.Tensor:
+    """float32 tensor -> uint8 e4m3fn codes (RNE, saturating at +-448)."""
+    return x.clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def visible_span(L: int, query_len: int, window: int, causal: bool):
+    """Token range [lo, hi) that at least one query row of a sequence can see."""
+    if L <= 0:
+        return 0, 0
+    last = L - 1
+    first_pos = L - query_len if causal else L - 1
+    if window > 0:
+        lo = max(0, first_pos - window + 1)
+    else:
+        lo = 0
+    return lo, last + 1
+
+
+def _layout_k(kl: torch.Tensor, elem_bytes: int) -> torch.Tensor:
+    """[P, H, page, D] -> packed [P, H, D/x, page, x]."""
+    P, H, page, D = kl.shape
+    x = 16 // elem_bytes
+    return kl.reshape(P, H, page, D // x, x).permute(0, 1, 3, 2, 4).contiguous()
+
+
+def _layout_v(vl: torch.Tensor, elem_bytes: int, transposed: bool) -> torch.Tensor:
+    """[P, H, page, D] -> plain [P, H, D, page] or transposed [P, H, page/x, D, x]."""
+    P, H, page, D = vl.shape
+    if not transposed:
+        return vl.permute(0, 1, 3, 2).contiguous()
+    x = 16 // elem_bytes
+    return vl.reshape(P, H, page // x, x, D).permute(0, 1, 2, 4, 3).contiguous()
+
+
+def build_dense(
+    prob: Problem,
+    context_lens: np.ndarray,
+    block_tables: np.ndarray,
+    seed: int,
+    fill: str = "visible",
+    poison: bool = True,
+    kv_amplitude: float = 1.0,
+    name: str = "",
+) -> Inputs:
+    """Dense (block-table) workload.
+
+    ``fill``: "visible" gives real data only to pages holding visible tokens,
+    "context" to every page a sequence references up to its length.
+    """
+    rq, rkv, rs = _streams(seed, 3)
+    P, H, page, D = prob.num_pages, prob.num_kv_heads, prob.page_size, prob.head_dim
+    fp8 = prob.kv_dtype == KV_FP8
+    q = rq.standard_normal((prob.rows, prob.num_q_heads, D), dtype=np.float32)
+    qt = to_bf16(q) if prob.q_dtype == "bf16" else torch.from_numpy(q).to(torch.float16)
+
+    # Which (physical page) holds real data, and which slots of it.
+    real_pages = []
+    valid_lo = np.zeros(P, np.int64)  # first slot with real data (per page)
+    valid_hi = np.zeros(P, np.int64)  # one past last slot with real data
+    for s in range(prob.num_seqs):
+        L = int(min(max(int(context_lens[s]), 0), prob.table_stride * page))
+        lo, hi = visible_span(L, prob.query_len, prob.sliding_window, prob.causal)
+        if fill == "context":
+            lo = 0 if L > 0 else 0
+        if hi <= lo:
+            continue
+        for j in range(lo // page, (hi + page - 1) // page):
+            pid = int(block_tables[s, j])
+            real_pages.append(pid)
+            valid_lo[pid] = max(lo - j * page, 0)
+            valid_hi[pid] = min(hi - j * page, page)
+    real_pages = np.asarray(real_pages, dtype=np.int64)
+    nreal = len(real_pages)
+
+    vals_k = torch.from_numpy(rkv.standard_normal((nreal, H, page, D), dtype=np.float32)) * kv_amplitude
+    vals_v = torch.from_numpy(rkv.standard_normal((nreal, H, page, D), dtype=np.float32)) * kv_amplitude
+
+    k_scale = v_scale = None
+    if fp8:
+        if prob.scale_mode == SCALE_TOKEN:
+            ks_real = vals_k.abs().amax(dim=3) / FP8_MAX  # [nreal, H, page]
+            vs_real = vals_v.abs().amax(dim=3) / FP8_MAX
+            ks_real = torch.where(ks_real == 0, torch.ones_like(ks_real), ks_real)
+            vs_real = torch.where(vs_real == 0, torch.ones_like(vs_real), vs_real)
+            qk = to_fp8_bytes(vals_k / ks_real[..., None])
+            qv = to_fp8_bytes(vals_v / vs_real[..., None])
+            k_scale = torch.full((P, H, page), SCALE_POISON if poison else 1.0, dtype=torch.float32)
+            v_scale = torch.full((P, H, page), SCALE_POISON if poison else 1.0, dtype=torch.float32)
+            if nreal:
+                k_scale[torch.from_numpy(real_pages)] = ks_real
+                v_scale[torch.from_numpy(real_pages)] = vs_real
+        elif prob.scale_mode == SCALE_TENSOR:
+            ka = float(vals_k.abs().max()) if nreal else 0.0
+            va = float(vals_v.abs().max()) if nreal else 0.0
+            ks = ka / FP8_MAX if ka > 0 else 1.0
+            vs = va / FP8_MAX if va > 0 else 1.0
+            qk = to_fp8_bytes(vals_k / ks)
+            qv = to_fp8_bytes(vals_v / vs)
+            k_scale = torch.tensor([ks], dtype=torch.float32)
+            v_scale = torch.tensor([vs], dtype=torch.float32)
+        else:
+            raise ValueError("FP8 caches need a scale mode")
+        kl = torch.full((P, H, page, D), FP8_POISON if poison else 0, dtype=torch.uint8)
+        vl = torch.full((P, H, page, D), FP8_POISON if poison else 0, dtype=torch.uint8)
+        elem = 1
+    else:
+        qk = vals_k.to(torch.bfloat16).view(torch.int16)
+        qv = vals_v.to(torch.bfloat16).view(torch.int16)
+        pv = np.int16(BF16_POISON).item() if poison else 0
+        kl = torch.full((P, H, page, D), pv, dtype=torch.int16)
+        vl = torch.full((P, H, page, D), pv, dtype=torch.int16)
+        elem = 2
+    if nreal:
+        idx = torch.from_numpy(real_pages)
+        kl[idx] = qk
+        vl[idx] = qv
+        if poison:
+            # Slots of a real page outside the visible span become poison again.
+            pz = kl.new_full((D,), FP8_POISON if fp8 else np.int16(BF16_POISON).item())
+            for pid in real_pages.tolist():
+                lo_s, hi_s = int(valid_lo[pid]), int(valid_hi[pid])
+                if lo_s > 0:
+                    kl[pid, :, :lo_s] = pz
+                    vl[pid, :, :lo_s] = pz
+                    if k_scale is not None and k_scale.numel() > 1:
+                        k_scale[pid, :, :lo_s] = SCALE_POISON
+                        v_scale[pid, :, :lo_s] = SCALE_POISON
+                if hi_s < page:
+                    kl[pid, :, hi_s:] = pz
+                    vl[pid, :, hi_s:] = pz
+                    if k_scale is not None and k_scale.numel() > 1:
+                        k_scale[pid, :, hi_s:] = SCALE_POISON
+                        v_scale[pid, :, hi_s:] = SCALE_POISON
+    kc = _layout_k(kl, elem)
+    vc = _layout_v(vl, elem, prob.v_transposed)
+    if not fp8:
+        kc = kc.view(torch.bfloat16)
+        vc = vc.view(torch.bfloat16)
+    sinks = None
+    if prob.has_sinks:
+        sinks = torch.from_numpy(rs.standard_normal(prob.num_q_heads, dtype=np.float32))
+    return Inputs(
+        problem=prob,
+        q=qt.contiguous(),
+        k_cache=kc,
+        v_cache=vc,
+        block_tables=torch.from_numpy(np.ascontiguousarray(block_tables, dtype=np.int32)),
+        context_lens=torch.from_numpy(np.ascontiguousarray(context_lens, dtype=np.int32)),
+        k_scale=k_scale,
+        v_scale=v_scale,
+        sinks=sinks,
+        name=name,
+    )
+
+
+def disjoint_tables(rng: np.random.Generator, lens_pages: np.ndarray, num_pages: int, stride: int) -> np.ndarray:
+    """Give each sequence a disjoint slice of a random page permutation; fill
+    entries past a sequence's extent with other sequences' page ids (stale)."""
+    perm = rng.permutation(num_pages).astype(np.int32)
+    bt = np.empty((len(lens_pages), stride), np.int32)
+    off = 0
+    for s, n in enumerate(lens_pages):
+        n = int(n)
+        bt[s, :n] = perm[off : off + n]
+        off += n
+        if n < stride:
+            bt[s, n:] = rng.choice(perm, size=stride - n) if num_pages > 0 else 0
+    return bt
+
+
+def make_dense_case(
+    seed: int,
+    context_lens,
+    query_len: int = 1,
+    num_q_heads: int = 8,
+    num_kv_heads: int = 1,
+    head_dim: int = 128,
+    page_size: int = 16,
+    kv_dtype: str = KV_FP8,
+    q_dtype: str = "bf16",
+    v_transposed: bool = False,
+    scale_mode: str = SCALE_TENSOR,
+    sliding_window: int = 0,
+    has_sinks: bool = False,
+    causal: bool = True,
+    extra_pages: int = 3,
+    table_slack: int = 2,
+    poison: bool = True,
+    fill: str = "visible",
+    kv_amplitude: float = 1.0,
+    name: str = "",
+) -> Inputs:
+    """A general dense case; used by the parity matrix."""
+    lens = np.asarray(context_lens, dtype=np.int64)
+    rng = _streams(seed ^ 0xB10C, 1)[0]
+    lens_pages = (lens + page_size - 1) // page_size
+    num_pages = int(lens_pages.sum()) + extra_pages
+    stride = int(max(1, lens_pages.max(initial=0) + table_slack))
+    bt = disjoint_tables(rng, lens_pages, num_pages, stride)
+    prob = Problem(
+        num_seqs=len(lens), query_len=query_len, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+        head_dim=head_dim, page_size=page_size, num_pages=num_pages, table_stride=stride,
+        q_dtype=q_dtype, kv_dtype=kv_dtype, v_transposed=v_transposed,
+        scale_mode=scale_mode if kv_dtype == KV_FP8 else SCALE_NONE, causal=causal,
+        sliding_window=sliding_window, has_sinks=has_sinks,
+    )
+    return build_dense(prob, lens.astype(np.int32), bt, seed, fill=fill, poison=poison,
+                       kv_amplitude=kv_amplitude, name=name)
+
+
+# ----------------------------------------------------------------------------
+# The five named workloads.
+# ----------------------------------------------------------------------------
+
+def config_tiny(v_transposed: bool = False, poison: bool = True) -> Inputs:
+    """C1: batch 2, Hq 8 / Hkv 1, D 128, QL 1, page 16, lengths 37 and 100,
+    tables a permutation of 16 pages, FP8 per-tensor amax/448, one partition."""
+    seed = config_seed(1)
+    rng = _streams(seed ^ 0xB10C, 1)[0]
+    bt = rng.permutation(16).astype(np.int32).reshape(2, 8)
+    prob = Problem(num_seqs=2, query_len=1, num_q_heads=8, num_kv_heads=1, head_dim=128, page_size=16,
+                   num_pages=16, table_stride=8, v_transposed=v_transposed, scale_mode=SCALE_TENSOR)
+    return build_dense(prob, np.array([37, 100], np.int32), bt, seed, fill="context", poison=poison, name="tiny")
+
+
+def config_long_d256(poison: bool = True, window: int = 8193) -> Inputs:
+    """C3: batch 4, Hkv 2, GQA 8, QL 4 causal, D 256, page 64, context 131072,
+    packed K, transposed V, per-tensor scales, window 8193."""
+    seed = config_seed(3)
+    rng = _streams(seed ^ 0xB10C, 1)[0]
+    L = 131072
+    pages_per = L // 64
+    num_pages = 4 * pages_per
+    bt = rng.permutation(num_pages).astype(np.int32).reshape(4, pages_per)
+    prob = Problem(num_seqs=4, query_len=4, num_q_heads=16, num_kv_heads=2, head_dim=256, page_size=64,
+                   num_pages=num_pages, table_stride=pages_per, v_transposed=True, scale_mode=SCALE_TENSOR,
+                   sliding_window=window)
+    return build_dense(prob, np.full(4, L, np.int32), bt, seed, fill="visible", poison=poison, name="long_d256")
+
+
+def dense_mtp4_lengths(rng: np.random.Generator, n: int = 32) -> np.ndarray:
+    return rng.integers(16384, 32768, size=n, endpoint=True).astype(np.int32)
+
+
+def config_dense_mtp4(kv_dtype: str = KV_FP8, poison: bool = True, num_seqs: int = 32) -> Inputs:
+    """C4: batch 32, Hq 16 / Hkv 1, D 128, QL 4 causal, page 128, lengths
+    uniform in [16384, 32768]; FP8 with per-token scales, or BF16 unscaled."""
+    seed = config_seed(4)
+    rng = _streams(seed ^ 0xB10C, 2)
+    lens = dense_mtp4_lengths(rng[1], 32)[:num_seqs]
+    lens_pages = (lens.astype(np.int64) + 127) // 128
+    num_pages = int(lens_pages.sum())
+    stride = 256
+    bt = disjoint_tables(rng[0], lens_pages, num_pages, stride)
+    prob = Problem(num_seqs=num_seqs, query_len=4, num_q_heads=16, num_kv_heads=1, head_dim=128, page_size=128,
+                   num_pages=num_pages, table_stride=stride, kv_dtype=kv_dtype,
+                   scale_mode=SCALE_TOKEN if kv_dtype == KV_FP8 else SCALE_NONE)
+    return build_dense(prob, lens, bt, seed, fill="context", poison=poison, name=f"dense_mtp4_{kv_dtype}")
+
+
+def ragged_lengths(rng: np.random.Generator, n: int = 128) -> np.ndarray:
+    u = rng.uniform(0.0, math.log(65537.0), size=n)
+    L = np.floor(np.exp(u)).astype(np.int64) - 1
+    L = np.clip(L, 0, 65536)
+    L[:8] = 0
+    L[8:16] = 1
+    rng.shuffle(L)
+    return L.astype(np.int32)
+
+
+def config_ragged(poison: bool = True) -> Inputs:
+    """C5: 128 sequences, lengths log-uniform in [0, 65536] with 8 empty and 8
+    of length 1, Hkv 4 / GQA 4, D 128, QL 1, page 16, FP8 per-token scales,
+    window 257, sink logits ~N(0,1)."""
+    seed = config_seed(5)
+    rng = _streams(seed ^ 0xB10C, 2)
+    lens = ragged_lengths(rng[1], 128)
+    lens_pages = (lens.astype(np.int64) + 15) // 16
+    num_pages = int(lens_pages.sum())
+    stride = int(max(1, lens_pages.max()))
+    bt = disjoint_tables(rng[0], lens_pages, num_pages, stride)
+    prob = Problem(num_seqs=128, query_len=1, num_q_heads=16, num_kv_heads=4, head_dim=128, page_size=16,
+                   num_pages=num_pages, table_stride=stride, scale_mode=SCALE_TOKEN, sliding_window=257,
+                   has_sinks=True)
+    return build_dense(prob, lens, bt, seed, fill="visible", poison=poison, name="ragged")
+
+
+def config_sparse(num_rows: int = 64, selected: int = 2048, pool_pages: int = 4096) -> Inputs:
+    """C2: 64 rows, Hq 16 / Hkv 1, D 128, page 16 FP8 with per-token scales;
+    each row attends `selected` distinct token slots drawn uniformly from a
+    65536-token pool.  ``block_tables[r][j]`` holds a physical token slot
+    (page * 16 + offset), ascending; ``context_lens[r]`` is the count."""
+    seed = config_seed(2)
+    rq, rkv, rsel = _streams(seed, 3)
+    page, H, D = 16, 1, 128
+    P = pool_pages
+    perm = rsel.permutation(P).astype(np.int64)
+    bt = np.empty((num_rows, selected), np.int32)
+    for r in range(num_rows):
+        logical = rsel.choice(P * page, size=selected, replace=False)
+        phys = perm[logical // page] * page + logical % page
+        bt[r] = np.sort(phys).astype(np.int32)
+    q = rq.standard_normal((num_rows, 16, D), dtype=np.float32)
+    vals_k = torch.from_numpy(rkv.standard_normal((P, H, page, D), dtype=np.float32))
+    vals_v = torch.from_numpy(rkv.standard_normal((P, H, page, D), dtype=np.float32))
+    ks = vals_k.abs().amax(dim=3) / FP8_MAX
+    vs = vals_v.abs().amax(dim=3) / FP8_MAX
+    ks = torch.where(ks == 0, torch.ones_like(ks), ks)
+    vs = torch.where(vs == 0, torch.ones_like(vs), vs)
+    kl = to_fp8_bytes(vals_k / ks[..., None])
+    vl = to_fp8_bytes(vals_v / vs[..., None])
+    prob = Problem(num_seqs=num_rows, query_len=1, num_q_heads=16, num_kv_heads=1, head_dim=D, page_size=page,
+                   num_pages=P, table_stride=selected, scale_mode=SCALE_TOKEN, token_table=True)
+    return Inputs(
+        problem=prob, q=to_bf16(q), k_cache=_layout_k(kl, 1), v_cache=_layout_v(vl, 1, False),
+        block_tables=torch.from_numpy(bt), context_lens=torch.full((num_rows,), selected, dtype=torch.int32),
+        k_scale=ks.contiguous(), v_scale=vs.contiguous(), sinks=None, name="sparse",
+    )
+
+
+CONFIGS = {
+    "tiny": config_tiny,
+    "sparse": config_sparse,
+    "long_d256": config_long_d256,
+    "dense_mtp4_fp8": lambda **kw: config_dense_mtp4(KV_FP8, **kw),
+    "dense_mtp4_bf16": lambda **kw: config_dense_mtp4(KV_BF16, **kw),
+    "ragged": config_ragged,
+}
+
+
+def kv_bytes_visible(inp: Inputs) -> int:
+    """Algorithmic KV bytes of one call: K + V (+ per-token K and V scales) of
+    the visible-token union of every (sequence, KV head), counted once."""
+    p = inp.problem
+    elem = 1 if p.kv_dtype == KV_FP8 else 2
+    per_tok = 2 * p.head_dim * elem + (8 if (p.kv_dtype == KV_FP8 and p.scale_mode == SCALE_TOKEN) else 0)
+    lens = inp.context_lens.numpy().astype(np.int64)
+    tot = 0
+    for s in range(p.num_seqs):
+        if p.token_table:
+            n = int(min(max(lens[s], 0), p.table_stride))
+        else:
+            L = int(min(max(lens[s], 0), p.table_stride * p.page_size))
+            lo, hi = visible_span(L, p.query_len, p.sliding_window, p.causal)
+            n = hi - lo
+        tot += n
+    return tot * p.num_kv_heads * per_tok

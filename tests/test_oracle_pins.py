@@ -1,0 +1,253 @@
+"""Pins of the CPU oracle against things other than itself.
+
+* the FP8/BF16/FP16 decoders against the format definitions (OCP OFP8 spec
+  values in tests/golden) and against torch/numpy library conversions;
+* the full computation against a dense brute force with an explicit mask in
+  long double, over lengths/query lengths/windows/pages/layouts/scales/sinks;
+* invariants of attention (one visible token, uniform keys, window 1, split
+  and merge, page permutation, sinks, power-of-two V scales, zero queries);
+* a cross-check of the unmasked single-row case against torch's float64
+  scaled_dot_product_attention.
+"""
+
+from __future__ import annotations
+
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import bruteforce
+from oracle import oracle as O
+from paged_attention_decode_plan_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_fp8():
+    rows = []
+    with open(os.path.join(GOLDEN, "fp8_e4m3fn_spec.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            c, v = line.split()
+            rows.append((int(c, 16), float(v)))
+    return rows
+
+
+def test_fp8_spec_values():
+    for code, val in _golden_fp8():
+        got = O.fp8_value(code)
+        if math.isnan(val):
+            assert math.isnan(got), hex(code)
+        else:
+            assert got == val and math.copysign(1, got) == math.copysign(1, val), hex(code)
+
+
+def test_fp8_all_codes_match_torch():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([O.fp8_value(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all()
+    assert (got[~nan] == ref[~nan]).all()
+    # monotone over positive finite codes, symmetric in sign
+    pos = got[:0x7F]
+    assert (np.diff(pos) > 0).all()
+    assert (got[0x80:0xFF] == -got[:0x7F]).all()
+
+
+def test_bf16_fp16_decoders():
+    bits = np.arange(0, 65536, 7, dtype=np.uint32)
+    ref16 = bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    got16 = np.array([O.fp16_value(int(b)) for b in bits])
+    nan = np.isnan(ref16)
+    assert (np.isnan(got16) == nan).all() and (got16[~nan] == ref16[~nan]).all()
+    refb = torch.from_numpy(bits.astype(np.uint16).view(np.int16)).view(torch.bfloat16).double().numpy()
+    gotb = np.array([O.bf16_value(int(b)) for b in bits])
+    nanb = np.isnan(refb)
+    assert (np.isnan(gotb) == nanb).all() and (gotb[~nanb] == refb[~nanb]).all()
+
+
+LENS = [0, 1, 2, 15, 16, 17, 33]
+
+
+@pytest.mark.parametrize("page", [16, 64])
+@pytest.mark.parametrize("vt", [False, True])
+@pytest.mark.parametrize("scale", ["tensor", "token", "bf16"])
+@pytest.mark.parametrize("sinks", [False, True])
+def test_oracle_vs_bruteforce(page, vt, scale, sinks):
+    kv = "bf16" if scale == "bf16" else "fp8"
+    sm = "none" if scale == "bf16" else scale
+    seed = hash((page, vt, scale, sinks)) & 0xFFFF
+    for ql, w in itertools.product([1, 2, 3, 4], [0, 1, 2, 17]):
+        inp = W.make_dense_case(seed + 97 * ql + w, LENS, query_len=ql, num_q_heads=4, num_kv_heads=2, head_dim=32
+                                if kv == "fp8" else 16, page_size=page, kv_dtype=kv, v_transposed=vt, scale_mode=sm,
+                                sliding_window=w, has_sinks=sinks, poison=False, fill="context")
+        got = O.attend(inp, nthreads=2).astype(np.float64)
+        ref = bruteforce.attend(inp)
+        np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-7, err_msg=f"ql={ql} w={w}")
+
+
+def test_oracle_vs_bruteforce_token_table():
+    inp = W.config_sparse(num_rows=3, selected=40, pool_pages=8)
+    got = O.attend(inp).astype(np.float64)
+    ref = bruteforce.attend(inp)
+    np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-7)
+
+
+def test_oracle_ignores_poison():
+    """Poisoned (NaN) tails, windows and stale table entries never reach it."""
+    inp = W.make_dense_case(5, [17, 40, 3], query_len=2, num_q_heads=4, num_kv_heads=1, head_dim=32, page_size=16,
+                            scale_mode="token", sliding_window=9, poison=True)
+    out = O.attend(inp)
+    assert np.isfinite(out).all()
+    clean = W.make_dense_case(5, [17, 40, 3], query_len=2, num_q_heads=4, num_kv_heads=1, head_dim=32, page_size=16,
+                              scale_mode="token", sliding_window=9, poison=False)
+    np.testing.assert_array_equal(out, O.attend(clean))
+
+
+def _case(**kw):
+    base = dict(query_len=1, num_q_heads=4, num_kv_heads=2, head_dim=32, page_size=16, poison=False, fill="context")
+    base.update(kw)
+    return base
+
+
+def _logical_v(inp, s, t, g):
+    K, V = bruteforce.logical_caches(inp)
+    p = inp.problem
+    page = int(inp.block_tables[s, t // p.page_size])
+    return V[page, g, t % p.page_size]
+
+
+def test_invariant_single_token():
+    inp = W.make_dense_case(11, [1, 1], **_case(scale_mode="token"))
+    out = O.attend(inp)
+    for s in range(2):
+        for h in range(4):
+            np.testing.assert_array_equal(out[s, h], _logical_v(inp, s, 0, h // 2).astype(np.float32))
+
+
+def test_invariant_window_one():
+    ql = 3
+    inp = W.make_dense_case(12, [9, 40], **_case(query_len=ql, sliding_window=1, scale_mode="tensor"))
+    out = O.attend(inp)
+    for s, L in enumerate([9, 40]):
+        for i in range(ql):
+            pos = L - ql + i
+            for h in range(4):
+                np.testing.assert_array_equal(out[s * ql + i, h], _logical_v(inp, s, pos, h // 2).astype(np.float32))
+
+
+def test_invariant_uniform_keys_and_zero_query():
+    inp = W.make_dense_case(13, [37, 5], **_case(scale_mode="tensor"))
+    inp.q.zero_()
+    out = O.attend(inp)
+    assert np.isfinite(out).all()
+    for s, L in enumerate([37, 5]):
+        for h in range(4):
+            mean = np.mean([_logical_v(inp, s, t, h // 2) for t in range(L)], axis=0)
+            np.testing.assert_allclose(out[s, h], mean, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("window", [0, 7])
+def test_invariant_split_merge(window):
+    inp = W.make_dense_case(14, [70], **_case(query_len=2, sliding_window=window, scale_mode="token", has_sinks=True))
+    full = O.attend(inp)
+    rng = np.random.default_rng(0)
+    for i in range(2):
+        for h in range(4):
+            cuts = np.sort(rng.choice(np.arange(1, 70), size=3, replace=False))
+            bounds = [0, *cuts.tolist(), 70]
+            parts = [O.partial(inp, 0, i, h, a, b) for a, b in zip(bounds[:-1], bounds[1:])]
+            merged = O.merge([p[0] for p in parts], [p[1] for p in parts], np.stack([p[2] for p in parts]),
+                             sink=float(inp.sinks[h]))
+            np.testing.assert_allclose(merged, full[i, h], rtol=1e-6, atol=1e-7)
+
+
+def test_invariant_page_permutation():
+    inp = W.make_dense_case(15, [50, 33], **_case(page_size=16, scale_mode="token", extra_pages=0))
+    out = O.attend(inp)
+    p = inp.problem
+    perm = torch.randperm(p.num_pages, generator=torch.Generator().manual_seed(3))
+    inv = torch.argsort(perm)
+    # new physical page j holds old page perm[j]; tables map old id -> new id
+    inp.k_cache = inp.k_cache[perm].contiguous()
+    inp.v_cache = inp.v_cache[perm].contiguous()
+    inp.k_scale = inp.k_scale[perm].contiguous()
+    inp.v_scale = inp.v_scale[perm].contiguous()
+    inp.block_tables = inv[inp.block_tables.long()].to(torch.int32)
+    np.testing.assert_array_equal(O.attend(inp), out)
+
+
+def test_invariant_sinks():
+    base = W.make_dense_case(16, [30], **_case(scale_mode="tensor", has_sinks=True))
+    nos = W.make_dense_case(16, [30], **_case(scale_mode="tensor", has_sinks=False))
+    out_nos = O.attend(nos).astype(np.float64)
+    base.sinks.fill_(-1e30)
+    np.testing.assert_allclose(O.attend(base), out_nos, rtol=1e-6, atol=1e-7)
+    for sink in [-3.0, 0.5, 4.0, 40.0]:
+        base.sinks.fill_(sink)
+        out = O.attend(base).astype(np.float64)
+        for h in range(4):
+            m, l, _ = O.partial(nos, 0, 0, h, 0, 1 << 30)
+            M = max(m, sink)
+            frac = l * math.exp(m - M) / (l * math.exp(m - M) + math.exp(sink - M))
+            np.testing.assert_allclose(out[0, h], out_nos[0, h] * frac, rtol=1e-5, atol=1e-7)
+
+
+def test_invariant_pow2_vscale():
+    inp = W.make_dense_case(17, [45, 3], **_case(scale_mode="token"))
+    out = O.attend(inp)
+    inp.v_scale.mul_(8.0)
+    np.testing.assert_array_equal(O.attend(inp), out * 8.0)
+
+
+def test_empty_and_negative_rows_are_zero():
+    inp = W.make_dense_case(18, [0, 2, 1], **_case(query_len=4))
+    out = O.attend(inp)
+    assert (out[0:4] == 0).all()  # empty sequence
+    assert (out[4:6] == 0).all()  # L=2, rows 0,1 have pos < 0
+    assert (out[6:8] != 0).any(axis=-1).all()
+    assert (out[8:11] == 0).all() and (out[11] != 0).any()
+
+
+def test_single_row_matches_sdpa():
+    inp = W.make_dense_case(19, [77, 20], **_case(kv_dtype="bf16", scale_mode="none", num_q_heads=2, num_kv_heads=2))
+    out = O.attend(inp).astype(np.float64)
+    K, V = bruteforce.logical_caches(inp)
+    for s, L in enumerate([77, 20]):
+        pages = inp.block_tables[s, np.arange(L) // 16].long().numpy()
+        offs = np.arange(L) % 16
+        for h in range(2):
+            k = torch.from_numpy(K[pages, h, offs])[None, None]
+            v = torch.from_numpy(V[pages, h, offs])[None, None]
+            q = inp.q[s, h].double()[None, None, None]
+            ref = torch.nn.functional.scaled_dot_product_attention(q, k, v)[0, 0, 0].numpy()
+            np.testing.assert_allclose(out[s, h], ref, rtol=1e-6, atol=1e-7)
+
+
+def test_planted_token_digits():
+    """A token whose key dominates by a wide margin: the output is exactly its
+    (integer-valued) V row."""
+    inp = W.make_dense_case(20, [100], **_case(kv_dtype="bf16", scale_mode="none", num_q_heads=1, num_kv_heads=1,
+                                               head_dim=16))
+    p = inp.problem
+    target = 57
+    qv = torch.ones(16)
+    inp.q[0, 0] = qv.to(torch.bfloat16)
+    x = 8
+    kc = inp.k_cache.view(p.num_pages, 1, 16 // x, 16, x)
+    vc = inp.v_cache.view(p.num_pages, 1, 16, 16)
+    for t in range(100):
+        page = int(inp.block_tables[0, t // 16])
+        slot = t % 16
+        val = 64.0 if t == target else -64.0
+        kc[page, 0, :, slot, :] = val
+        vc[page, 0, :, slot] = torch.tensor([(page + d) % 16 for d in range(16)], dtype=torch.bfloat16)
+    out = O.attend(inp)
+    page = int(inp.block_tables[0, target // 16])
+    np.testing.assert_array_equal(out[0, 0], np.array([(page + d) % 16 for d in range(16)], np.float32))
