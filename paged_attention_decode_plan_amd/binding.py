@@ -1,0 +1,196 @@
+"""ctypes binding of libpa.so (argument marshalling only).
+
+Every step of the decode runs in the library's HIP kernels; this module only
+checks tensors, fills the C structs and maps status codes to exceptions
+(PA_ERR_INVALID / PA_ERR_WORKSPACE -> ValueError, PA_ERR_UNSUPPORTED ->
+NotImplementedError, PA_ERR_DEVICE -> RuntimeError).  Importing it fails
+loudly when libpa.so has not been built; there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpa.so")
+
+PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_DEVICE = range(5)
+PA_BF16, PA_FP16, PA_FP8_E4M3FN = range(3)
+PA_V_PLAIN, PA_V_TRANSPOSED = range(2)
+PA_SCALE_NONE, PA_SCALE_PER_TENSOR, PA_SCALE_PER_TOKEN = range(3)
+
+EXPORTS = ["pa_plan", "pa_plan_sizes", "pa_plan_info", "pa_plan_work", "pa_plan_free", "pa_decode", "pa_reduce",
+           "pa_last_error"]
+
+
+class PaProblem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_seqs", "query_len", "num_q_heads", "num_kv_heads", "head_dim", "page_size", "num_pages",
+        "table_stride", "q_dtype", "kv_dtype", "v_layout", "scale_mode", "causal", "sliding_window",
+        "has_sinks", "token_table")] + [("softmax_scale", ctypes.c_float)]
+
+
+class PaPlanOpts(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("cu_count", "max_partitions", "partition_tokens", "stage_limit")]
+
+
+class PaPlanInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_items", "num_slots", "num_reduce", "rows_per_group", "row_groups", "max_parts", "total_tiles",
+        "cu_count")]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libpa.so; raises ImportError if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libpa.so not found at {path}: build it with paged_attention_decode_plan_amd.build")
+    L = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    L.pa_plan.restype = ctypes.c_int
+    L.pa_plan.argtypes = [ctypes.POINTER(PaProblem), vp, ctypes.POINTER(PaPlanOpts), ctypes.POINTER(vp)]
+    L.pa_plan_sizes.restype = ctypes.c_int
+    L.pa_plan_sizes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+    L.pa_plan_info.restype = ctypes.c_int
+    L.pa_plan_info.argtypes = [vp, ctypes.POINTER(PaPlanInfo)]
+    L.pa_plan_work.restype = ctypes.c_int
+    L.pa_plan_work.argtypes = [vp, vp, ctypes.c_int32]
+    L.pa_plan_free.restype = None
+    L.pa_plan_free.argtypes = [vp]
+    L.pa_decode.restype = ctypes.c_int
+    L.pa_decode.argtypes = [vp] * 13
+    L.pa_reduce.restype = ctypes.c_int
+    L.pa_reduce.argtypes = [vp] * 6
+    L.pa_last_error.restype = ctypes.c_char_p
+    L.pa_last_error.argtypes = []
+    _lib = L
+    return L
+
+
+def _check(st: int):
+    if st == PA_OK:
+        return
+    msg = load_library().pa_last_error().decode()
+    if st == PA_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    if st in (PA_ERR_INVALID, PA_ERR_WORKSPACE):
+        raise ValueError(msg)
+    raise RuntimeError(f"status {st}: {msg}")
+
+
+def make_problem(num_seqs, query_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages, table_stride,
+                 q_dtype="bf16", kv_dtype="fp8", v_transposed=False, scale_mode="tensor", causal=True,
+                 sliding_window=0, has_sinks=False, token_table=False, softmax_scale=0.0) -> PaProblem:
+    dt = {"bf16": PA_BF16, "fp16": PA_FP16, "fp8": PA_FP8_E4M3FN}
+    sm = {"none": PA_SCALE_NONE, "tensor": PA_SCALE_PER_TENSOR, "token": PA_SCALE_PER_TOKEN}
+    return PaProblem(num_seqs, query_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages, table_stride,
+                     dt[q_dtype], dt[kv_dtype], PA_V_TRANSPOSED if v_transposed else PA_V_PLAIN, sm[scale_mode],
+                     int(causal), int(sliding_window), int(has_sinks), int(token_table), float(softmax_scale))
+
+
+def problem_of(p) -> PaProblem:
+    """PaProblem from any object with the problem's attribute names."""
+    return make_problem(p.num_seqs, p.query_len, p.num_q_heads, p.num_kv_heads, p.head_dim, p.page_size,
+                        p.num_pages, p.table_stride, p.q_dtype, p.kv_dtype, p.v_transposed, p.scale_mode, p.causal,
+                        p.sliding_window, p.has_sinks, p.token_table, p.softmax_scale)
+
+
+class Plan:
+    """Owns a pa_plan_t plus the device metadata and workspace it needs."""
+
+    def __init__(self, problem: PaProblem, context_lens_host, cu_count=0, max_partitions=0, partition_tokens=0,
+                 stage_limit=0):
+        L = load_library()
+        self.problem = problem
+        lens = torch.as_tensor(context_lens_host, dtype=torch.int32).contiguous().cpu()
+        self._lens = lens
+        opts = PaPlanOpts(cu_count, max_partitions, partition_tokens, stage_limit)
+        h = ctypes.c_void_p()
+        _check(L.pa_plan(ctypes.byref(problem), lens.data_ptr() if lens.numel() else None, ctypes.byref(opts),
+                         ctypes.byref(h)))
+        self.handle = h
+        mb, wb = ctypes.c_size_t(), ctypes.c_size_t()
+        _check(L.pa_plan_sizes(h, ctypes.byref(mb), ctypes.byref(wb)))
+        self.meta_bytes, self.workspace_bytes = mb.value, wb.value
+        self.meta = None
+        self.workspace = None
+
+    def info(self) -> PaPlanInfo:
+        inf = PaPlanInfo()
+        _check(load_library().pa_plan_info(self.handle, ctypes.byref(inf)))
+        return inf
+
+    def work(self) -> torch.Tensor:
+        n = self.info().num_items
+        out = torch.zeros((max(n, 1), 8), dtype=torch.int32)
+        _check(load_library().pa_plan_work(self.handle, out.data_ptr(), n))
+        return out[:n]
+
+    def allocate(self, device="cuda"):
+        """Device metadata and workspace (16-byte aligned torch allocations)."""
+        self.meta = torch.empty(max(self.meta_bytes, 16), dtype=torch.uint8, device=device)
+        self.workspace = torch.empty(max(self.workspace_bytes // 4, 4), dtype=torch.float32, device=device)
+        return self
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            try:
+                load_library().pa_plan_free(h)
+            except Exception:
+                pass
+            self.handle = None
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def pa_decode(plan: Plan, out, q, k_cache, v_cache, block_tables, context_lens, k_scale=None, v_scale=None,
+              sinks=None, stream=None):
+    for name, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_tables", block_tables), ("context_lens", context_lens)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale), ("sinks", sinks)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda):
+            raise ValueError(f"{name} must be a contiguous float32 device tensor")
+    if plan.meta is None:
+        plan.allocate(q.device)
+    _check(load_library().pa_decode(plan.handle, _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(block_tables), _ptr(context_lens), _ptr(k_scale), _ptr(v_scale),
+                                    _ptr(sinks), _ptr(plan.meta), _ptr(plan.workspace), _stream_ptr(stream)))
+
+
+def pa_reduce(plan: Plan, out, sinks=None, stream=None):
+    _check(load_library().pa_reduce(plan.handle, _ptr(out), _ptr(sinks), _ptr(plan.meta), _ptr(plan.workspace),
+                                    _stream_ptr(stream)))
+
+
+def attend(plan: Plan, out, q, k_cache, v_cache, block_tables, context_lens, k_scale=None, v_scale=None, sinks=None,
+           stream=None):
+    """pa_decode followed by pa_reduce on the same stream."""
+    pa_decode(plan, out, q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale, sinks, stream)
+    pa_reduce(plan, out, sinks, stream)
+    return out

@@ -1,0 +1,68 @@
+// Internal plan representation shared by the host planner and the launch code.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "pa_decode.h"
+
+namespace pa {
+
+constexpr int kTileTokens = 128;   // tokens per pipeline tile (a multiple of every page size)
+constexpr int kMaxRowsPerItem = 64; // query rows one work item carries (4 row tiles of 16)
+constexpr int kStageCap = 1024;     // page / slot ids staged in LDS per work item
+constexpr int kMaxPartitions = 256; // static per-(sequence, KV head) bound
+
+// One workgroup's work: 8 int32, uploaded verbatim.
+struct WorkItem {
+  int32_t seq, kvh, rg;           // sequence, KV head, row group
+  int32_t tile_begin, tile_end;   // tiles relative to the page-aligned span start; -1: to the end
+  int32_t slot;                   // partial slot; -1: direct output
+  int32_t part, nparts;
+};
+static_assert(sizeof(WorkItem) == 32, "work item is 32 bytes");
+
+// One multi-partition (sequence, KV head, row group): its partials occupy
+// slots [first_slot, first_slot + nparts) in partition order.
+struct ReduceItem {
+  int32_t seq, kvh, rg, first_slot, nparts, pad0, pad1, pad2;
+};
+static_assert(sizeof(ReduceItem) == 32, "reduce item is 32 bytes");
+
+// Layout of meta_dev: [WorkItem x num_items][ReduceItem x num_reduce]
+struct Plan {
+  pa_problem prob;
+  pa_plan_opts opts;
+  int cu_count = 0;
+  int rows_total = 0;      // QL * G
+  int rows_per_group = 0;  // min(64, rows_total)
+  int row_groups = 0;
+  int nrt = 0;             // 16-row tiles per work item (1, 2 or 4)
+  int stage_limit = kStageCap;
+  int max_parts = 0;
+  int total_tiles = 0;
+  float scale_log2 = 0.f;  // softmax_scale * log2(e)
+  std::vector<WorkItem> items;
+  std::vector<ReduceItem> reduce;
+  int num_slots = 0;
+  // the meta_dev this plan was last uploaded to (re-upload on change)
+  mutable void* uploaded_to = nullptr;
+  std::vector<uint8_t> meta_host;  // serialised metadata
+
+  size_t meta_bytes() const { return meta_host.size(); }
+  // partial state per slot: m[rows_per_group], l[rows_per_group], o[rows_per_group][D]
+  size_t slot_floats() const { return (size_t)rows_per_group * (2 + prob.head_dim); }
+  size_t workspace_bytes() const { return (size_t)num_slots * slot_floats() * sizeof(float); }
+};
+
+// thread-local error message helper (defined in pa_plan.cpp)
+pa_status set_error(pa_status st, const std::string& msg);
+pa_status validate_problem(const pa_problem* p);
+
+}  // namespace pa
+
+struct pa_plan_s {
+  pa::Plan plan;
+};

@@ -1,0 +1,248 @@
+// Host work planner and the host-only part of the C ABI.
+//
+// Split-KV planning follows the FlyDSL decode pages: partitions per
+// (sequence, KV head) are bounded by the device compute-unit count and a
+// static 256-partition limit (aiter PR #4332, the commit that defaults the
+// per-sequence plan limit to the CU count); the partition range is the tile
+// union a sliding window and multi-token (MTP) rows can see (aiter PR #6617,
+// "Size staged page IDs from the visible sliding-window tile union"); empty
+// sequences clear their rows (aiter PR #7079, "Partition merges").
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <queue>
+#include <string>
+#include <vector>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+static thread_local std::string g_last_error;
+
+pa_status set_error(pa_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+pa_status validate_problem(const pa_problem* p) {
+  if (!p) return set_error(PA_ERR_INVALID, "problem is NULL");
+  if (p->num_seqs < 0) return set_error(PA_ERR_INVALID, "num_seqs < 0");
+  if (p->query_len < 1) return set_error(PA_ERR_INVALID, "query_len < 1");
+  if (p->num_q_heads < 1 || p->num_kv_heads < 1) return set_error(PA_ERR_INVALID, "head counts must be >= 1");
+  if (p->num_q_heads % p->num_kv_heads != 0)
+    return set_error(PA_ERR_INVALID, "num_q_heads must be a multiple of num_kv_heads");
+  if (p->head_dim < 1 || p->page_size < 1) return set_error(PA_ERR_INVALID, "head_dim and page_size must be >= 1");
+  if (p->num_pages < 0) return set_error(PA_ERR_INVALID, "num_pages < 0");
+  if (p->num_seqs > 0 && p->table_stride < 1) return set_error(PA_ERR_INVALID, "table_stride < 1");
+  if (p->sliding_window < 0) return set_error(PA_ERR_INVALID, "sliding_window < 0");
+  if (p->q_dtype != PA_BF16 && p->q_dtype != PA_FP16) return set_error(PA_ERR_INVALID, "q_dtype must be BF16 or FP16");
+  if (p->kv_dtype != PA_FP8_E4M3FN && p->kv_dtype != PA_BF16)
+    return set_error(PA_ERR_INVALID, "kv_dtype must be FP8_E4M3FN or BF16");
+  if (p->v_layout != PA_V_PLAIN && p->v_layout != PA_V_TRANSPOSED) return set_error(PA_ERR_INVALID, "bad v_layout");
+  if (p->scale_mode < PA_SCALE_NONE || p->scale_mode > PA_SCALE_PER_TOKEN)
+    return set_error(PA_ERR_INVALID, "bad scale_mode");
+  if ((p->causal | p->has_sinks | p->token_table) & ~1) return set_error(PA_ERR_INVALID, "flags must be 0 or 1");
+  double cache_elems = (double)p->num_pages * p->num_kv_heads * p->page_size * p->head_dim;
+  if (cache_elems > (double)(1ull << 40)) return set_error(PA_ERR_INVALID, "cache larger than 2^40 elements");
+  // Valid but not implemented here.
+  if (p->head_dim != 128 && p->head_dim != 256)
+    return set_error(PA_ERR_UNSUPPORTED, "head_dim must be 128 or 256");
+  if (p->page_size != 16 && p->page_size != 64 && p->page_size != 128)
+    return set_error(PA_ERR_UNSUPPORTED, "page_size must be 16, 64 or 128");
+  if (p->kv_dtype == PA_FP8_E4M3FN && p->scale_mode == PA_SCALE_NONE)
+    return set_error(PA_ERR_UNSUPPORTED, "FP8 caches need a per-tensor or per-token scale");
+  if (p->kv_dtype == PA_BF16 && p->scale_mode != PA_SCALE_NONE)
+    return set_error(PA_ERR_UNSUPPORTED, "BF16 caches take no dequant scale");
+  if (p->kv_dtype == PA_BF16 && p->head_dim != 128)
+    return set_error(PA_ERR_UNSUPPORTED, "BF16 caches support head_dim 128 only");
+  if (p->kv_dtype == PA_BF16 && p->q_dtype != PA_BF16)
+    return set_error(PA_ERR_UNSUPPORTED, "BF16 caches need BF16 queries");
+  if (p->token_table && (p->sliding_window > 0 || p->query_len != 1))
+    return set_error(PA_ERR_UNSUPPORTED, "token tables need query_len 1 and no sliding window");
+  return PA_OK;
+}
+
+// Workgroups of the decode kernel that stay resident on one CU together.
+static int resident_per_cu(const pa_problem& p, int nrt) {
+  if (nrt >= 4 || p.head_dim > 128) return 1;
+  return 2;
+}
+
+static inline long ceil_div(long a, long b) { return (a + b - 1) / b; }
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" pa_status pa_plan(const pa_problem* problem, const int32_t* context_lens_host, const pa_plan_opts* opts,
+                             pa_plan_t** out) {
+  if (!out) return set_error(PA_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  pa_status st = validate_problem(problem);
+  if (st != PA_OK) return st;
+  if (problem->num_seqs > 0 && !context_lens_host) return set_error(PA_ERR_INVALID, "context_lens_host is NULL");
+  pa_plan_opts o{};
+  if (opts) o = *opts;
+  if (o.cu_count < 0 || o.max_partitions < 0 || o.partition_tokens < 0 || o.stage_limit < 0)
+    return set_error(PA_ERR_INVALID, "plan options must be >= 0");
+  const pa_problem& p = *problem;
+
+  int cu = o.cu_count;
+  if (cu == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) {
+      (void)hipGetLastError();
+      return set_error(PA_ERR_DEVICE, "cu_count is 0 and the device CU count could not be queried");
+    }
+  }
+
+  auto* handle = new pa_plan_s();
+  Plan& P = handle->plan;
+  P.prob = p;
+  if (P.prob.softmax_scale <= 0.f) P.prob.softmax_scale = 1.0f / std::sqrt((float)p.head_dim);
+  P.opts = o;
+  P.cu_count = cu;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  P.rows_total = p.query_len * G;
+  P.rows_per_group = std::min(P.rows_total, kMaxRowsPerItem);
+  P.row_groups = (int)ceil_div(P.rows_total, kMaxRowsPerItem);
+  int rt = (int)ceil_div(P.rows_per_group, 16);
+  P.nrt = rt <= 1 ? 1 : (rt <= 2 ? 2 : 4);
+  P.stage_limit = o.stage_limit > 0 ? std::min(o.stage_limit, kStageCap) : kStageCap;
+  P.scale_log2 = P.prob.softmax_scale * 1.4426950408889634f;
+  int maxp = o.max_partitions > 0 ? o.max_partitions : cu;
+  maxp = std::max(1, std::min(maxp, kMaxPartitions));
+
+  // Tiles of each sequence's visible span (the same for all its KV heads).
+  const long cap = p.token_table ? (long)p.table_stride : (long)p.table_stride * p.page_size;
+  std::vector<int> seq_tiles(p.num_seqs, 0);
+  for (int s = 0; s < p.num_seqs; ++s) {
+    long L = std::min<long>(std::max<long>(context_lens_host[s], 0), cap);
+    long lo = 0, hi = L;
+    if (!p.token_table && L > 0 && p.sliding_window > 0) {
+      long first_pos = p.causal ? L - p.query_len : L - 1;
+      lo = std::max<long>(0, first_pos - p.sliding_window + 1);
+    }
+    long t0 = p.token_table ? 0 : (lo / p.page_size) * p.page_size;
+    seq_tiles[s] = hi > lo ? (int)ceil_div(hi - t0, kTileTokens) : 0;
+  }
+
+  // Units: (sequence, KV head, row group).  Choose partition counts.
+  const int units_per_seq = p.num_kv_heads * P.row_groups;
+  const long nunits = (long)p.num_seqs * units_per_seq;
+  std::vector<int> parts(p.num_seqs, 1);  // identical for every unit of a sequence
+  const int occ = resident_per_cu(p, P.nrt);
+  const long slots_budget = std::max<long>((long)cu * occ, nunits);
+  if (o.partition_tokens > 0) {
+    int tiles_per_part = (int)ceil_div(o.partition_tokens, kTileTokens);
+    for (int s = 0; s < p.num_seqs; ++s)
+      parts[s] = std::max(1, std::min<int>({(int)ceil_div(seq_tiles[s], tiles_per_part), maxp,
+                                            std::max(seq_tiles[s], 1)}));
+  } else {
+    // Greedy: split the sequence with the longest work item while the shorter
+    // makespan outweighs the added partial traffic and the budget allows.
+    const double elem = p.kv_dtype == PA_FP8_E4M3FN ? 1.0 : 2.0;
+    const double tile_bytes = kTileTokens * (2.0 * p.head_dim * elem + 8.0);
+    const double partial_bytes = P.rows_per_group * (p.head_dim + 2.0) * 4.0;
+    const double cost_per_item = 2.0 * partial_bytes / (tile_bytes * cu);  // in tile-times
+    long items = nunits;
+    using E = std::pair<long, int>;  // (current longest item tiles, seq)
+    std::priority_queue<E> pq;
+    for (int s = 0; s < p.num_seqs; ++s)
+      if (seq_tiles[s] > 1) pq.push({seq_tiles[s], s});
+    while (!pq.empty()) {
+      auto [len, s] = pq.top();
+      pq.pop();
+      int np = parts[s] + 1;
+      if (np > maxp || np > seq_tiles[s]) continue;
+      if (items + units_per_seq > slots_budget) break;
+      long newlen = ceil_div(seq_tiles[s], np);
+      // the first split of a sequence also creates its first partial slots
+      double added = cost_per_item * units_per_seq * (parts[s] == 1 ? 2 : 1);
+      if ((double)(len - newlen) < added) continue;
+      parts[s] = np;
+      items += units_per_seq;
+      pq.push({ceil_div(seq_tiles[s], np), s});
+    }
+  }
+
+  // Emit items: slots are contiguous per unit, in partition order.
+  int slot = 0;
+  P.max_parts = 1;
+  P.total_tiles = 0;
+  for (int s = 0; s < p.num_seqs; ++s) {
+    int np = parts[s];
+    int nt = seq_tiles[s];
+    P.max_parts = std::max(P.max_parts, np);
+    for (int g = 0; g < p.num_kv_heads; ++g)
+      for (int rg = 0; rg < P.row_groups; ++rg) {
+        int first = np > 1 ? slot : -1;
+        if (np > 1) {
+          P.reduce.push_back(ReduceItem{s, g, rg, slot, np, 0, 0, 0});
+          slot += np;
+        }
+        for (int part = 0; part < np; ++part) {
+          // balanced split: the first (nt % np) parts get one extra tile
+          int base = nt / np, extra = nt % np;
+          int b = part * base + std::min(part, extra);
+          int e = b + base + (part < extra ? 1 : 0);
+          WorkItem w{s, g, rg, b, part == np - 1 ? -1 : e, np > 1 ? first + part : -1, part, np};
+          P.items.push_back(w);
+          P.total_tiles += e - b;
+        }
+      }
+  }
+  P.num_slots = slot;
+  // Longest items first; ties keep (sequence, head, part) order.
+  std::stable_sort(P.items.begin(), P.items.end(), [&](const WorkItem& a, const WorkItem& b) {
+    auto len = [&](const WorkItem& w) {
+      int e = w.tile_end >= 0 ? w.tile_end : seq_tiles[w.seq];
+      return e - w.tile_begin;
+    };
+    return len(a) > len(b);
+  });
+  P.meta_host.resize(P.items.size() * sizeof(WorkItem) + P.reduce.size() * sizeof(ReduceItem));
+  if (!P.items.empty()) std::memcpy(P.meta_host.data(), P.items.data(), P.items.size() * sizeof(WorkItem));
+  if (!P.reduce.empty())
+    std::memcpy(P.meta_host.data() + P.items.size() * sizeof(WorkItem), P.reduce.data(),
+                P.reduce.size() * sizeof(ReduceItem));
+  *out = handle;
+  return PA_OK;
+}
+
+extern "C" pa_status pa_plan_sizes(const pa_plan_t* plan, size_t* meta_bytes, size_t* workspace_bytes) {
+  if (!plan) return set_error(PA_ERR_INVALID, "plan is NULL");
+  if (meta_bytes) *meta_bytes = plan->plan.meta_bytes();
+  if (workspace_bytes) *workspace_bytes = plan->plan.workspace_bytes();
+  return PA_OK;
+}
+
+extern "C" pa_status pa_plan_info(const pa_plan_t* plan, pa_plan_info_t* info) {
+  if (!plan || !info) return set_error(PA_ERR_INVALID, "plan or info is NULL");
+  const Plan& P = plan->plan;
+  info->num_items = (int32_t)P.items.size();
+  info->num_slots = P.num_slots;
+  info->num_reduce = (int32_t)P.reduce.size();
+  info->rows_per_group = P.rows_per_group;
+  info->row_groups = P.row_groups;
+  info->max_parts = P.max_parts;
+  info->total_tiles = P.total_tiles;
+  info->cu_count = P.cu_count;
+  return PA_OK;
+}
+
+extern "C" pa_status pa_plan_work(const pa_plan_t* plan, int32_t* out, int32_t n_items_capacity) {
+  if (!plan || (!out && n_items_capacity > 0)) return set_error(PA_ERR_INVALID, "plan or out is NULL");
+  const Plan& P = plan->plan;
+  if (n_items_capacity < (int32_t)P.items.size()) return set_error(PA_ERR_INVALID, "capacity too small");
+  if (!P.items.empty()) std::memcpy(out, P.items.data(), P.items.size() * sizeof(WorkItem));
+  return PA_OK;
+}
+
+extern "C" void pa_plan_free(pa_plan_t* plan) { delete plan; }
+
+extern "C" const char* pa_last_error(void) { return g_last_error.c_str(); }

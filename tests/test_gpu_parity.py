@@ -1,0 +1,183 @@
+"""GPU parity: libpa.so against the CPU oracle, element by element, within
+atol = rtol = 0.005 (the FP32-reference tolerance of the FlyDSL D256 decode
+page, aiter PR #6617, Validation), on seeded inputs with NaN-poisoned output
+and workspace before every call."""
+
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import announce, compare, run, to_device
+from oracle import oracle as O
+from paged_attention_decode_plan_amd import binding as B
+from paged_attention_decode_plan_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+LENS = [0, 1, 2, 15, 17, 150, 300, 1000]
+
+
+def _parity(inp, sel=None, **plan_kw):
+    got, plan = run(inp, **plan_kw)
+    if sel is None:
+        ref = O.attend(inp)
+        return compare(got, ref, inp.name), plan
+    ref = O.attend(inp, sel=sel)
+    g = np.stack([got[r, h] for r, h in sel])
+    return compare(g, ref, inp.name), plan
+
+
+@pytest.mark.parametrize("vt", [False, True])
+@pytest.mark.parametrize("maxp", [1, 0])
+def test_tiny(vt, maxp):
+    inp = W.config_tiny(v_transposed=vt)
+    announce(f"tiny vt={vt} maxp={maxp}")
+    err, plan = _parity(inp, max_partitions=maxp)
+    if maxp == 1:
+        assert plan.info().num_slots == 0
+
+
+@pytest.mark.parametrize("page", [16, 64, 128])
+@pytest.mark.parametrize("vt", [False, True])
+@pytest.mark.parametrize("scale", ["tensor", "token"])
+def test_matrix_fp8(page, vt, scale):
+    seed = 1000 + page * 4 + vt * 2 + (scale == "token")
+    for ql, window, sinks, (hq, hkv) in itertools.product([1, 2, 3, 4], [0, 1, 17, 257], [False, True],
+                                                          [(8, 1), (16, 1), (8, 2)]):
+        if (ql + window + hq) % 3 != seed % 3 and not (ql == 4 and hq == 16):
+            continue  # a deterministic third of the product, plus every 64-row case
+        inp = W.make_dense_case(seed, LENS, query_len=ql, num_q_heads=hq, num_kv_heads=hkv, head_dim=128,
+                                page_size=page, v_transposed=vt, scale_mode=scale, sliding_window=window,
+                                has_sinks=sinks)
+        announce(f"fp8 page={page} vt={vt} scale={scale} ql={ql} w={window} sinks={sinks} hq={hq} hkv={hkv}")
+        _parity(inp, cu_count=64)
+        seed += 1
+
+
+@pytest.mark.parametrize("page", [16, 64, 128])
+def test_matrix_bf16(page):
+    seed = 2000 + page
+    for ql, window, sinks, vt, (hq, hkv) in itertools.product([1, 4], [0, 17], [False, True], [False, True],
+                                                              [(8, 1), (16, 1)]):
+        inp = W.make_dense_case(seed, LENS, query_len=ql, num_q_heads=hq, num_kv_heads=hkv, head_dim=128,
+                                page_size=page, kv_dtype="bf16", v_transposed=vt, sliding_window=window,
+                                has_sinks=sinks)
+        announce(f"bf16 page={page} vt={vt} ql={ql} w={window} sinks={sinks} hq={hq}")
+        _parity(inp, cu_count=64)
+        seed += 1
+
+
+@pytest.mark.parametrize("ql,hq,hkv", [(1, 8, 1), (4, 16, 2), (4, 16, 1)])
+def test_d256(ql, hq, hkv):
+    seed = 3000 + ql * 10 + hq
+    for page, vt, window in itertools.product([16, 64], [False, True], [0, 257]):
+        inp = W.make_dense_case(seed, LENS, query_len=ql, num_q_heads=hq, num_kv_heads=hkv, head_dim=256,
+                                page_size=page, v_transposed=vt, scale_mode="tensor", sliding_window=window)
+        announce(f"d256 page={page} vt={vt} ql={ql} w={window} hq={hq} hkv={hkv}")
+        _parity(inp, cu_count=64)
+        seed += 1
+
+
+def test_fp16_queries():
+    inp = W.make_dense_case(41, LENS, query_len=2, num_q_heads=16, num_kv_heads=2, head_dim=128, page_size=16,
+                            q_dtype="fp16", scale_mode="token", sliding_window=17, has_sinks=True)
+    announce("fp16 queries")
+    _parity(inp, cu_count=64)
+
+
+def test_many_partitions_and_fixed_partition_length():
+    inp = W.make_dense_case(42, [5000, 7000, 3], query_len=4, num_q_heads=16, num_kv_heads=1, page_size=64,
+                            scale_mode="token")
+    announce("partition_tokens=128")
+    _, plan = _parity(inp, cu_count=256, partition_tokens=128)
+    assert plan.info().max_parts > 20
+    announce("max_partitions=2")
+    _parity(inp, cu_count=256, max_partitions=2)
+
+
+def test_staging_fallback():
+    """Page ids past a tiny staging bound come straight from the block table."""
+    inp = W.make_dense_case(43, [3000, 900], query_len=1, num_q_heads=8, num_kv_heads=1, page_size=16,
+                            scale_mode="tensor")
+    for lim in [1, 7, 64]:
+        announce(f"stage_limit={lim}")
+        _parity(inp, cu_count=4, max_partitions=1, stage_limit=lim)
+
+
+def test_device_context_longer_than_plan():
+    """A plan made for shorter lengths still covers the device lengths."""
+    inp = W.make_dense_case(44, [2000, 700], query_len=2, num_q_heads=8, num_kv_heads=1, page_size=16,
+                            scale_mode="token", sliding_window=0)
+    announce("plan lengths below device lengths")
+    got, _ = run(inp, lens_for_plan=[1000, 300], cu_count=16)
+    compare(got, O.attend(inp), "longer device context")
+
+
+def test_run_to_run_bit_exact():
+    inp = W.config_ragged()
+    dev = to_device(inp)
+    announce("ragged twice")
+    a, plan = run(inp, dev=dev)
+    b, _ = run(inp, dev=dev, plan=plan)
+    assert np.array_equal(a, b)
+
+
+def test_planted_token_digits_exact():
+    """One token's key dominates; the output must equal its integer V digits
+    exactly, wherever the token sits (page / tile / partition / staged-bound /
+    window edges)."""
+    page, L = 16, 700
+    for ql, window, target_off in [(1, 0, None), (4, 0, None), (1, 33, None)]:
+        base = W.make_dense_case(45, [L], query_len=ql, num_q_heads=4, num_kv_heads=1, head_dim=128, page_size=page,
+                                 scale_mode="tensor", sliding_window=window, poison=True, fill="context")
+        p = base.problem
+        base.k_scale.fill_(1.0)
+        base.v_scale.fill_(1.0)
+        base.q.fill_(1.0)
+        kc = base.k_cache.view(p.num_pages, 1, 128 // 16, page, 16)
+        vc = base.v_cache.view(p.num_pages, 1, 128, page)
+        lo = max(0, L - ql - window + 1) if window else 0
+        targets = sorted({lo, lo + 1, 127, 128, 129, 255, 256, 511, 512, L - ql, L - ql - 1} & set(range(lo, L - ql + 1)))
+        for tgt in targets:
+            pos_code = 0x58  # +16.0 in e4m3fn
+            neg_code = 0xD8  # -16.0
+            for t in range(lo, L):
+                pid = int(base.block_tables[0, t // page])
+                kc[pid, 0, :, t % page, :] = pos_code if t == tgt else neg_code
+                digits = torch.tensor([((pid * 7 + d) % 16) for d in range(128)], dtype=torch.float32)
+                vc[pid, 0, :, t % page] = W.to_fp8_bytes(digits)
+            announce(f"planted ql={ql} w={window} target={tgt}")
+            for kw in [dict(cu_count=4, max_partitions=1, stage_limit=5), dict(cu_count=256, partition_tokens=128)]:
+                got, _ = run(base, **kw)
+                pid = int(base.block_tables[0, tgt // page])
+                want = np.array([((pid * 7 + d) % 16) for d in range(128)], np.float32)
+                for i in range(ql):
+                    pos = L - ql + i
+                    vis_lo = max(0, pos - window + 1) if window else 0
+                    if vis_lo <= tgt <= pos:
+                        for h in range(4):
+                            assert np.array_equal(got[i, h], want), (tgt, i, h, kw)
+
+
+def test_uniform_attention_census():
+    """K = 0 and one-hot V rows: out[d] * |visible| counts visible t with t mod D == d."""
+    L, page = 333, 64
+    inp = W.make_dense_case(46, [L], query_len=1, num_q_heads=8, num_kv_heads=1, head_dim=128, page_size=page,
+                            kv_dtype="bf16", poison=True, fill="context")
+    p = inp.problem
+    kc = inp.k_cache.view(torch.int16).view(p.num_pages, 1, 16, page, 8)
+    vc = inp.v_cache.view(torch.int16).view(p.num_pages, 1, 128, page)
+    one = torch.tensor([1.0], dtype=torch.bfloat16).view(torch.int16)[0]
+    for t in range(L):
+        pid = int(inp.block_tables[0, t // page])
+        kc[pid, 0, :, t % page, :] = 0
+        vc[pid, 0, :, t % page] = 0
+        vc[pid, 0, t % 128, t % page] = one
+    announce("census")
+    got, _ = run(inp, cu_count=16, partition_tokens=128)
+    counts = np.bincount(np.arange(L) % 128, minlength=128)
+    np.testing.assert_allclose(got[0] * L, np.broadcast_to(counts, (8, 128)), rtol=0.004, atol=0.0)
