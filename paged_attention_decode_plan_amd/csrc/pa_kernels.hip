@@ -14,8 +14,10 @@
 // gfx950 design (not the pages' FlyDSL tiling):
 //  * a workgroup of 4 waves owns one work item = (sequence, KV head, row
 //    group of up to 64 query rows, a contiguous range of 128-token tiles);
-//  * K/V pages of a tile are staged in LDS through registers with 16-byte
-//    coalesced loads, double-buffered so tile j+1 loads while tile j computes;
+//  * dense caches: K/V pages of a tile go straight from HBM into an LDS ring
+//    (global_load_lds_dwordx4, 16 bytes per lane, coalesced page-head blocks),
+//    2 or 3 tiles deep, so later tiles stream in while one tile computes;
+//    token-table (sparse) caches gather through registers instead;
 //  * each wave takes 32 tokens of every tile for all of the item's query rows,
 //    so every K/V byte is read from LDS and converted exactly once; the four
 //    waves keep independent online-softmax states merged once at the end;
@@ -24,7 +26,7 @@
 //    registers (v_cvt_scalef32_pk_f16_fp8), BF16 queries are scaled by a
 //    per-row power of two into FP16 (exact), probabilities go from the QK
 //    accumulator to the PV operand in registers (the QK rows are read in the
-//    token order PV contracts), FP16 P keeps 11 significant bits;
+//    token order PV contracts) as RNE FP16 with 11 significant bits;
 //  * row max/sum across the 4 lane groups of a row use v_permlane16/32_swap;
 //  * rescaling of the accumulator is lazy: only when a row maximum grows by
 //    more than 2^8, or the per-token V-scale reference leaves its band.
@@ -42,14 +44,24 @@ namespace pa {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int TT = kTileTokens;  // 128 tokens per tile
-constexpr int NWAVES = 4;
-constexpr int NTHREADS = 64 * NWAVES;
-constexpr float TAU = 8.0f;  // lazy-rescale band (log2 units): probabilities stay <= 2^8
+// Waves per workgroup: 16-row items use 4 waves (and two workgroups share a
+// CU); 32- and 64-row items use 8 waves so that each SIMD runs two waves of
+// one workgroup.  Every wave owns one 16-row tile of the item.
+template <int NRT>
+struct Waves {
+  static constexpr int NW = NRT >= 2 ? 8 : 4;
+  static constexpr int NT = 64 * NW;
+};
+constexpr float TAU = 12.0f;     // probabilities are taken against a reference max: p <= 2^12
+constexpr float VS_BAND = 8.0f;  // per-token V scales against a reference: vs/ref <= 8
+constexpr float LOG2E = 1.4426950408889634f;
 
 struct KernelArgs {
   void* out;
@@ -65,7 +77,7 @@ struct KernelArgs {
   float* workspace;
   long long page_stride;  // bytes between physical pages (Hkv * D * page * elem)
   long long head_stride;  // bytes between KV heads of a page (D * page * elem)
-  int QL, Hq, G, page_size, table_stride, window, causal;
+  int QL, Hq, Hkv, G, page_size, table_stride, window, causal;
   int v_transposed, scale_mode, q_fp16, has_sinks, rows_total, rows_per_group, stage_limit;
   float scale_log2;  // softmax_scale * log2(e)
 };
@@ -99,55 +111,82 @@ __device__ __forceinline__ half8 fp8x8_to_half8(u32x2 v) {
 }
 
 // Token position of a K row inside the LDS K tile (16-byte rows).  The XOR
-// spreads the QK operand reads of one lane group over all bank quads.
+// spreads the QK operand reads of one lane group over more bank quads; it is
+// its own inverse.
 __device__ __forceinline__ int kswz(int t) { return t ^ (((t >> 3) & 1) << 2); }
 
-// Row d of a staged V tile holds TT tokens; with FP8 its 8-byte units are
-// stored at unit ^ (d & 15), with BF16 its 16-byte units likewise, so the 16
-// lanes reading one unit column from 16 rows hit distinct banks.
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
-template <int D, bool FP8>
+// s_waitcnt lgkmcnt(0) with the other counters unconstrained.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
+
+template <int D, bool FP8, int NT>
 struct Tile {
   static constexpr int E = FP8 ? 1 : 2;      // bytes per KV element
   static constexpr int X = 16 / E;           // elements per 16-byte chunk
-  static constexpr int KBYTES = D * TT * E;  // K tile bytes
-  static constexpr int VROW = TT * E;        // bytes per V row
+  static constexpr int KBYTES = D * TT * E;  // K tile: [D/X chunks][TT tokens][16 B]
+  static constexpr int VROW = TT * E;        // V tile: [D rows][TT tokens]
   static constexpr int VBYTES = D * VROW;
+  static constexpr int VUPR = VROW / 16;     // 16-byte units per V row
   static constexpr int SBYTES = FP8 ? 2 * TT * 4 : 0;  // per-token k and v scales
   static constexpr int STAGE = KBYTES + VBYTES + SBYTES;
-  static constexpr int KUNITS = KBYTES / 16;
-  static constexpr int VUNITS = VBYTES / 16;
-  static constexpr int KPT = KUNITS / NTHREADS;  // 16-byte K units per thread per tile
-  static constexpr int VPT = VUNITS / NTHREADS;
-  static constexpr int NM = D / 32;               // MFMA k-steps over the head dim
-  static constexpr int NDT = D / 16;              // 16-wide d tiles of O
+  static constexpr int KPT = KBYTES / 16 / NT;  // 16-byte K units per thread per tile
+  static constexpr int VPT = VBYTES / 16 / NT;
+  static constexpr int NM = D / 32;  // MFMA k-steps over the head dim
+  static constexpr int NDT = D / 16; // 16-wide d tiles of O
 };
 
-template <int D, bool FP8, int NRT>
-struct Smem {
-  static constexpr int STAGES = 2;
-  static constexpr int STAGE = Tile<D, FP8>::STAGE;
-  static constexpr int MERGE = 2 * NRT * 16 * (D + 4) * 4;  // two O buffers with padded rows
-  static constexpr int MAIN = (STAGES * STAGE > MERGE) ? STAGES * STAGE : MERGE;
-  static constexpr int IDS = kStageCap * 4;
-  static constexpr int STATS = NWAVES * NRT * 16 * 2 * 4 + NWAVES * 4 + NRT * 16 * 4 * 4;
-  static constexpr int TOTAL = MAIN + IDS + STATS;
-};
-
-// Staging registers of one tile for one thread.
-template <int D, bool FP8>
-struct Staged {
-  u32x4 k[Tile<D, FP8>::KPT];
-  u32x4 v[Tile<D, FP8>::VPT];
-  u32x4 s;  // 4 per-token scales (threads 0..63: K scales, 64..127: V scales)
-  uint32_t kmask, vmask;
-  int sdst;
+// Wave roles: a workgroup's 4 waves split an item's rows into WR groups of
+// NRW row tiles and each tile's 128 tokens into WT groups (WR * WT = 4), so
+// that one wave's O accumulator stays at 64 registers: D 128 keeps two row
+// tiles per wave, D 256 one.
+template <int D, int NRT>
+struct Roles {
+  static constexpr int NW = Waves<NRT>::NW;
+  static constexpr int NRW = 1;         // row tiles per wave
+  static constexpr int WR = NRT;        // row groups
+  static constexpr int WT = NW / WR;    // token groups
+  static constexpr int STEPS = 4 / WT;  // 32-token steps per wave per tile
+  static_assert(WR * WT == NW && WT <= 4 && NRW * WR == NRT, "wave roles");
 };
 
 template <int D, bool FP8, int NRT, bool SPARSE>
-__global__ __launch_bounds__(NTHREADS) void pa_decode_kernel(KernelArgs a) {
-  using T = Tile<D, FP8>;
-  using S = Smem<D, FP8, NRT>;
+struct Smem {
+  using R = Roles<D, NRT>;
+  static constexpr int STAGES = (!SPARSE && FP8 && D == 128 && NRT >= 2) ? 4 : 2;
+  static constexpr int STAGE = Tile<D, FP8, Waves<NRT>::NT>::STAGE;
+  static constexpr int MERGE = NRT * 16 * (D + 4) * 4;  // one O buffer with padded rows
+  static constexpr int MAIN = (STAGES * STAGE > MERGE) ? STAGES * STAGE : MERGE;
+  static constexpr int IDS = kStageCap * 4;
+  static constexpr int STATS = (R::WT * NRT * 16 * 2 + R::NW + NRT * 16 * 4 + 4) * 4;
+  static constexpr int TOTAL = MAIN + IDS + STATS;
+};
+
+// Register staging of one tile (token-table path).
+template <int D, bool FP8, int NT>
+struct Staged {
+  u32x4 k[Tile<D, FP8, NT>::KPT];
+  u32x4 v[Tile<D, FP8, NT>::VPT];
+  u32x4 s;
+};
+
+template <int D, bool FP8, int NRT, bool SPARSE>
+__global__ __launch_bounds__(Waves<NRT>::NT) void pa_decode_kernel(KernelArgs a) {
+  constexpr int NTHREADS = Waves<NRT>::NT;
+  constexpr int NWAVES = Waves<NRT>::NW;
+  using T = Tile<D, FP8, NTHREADS>;
+  using S = Smem<D, FP8, NRT, SPARSE>;
+  using R = Roles<D, NRT>;
+  constexpr int NST = S::STAGES;
+  constexpr int NRW = R::NRW;
+  constexpr int NM = T::NM;
+  constexpr int NDT = T::NDT;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* stage_base = smem;
   int32_t* ids = (int32_t*)(smem + S::MAIN);
@@ -158,6 +197,8 @@ __global__ __launch_bounds__(NTHREADS) void pa_decode_kernel(KernelArgs a) {
   const int lane = tid & 63;
   const int c = lane & 15;
   const int g = lane >> 4;
+  const int wr = w % R::WR;  // this wave's row group
+  const int wt = w / R::WR;  // this wave's token group
 
   const WorkItem it = a.items[blockIdx.x];
   const int s = it.seq, kvh = it.kvh, rg = it.rg;
@@ -176,14 +217,14 @@ __global__ __launch_bounds__(NTHREADS) void pa_decode_kernel(KernelArgs a) {
   const int tb = min(it.tile_begin, ntiles);
   const int te = it.tile_end < 0 ? ntiles : min(it.tile_end, ntiles);
 
-  // Rows of this item.
+  // Rows of this item; the wave owns row tiles wr*NRW .. wr*NRW+NRW-1.
   const int rpg = a.rows_per_group;
   const int row0 = rg * kMaxRowsPerItem;
   const int nrows = min(rpg, a.rows_total - row0);
-  int lo_r[NRT], hi_r[NRT];
+  int lo_r[NRW], hi_r[NRW];
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    int r = rt * 16 + c;
+  for (int rt = 0; rt < NRW; ++rt) {
+    int r = (wr * NRW + rt) * 16 + c;
     if (r < nrows) {
       int gr = row0 + r, i = gr / a.G;
       int pos = a.causal ? L - a.QL + i : L - 1;
@@ -194,7 +235,8 @@ __global__ __launch_bounds__(NTHREADS) void pa_decode_kernel(KernelArgs a) {
       hi_r[rt] = 0;
     }
   }
-  // Bounds shared by all rows: a tile inside [lo_max, hi_min] needs no mask.
+  // Bounds shared by all rows of the item: a tile inside [lo_max, hi_min]
+  // needs no mask at all.
   int lo_max, hi_min;
   {
     int i_first = row0 / a.G, i_last = (row0 + nrows - 1) / a.G;
@@ -212,17 +254,15 @@ __global__ __launch_bounds__(NTHREADS) void pa_decode_kernel(KernelArgs a) {
   const int32_t* bt_row = a.block_tables + (long)s * a.table_stride;
   for (int k = tid; k < nstaged; k += NTHREADS) ids[k] = bt_row[id0 + k];
 
-  // ---- query fragments ----
+  // ---- query fragments of the wave's rows ----
   // FP8 caches: d of MFMA step m, lane group g, slot p is 64(m/2)+16g+8(m%2)+p;
   // BF16 caches: 32m+8g+p.  Both read 8 contiguous d per (m, g).
-  constexpr int NM = T::NM;
-  constexpr int NDT = T::NDT;
   using QFrag = typename std::conditional<FP8, half8, bf16x8>::type;
-  QFrag qf[NRT][NM];
-  float crow[NRT];  // log2-domain score scale of the row (incl. query pre-scale)
+  QFrag qf[NRW][NM];
+  float crow[NRW];  // log2-domain score scale of the row (incl. query pre-scale)
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    int r = rt * 16 + c;
+  for (int rt = 0; rt < NRW; ++rt) {
+    int r = (wr * NRW + rt) * 16 + c;
     bool valid = r < nrows;
     int gr = row0 + (valid ? r : 0);
     int i = gr / a.G, hl = gr % a.G;
@@ -235,23 +275,24 @@ __global__ __launch_bounds__(NTHREADS) void pa_decode_kernel(KernelArgs a) {
       raw[m] = valid ? *(const u32x4*)(qrow + d0) : u32x4{0, 0, 0, 0};
     }
     if constexpr (FP8) {
-      float amax = 0.f;
       float qv[NM][8];
+      if (a.q_fp16) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int p = 0; p < 8; ++p)
+            qv[m][p] = (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[m][p >> 1] >> (16 * (p & 1))));
+      } else {
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int p = 0; p < 8; ++p) qv[m][p] = __uint_as_float((raw[m][p >> 1] >> (16 * (p & 1))) << 16);
+      }
+      float amax = 0.f;
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          uint32_t word = raw[m][p >> 1];
-          uint16_t bits = (p & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFF);
-          float f;
-          if (a.q_fp16) {
-            f = (float)__builtin_bit_cast(_Float16, bits);
-          } else {
-            f = __uint_as_float((uint32_t)bits << 16);
-          }
-          qv[m][p] = f;
-          amax = fmaxf(amax, fabsf(f));
-        }
+        for (int p = 0; p < 8; ++p) amax = fmaxf(amax, fabsf(qv[m][p]));
       amax = group_max(amax);
       // BF16 rows are scaled by 2^e so |q| lands in [2^14, 2^15): exact in FP16.
       int e = 0;
@@ -260,7 +301,7 @@ __global__ __launch_bounds__(NTHREADS) void pa_decode_kernel(KernelArgs a) {
         frexpf(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1)
         e = 15 - ex;
       }
-      float mul = ldexpf(1.0f, e);
+      const float mul = ldexpf(1.0f, e);
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -273,381 +314,354 @@ __global__ __launch_bounds__(NTHREADS) void pa_decode_kernel(KernelArgs a) {
     }
   }
   const bool per_token = FP8 && a.scale_mode == PA_SCALE_PER_TOKEN;
-  float vs_ref = 1.0f;  // O holds sum p*v / vs_ref (per-token V scales)
+  float vs_ref = 1.0f;  // O holds sum p*v / vs_ref
   if (FP8 && !per_token) {
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) crow[rt] *= a.k_scale[0];
+    for (int rt = 0; rt < NRW; ++rt) crow[rt] *= a.k_scale[0];
     vs_ref = a.v_scale[0];
   }
   if (per_token) vs_ref = 0.f;
   float inv_ref = per_token ? 0.f : 1.0f;
 
-  // ---- online softmax state (lane holds row rt*16+c) ----
-  float m_ref[NRT], l_part[NRT];
-  f4 o[NRT][NDT];
+  // ---- online softmax state (lane holds row (wr*NRW+rt)*16+c) ----
+  // Probabilities are exp2(score - m_ref) with m_ref a reference maximum set
+  // at a row's first visible token and V scales are taken relative to vs_ref,
+  // so the FP16 PV operand stays <= 2^12 * 8.  A later score more than TAU
+  // above m_ref (or a V scale more than VS_BAND above vs_ref) marks the
+  // attempt as overflowed: the workgroup restarts the item with the larger
+  // references.  O is therefore only ever written by MFMAs in the loop.
+  float m_ref[NRW], m_hi[NRW], l_part[NRW];
+  f4 o[NRW][NDT];
+  float vs_hi = 0.f;
+  bool ovf = false;
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
+  for (int rt = 0; rt < NRW; ++rt) {
     m_ref[rt] = -INFINITY;
-    l_part[rt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[rt][dt] = f4{0.f, 0.f, 0.f, 0.f};
+    m_hi[rt] = -INFINITY;
   }
+  int* restart_flag = (int*)(stats + S::STATS / 4 - 4);
+  if (tid == 0) *restart_flag = 0;
 
   const uint8_t* kbase = a.k_cache + (long long)kvh * a.head_stride;
   const uint8_t* vbase = a.v_cache + (long long)kvh * a.head_stride;
 
   __syncthreads();  // staged ids visible
 
-  // Page id (dense) or token slot (sparse) number j of the item.
-  auto item_id = [&](long j) -> long {
-    return j < nstaged ? (long)ids[j] : (long)bt_row[id0 + j];
-  };
+  // Page id (dense) or token slot (sparse) number j of the item: from the LDS
+  // list, or past the staged bound from the block table.  The two readers are
+  // kept apart so the LDS-only path never emits a generic (flat) load, which
+  // would make every DMA issue wait for all outstanding loads.
+  auto staged_id = [&](long j) -> long { return (long)ids[j]; };
+  auto item_id = [&](long j) -> long { return j < nstaged ? (long)ids[j] : (long)bt_row[id0 + j]; };
 
-  // ---- tile loader: global -> registers ----
-  auto load_tile = [&](int tile, Staged<D, FP8>& st) {
-    const int ts = t0 + tile * TT;          // first token (index) of the tile
-    const long jt = (long)(tile - tb) * ppt;  // first id of the tile within the item
-    if constexpr (!SPARSE) {
-      // K: unit u -> chunk cc = u / TT, token t = u % TT
-      st.kmask = 0;
+  // ---- dense: DMA of one tile into an LDS stage ----
+  // K unit u = tid + k*NTHREADS holds chunk tid/TT + 2k of token kswz(tid%TT);
+  // V unit u holds 16 bytes of row tid/VUPR + k*(NTHREADS/VUPR) at position
+  // tid%VUPR.  So each thread's K units share one page (likewise V), and its
+  // k-th unit sits a constant stride after the first.  Every thread issues
+  // the same number of loads per tile (a page outside the visible span is
+  // replaced by page 0 of the head: those LDS bytes are masked), so a
+  // constant vmcnt tracks the tiles in flight.
+  constexpr int KCH = NTHREADS / TT;       // chunks covered per k step
+  constexpr int VRS = NTHREADS / T::VUPR;  // V rows covered per k step
+  const int k_tok = kswz(tid % TT);
+  const int k_pg = k_tok / ps;
+  const long k_off = ((long)(tid / TT) * ps + k_tok % ps) * 16;
+  const long k_step = (long)KCH * ps * 16;
+  const int v_row = tid / T::VUPR;
+  const int v_tok = ((tid % T::VUPR) ^ (v_row & (T::VUPR - 1))) * T::X;  // first token of the unit
+  const int v_pg = v_tok / ps;
+  const int v_sx = (v_tok % ps) / T::X;
+  const long v_off = a.v_transposed ? ((long)v_sx * D + v_row) * 16 : (long)v_row * ps * T::E + v_sx * 16;
+  const long v_step = a.v_transposed ? (long)VRS * 16 : (long)VRS * ps * T::E;
+  const int s_tok = (lane & 31) * 4;  // scales: wave 0, lanes 0-31 K, 32-63 V
+  const int s_pg = s_tok / ps;
+  const float* s_src0 = (lane >> 5) ? a.v_scale : a.k_scale;
+
+  auto issue_tile_ids = [&](int tile, uint8_t* stg, auto get_id) {
+    const int ts = t0 + tile * TT;
+    const long jt = (long)(tile - tb) * ppt;
+    auto page_ok = [&](int j) {
+      int tok0 = ts + j * ps;
+      return tok0 < hi_u && tok0 + ps > lo_u;
+    };
+    const uint8_t* ksrc = kbase + k_off;
+    if (page_ok(k_pg)) ksrc += get_id(jt + k_pg) * a.page_stride;
+    uint8_t* kdst = stg + (tid - lane) * 16;
 #pragma unroll
-      for (int k = 0; k < T::KPT; ++k) {
-        int u = tid + k * NTHREADS;
-        int cc = u / TT, t = u % TT;
-        int j = t / ps, slot = t % ps;
-        int tok0 = ts + j * ps;
-        bool ok = tok0 < hi_u && tok0 + ps > lo_u;
-        st.k[k] = u32x4{0, 0, 0, 0};
-        if (ok) {
-          long pid = item_id(jt + j);
-          const uint8_t* src = kbase + pid * a.page_stride + ((long)cc * ps + slot) * 16;
-          st.k[k] = *(const u32x4*)src;
-          st.kmask |= 1u << k;
-        }
-      }
-      // V: unit u -> page j, row d, 16-byte unit within the row of the page
-      const int n16 = ps * T::E / 16;  // 16-byte units per (row, page)
-      st.vmask = 0;
+    for (int k = 0; k < T::KPT; ++k)
+      __builtin_amdgcn_global_load_lds((const void*)(ksrc + k * k_step), (lds_void*)(kdst + k * NTHREADS * 16), 16,
+                                       0, 0);
+    const uint8_t* vsrc = vbase + v_off;
+    if (page_ok(v_pg)) vsrc += get_id(jt + v_pg) * a.page_stride;
+    uint8_t* vdst = stg + T::KBYTES + (tid - lane) * 16;
 #pragma unroll
-      for (int k = 0; k < T::VPT; ++k) {
-        int u = tid + k * NTHREADS;
-        int per_page = D * n16;
-        int j = u / per_page, rem = u % per_page;
-        int d, s16;
-        if (a.v_transposed) {
-          s16 = rem / D;
-          d = rem % D;
-        } else {
-          d = rem / n16;
-          s16 = rem % n16;
-        }
-        int tok0 = ts + j * ps;
-        bool ok = tok0 < hi_u && tok0 + ps > lo_u;
-        st.v[k] = u32x4{0, 0, 0, 0};
-        if (ok) {
-          long pid = item_id(jt + j);
-          long off = a.v_transposed ? ((long)s16 * D + d) * 16 : (long)d * ps * T::E + s16 * 16;
-          st.v[k] = *(const u32x4*)(vbase + pid * a.page_stride + off);
-          st.vmask |= 1u << k;
-        }
-      }
-      if (FP8 && per_token && tid < 2 * TT / 4) {
-        int which = tid / (TT / 4);  // 0: K scales, 1: V scales
-        int t = (tid % (TT / 4)) * 4;
-        int j = t / ps, slot = t % ps;
-        int tok0 = ts + j * ps;
-        st.s = u32x4{0, 0, 0, 0};
-        st.sdst = which * TT + t;
-        if (tok0 < hi_u && tok0 + ps > lo_u) {
-          long pid = item_id(jt + j);
-          const float* sc = which ? a.v_scale : a.k_scale;
-          st.s = *(const u32x4*)(sc + (pid * (a.page_stride / (D * ps * T::E)) + kvh) * ps + slot);
-        }
-      }
-    } else {
-      // Sparse: every token has its own physical slot.
-      const int nh = (int)(a.page_stride / a.head_stride);  // KV heads
-      st.kmask = 0;
-#pragma unroll
-      for (int k = 0; k < T::KPT; ++k) {
-        int u = tid + k * NTHREADS;
-        int cc = u / TT, t = u % TT;
-        st.k[k] = u32x4{0, 0, 0, 0};
-        if (ts + t < hi_u) {
-          long S = item_id(jt + t);
-          long pid = S / ps;
-          int slot = (int)(S % ps);
-          st.k[k] = *(const u32x4*)(kbase + pid * a.page_stride + ((long)cc * ps + slot) * 16);
-          st.kmask |= 1u << k;
-        }
-      }
-      // V: unit u -> row d, 16 consecutive tokens (gathered element by element)
-      st.vmask = 0;
-#pragma unroll
-      for (int k = 0; k < T::VPT; ++k) {
-        int u = tid + k * NTHREADS;
-        int upr = TT * T::E / 16;  // units per row
-        int d = u / upr, t0u = (u % upr) * (16 / T::E);
-        uint8_t bytes[16];
-#pragma unroll
-        for (int e = 0; e < 16 / T::E; ++e) {
-          int t = t0u + e;
-          if (ts + t < hi_u) {
-            long S = item_id(jt + t);
-            long pid = S / ps;
-            int slot = (int)(S % ps);
-            long off = a.v_transposed ? ((long)(slot / T::X) * D + d) * 16 + (slot % T::X) * T::E
-                                      : ((long)d * ps + slot) * T::E;
-            const uint8_t* src = vbase + pid * a.page_stride + off;
-#pragma unroll
-            for (int b = 0; b < T::E; ++b) bytes[e * T::E + b] = src[b];
-          } else {
-#pragma unroll
-            for (int b = 0; b < T::E; ++b) bytes[e * T::E + b] = 0;
-          }
-        }
-        std::memcpy(&st.v[k], bytes, 16);
-        st.vmask |= 1u << k;
-      }
-      if (FP8 && per_token && tid < 2 * TT / 4) {
-        int which = tid / (TT / 4);
-        int t = (tid % (TT / 4)) * 4;
-        st.sdst = which * TT + t;
-        const float* sc = which ? a.v_scale : a.k_scale;
-        float f[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          f[e] = 0.f;
-          if (ts + t + e < hi_u) {
-            long S = item_id(jt + t + e);
-            long pid = S / ps;
-            int slot = (int)(S % ps);
-            f[e] = sc[(pid * nh + kvh) * ps + slot];
-          }
-        }
-        st.s = u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
-      }
+    for (int k = 0; k < T::VPT; ++k)
+      __builtin_amdgcn_global_load_lds((const void*)(vsrc + k * v_step), (lds_void*)(vdst + k * NTHREADS * 16), 16,
+                                       0, 0);
+    if (FP8 && per_token && w == 0) {
+      const float* src = s_src0;
+      if (page_ok(s_pg)) src += (get_id(jt + s_pg) * a.Hkv + kvh) * ps + s_tok % ps;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(stg + T::KBYTES + T::VBYTES), 16, 0, 0);
     }
   };
+  auto issue_tile = [&](int tile, uint8_t* stg) {
+    if (min((long)(tile - tb + 1) * ppt, id_end - id0) <= (long)nstaged)
+      issue_tile_ids(tile, stg, staged_id);  // every id the tile needs is in LDS
+    else
+      issue_tile_ids(tile, stg, item_id);
+  };
 
-  // ---- registers -> LDS stage ----
-  auto store_tile = [&](const Staged<D, FP8>& st, uint8_t* stg) {
-    uint8_t* kl = stg;
-    uint8_t* vl = stg + T::KBYTES;
-    float* sl = (float*)(stg + T::KBYTES + T::VBYTES);
+  // ---- sparse: gather one tile into registers, then store it to LDS ----
+  auto load_sparse = [&](int tile, Staged<D, FP8, NTHREADS>& st) {
+    const int ts = t0 + tile * TT;
+    const long jt = (long)(tile - tb) * ppt;
 #pragma unroll
     for (int k = 0; k < T::KPT; ++k) {
-      if (!(st.kmask & (1u << k))) continue;
       int u = tid + k * NTHREADS;
-      int cc = u / TT, t = u % TT;
-      *(u32x4*)(kl + cc * TT * 16 + kswz(t) * 16) = st.k[k];
+      int cc = u / TT, t = kswz(u % TT);
+      st.k[k] = u32x4{0, 0, 0, 0};
+      if (ts + t < hi_u) {
+        long Sl = item_id(jt + t);
+        long pid = Sl / ps;
+        int slot = (int)(Sl % ps);
+        st.k[k] = *(const u32x4*)(kbase + pid * a.page_stride + ((long)cc * ps + slot) * 16);
+      }
     }
 #pragma unroll
     for (int k = 0; k < T::VPT; ++k) {
-      if (!(st.vmask & (1u << k))) continue;
       int u = tid + k * NTHREADS;
-      int d, unit;  // destination row and 16-byte unit within the row
-      if constexpr (SPARSE) {
-        int upr = TT * T::E / 16;
-        d = u / upr;
-        unit = u % upr;
-      } else {
-        const int n16 = ps * T::E / 16;
-        int per_page = D * n16;
-        int j = u / per_page, rem = u % per_page, s16;
-        if (a.v_transposed) {
-          s16 = rem / D;
-          d = rem % D;
+      int d = u / T::VUPR, q = u % T::VUPR;
+      int tfirst = (q ^ (d & (T::VUPR - 1))) * T::X;
+      uint8_t bytes[16];
+#pragma unroll
+      for (int e = 0; e < T::X; ++e) {
+        int t = tfirst + e;
+        if (ts + t < hi_u) {
+          long Sl = item_id(jt + t);
+          long pid = Sl / ps;
+          int slot = (int)(Sl % ps);
+          long off = a.v_transposed ? ((long)(slot / T::X) * D + d) * 16 + (slot % T::X) * T::E
+                                    : ((long)d * ps + slot) * T::E;
+          const uint8_t* src = vbase + pid * a.page_stride + off;
+#pragma unroll
+          for (int b = 0; b < T::E; ++b) bytes[e * T::E + b] = src[b];
         } else {
-          d = rem / n16;
-          s16 = rem % n16;
+#pragma unroll
+          for (int b = 0; b < T::E; ++b) bytes[e * T::E + b] = 0;
         }
-        unit = j * n16 + s16;
       }
-      uint8_t* row = vl + d * T::VROW;
-      if constexpr (FP8) {
-        int e = d & 15;
-        u32x4 val = st.v[k];
-        if (e & 1) val = u32x4{val[2], val[3], val[0], val[1]};
-        *(u32x4*)(row + ((2 * unit) ^ (e & 14)) * 8) = val;
-      } else {
-        *(u32x4*)(row + (unit ^ (d & 15)) * 16) = st.v[k];
-      }
+      std::memcpy(&st.v[k], bytes, 16);
     }
-    if (FP8 && per_token && tid < 2 * TT / 4) *(u32x4*)(sl + st.sdst) = st.s;
+    if (FP8 && per_token && w == 0) {
+      const float* sc = s_src0;
+      float f[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[e] = 0.f;
+        if (ts + s_tok + e < hi_u) {
+          long Sl = item_id(jt + s_tok + e);
+          long pid = Sl / ps;
+          int slot = (int)(Sl % ps);
+          f[e] = sc[(pid * a.Hkv + kvh) * ps + slot];
+        }
+      }
+      st.s = u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+    }
+  };
+  auto store_sparse = [&](const Staged<D, FP8, NTHREADS>& st, uint8_t* stg) {
+#pragma unroll
+    for (int k = 0; k < T::KPT; ++k) *(u32x4*)(stg + (tid + k * NTHREADS) * 16) = st.k[k];
+#pragma unroll
+    for (int k = 0; k < T::VPT; ++k) *(u32x4*)(stg + T::KBYTES + (tid + k * NTHREADS) * 16) = st.v[k];
+    if (FP8 && per_token && w == 0) *(u32x4*)(stg + T::KBYTES + T::VBYTES + lane * 16) = st.s;
   };
 
-  // ---- main loop ----
-  Staged<D, FP8> st;
-  if (tb < te) {
-    load_tile(tb, st);
-    store_tile(st, stage_base);
-  }
-  for (int tile = tb; tile < te; ++tile) {
-    __syncthreads();
-    const int cur = (tile - tb) & 1;
-    uint8_t* stg = stage_base + cur * T::STAGE;
-    const bool more = tile + 1 < te;
-    if (more) load_tile(tile + 1, st);
-
-    const int ts = t0 + tile * TT;
-    const int wt = ts + 32 * w;  // first token of this wave's 32
+  // ---- one 32-token step of one wave on a staged tile ----
+  // Token group tg covers tile tokens 32tg .. 32tg+31.  PT: per-token scales;
+  // IN: an interior tile (every token visible to every row: no masks).
+  auto step = [&](auto PTc, auto INc, int ts, int tg, const uint8_t* stg) {
+    constexpr bool PT = decltype(PTc)::value;
+    constexpr bool IN = decltype(INc)::value;
+    // lane-derived LDS offsets are recomputed per step rather than kept live
+    // across the loop (registers are the scarce resource here)
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    const int wt0 = ts + 32 * tg;  // first token of the step
+    if constexpr (!IN) {
+      if (!(wt0 < hi_u && wt0 + 32 > lo_u)) return;
+    }
     const uint8_t* kl = stg;
     const uint8_t* vl = stg + T::KBYTES;
     const float* sl = (const float*)(stg + T::KBYTES + T::VBYTES);
-    const bool interior = ts >= lo_max && ts + TT - 1 <= hi_min;
 
-    if (wt < hi_u && wt + 32 > lo_u) {
-      // --- S^T = K Q^T for the wave's 32 tokens: block b, row i <-> token 8(i/4)+4b+(i%4)
-      f4 sacc[NRT][2];
+    // --- S^T = K Q^T: block b, row i <-> token 8(i/4)+4b+(i%4) of the step
+    f4 sacc[NRW][2];
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) sacc[rt][0] = sacc[rt][1] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < NRW; ++rt) sacc[rt][0] = sacc[rt][1] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        int tok = 32 * w + 8 * (c >> 2) + 4 * b + (c & 3);
-        const uint8_t* krow = kl + kswz(tok) * 16;
-        if constexpr (FP8) {
+    for (int b = 0; b < 2; ++b) {
+      // keep the K fragments of one block live at a time (register pressure)
+      __builtin_amdgcn_sched_barrier(0);
+      const int tok = 32 * tg + 8 * (c >> 2) + 4 * b + (c & 3);
+      const uint8_t* krow = kl + kswz(tok) * 16;
+      if constexpr (FP8) {
 #pragma unroll
-          for (int kk = 0; kk < D / 64; ++kk) {
-            u32x4 raw = *(const u32x4*)(krow + (4 * kk + g) * TT * 16);
-            half8 k0 = fp8x8_to_half8(u32x2{raw[0], raw[1]});
-            half8 k1 = fp8x8_to_half8(u32x2{raw[2], raw[3]});
+        for (int kk = 0; kk < D / 64; ++kk) {
+          u32x4 raw = *(const u32x4*)(krow + (4 * kk + g) * TT * 16);
+          half8 k0 = fp8x8_to_half8(u32x2{raw[0], raw[1]});
+          half8 k1 = fp8x8_to_half8(u32x2{raw[2], raw[3]});
 #pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) {
-              sacc[rt][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[rt][2 * kk], sacc[rt][b], 0, 0, 0);
-              sacc[rt][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[rt][2 * kk + 1], sacc[rt][b], 0, 0, 0);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int m = 0; m < NM; ++m) {
-            u32x4 raw = *(const u32x4*)(krow + (4 * m + g) * TT * 16);
-            bf16x8 kf = __builtin_bit_cast(bf16x8, raw);
-#pragma unroll
-            for (int rt = 0; rt < NRT; ++rt)
-              sacc[rt][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rt][m], sacc[rt][b], 0, 0, 0);
+          for (int rt = 0; rt < NRW; ++rt) {
+            sacc[rt][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[rt][2 * kk], sacc[rt][b], 0, 0, 0);
+            sacc[rt][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[rt][2 * kk + 1], sacc[rt][b], 0, 0, 0);
           }
         }
-      }
-
-      // --- per-token scales of the lane's 8 tokens (slot p = 4b + r <-> token 8g + p)
-      const int tl = 32 * w + 8 * g;  // first of the lane's 8 tokens (tile-relative)
-      float ks[8], vsn[8];
-      if (per_token) {
-        f4 k0 = *(const f4*)(sl + tl), k1 = *(const f4*)(sl + tl + 4);
-        f4 v0 = *(const f4*)(sl + TT + tl), v1 = *(const f4*)(sl + TT + tl + 4);
+      } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          ks[r] = k0[r];
-          ks[4 + r] = k1[r];
-          vsn[r] = v0[r];
-          vsn[4 + r] = v1[r];
+        for (int m = 0; m < NM; ++m) {
+          u32x4 raw = *(const u32x4*)(krow + (4 * m + g) * TT * 16);
+          bf16x8 kf = __builtin_bit_cast(bf16x8, raw);
+#pragma unroll
+          for (int rt = 0; rt < NRW; ++rt)
+            sacc[rt][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rt][m], sacc[rt][b], 0, 0, 0);
         }
       }
-      // union validity of the lane's tokens (garbage outside it)
-      const int tv = ts + tl;
-      const int va = min(max(lo_u - tv, 0), 8), vb = min(max(hi_u - tv, 0), 8);  // valid slots [va, vb)
-      if (per_token) {
+    }
+
+    // --- the lane's 8 tokens: slot p = 4b + r <-> token 8g + p of the step
+    const int tl = 32 * tg + 8 * g;  // tile-relative
+    const int tv = ts + tl;          // absolute
+    int va = 0, vb = 8;              // slots [va, vb) lie in the visible span
+    if constexpr (!IN) {
+      va = min(max(lo_u - tv, 0), 8);
+      vb = min(max(hi_u - tv, 0), 8);
+    }
+    float ks[8], vsr[8];
+    if constexpr (PT) {
+      f4 k0 = *(const f4*)(sl + tl), k1 = *(const f4*)(sl + tl + 4);
+      f4 v0 = *(const f4*)(sl + TT + tl), v1 = *(const f4*)(sl + TT + tl + 4);
 #pragma unroll
-        for (int p = 0; p < 8; ++p)
-          if (p < va || p >= vb) vsn[p] = 0.f;
-        float vmax = 0.f;
+      for (int r = 0; r < 4; ++r) {
+        ks[r] = k0[r];
+        ks[4 + r] = k1[r];
+        vsr[r] = v0[r];
+        vsr[4 + r] = v1[r];
+      }
+      if constexpr (!IN) {
 #pragma unroll
-        for (int p = 0; p < 8; ++p) vmax = fmaxf(vmax, vsn[p]);
-        vmax = group_max(vmax);
-        // wave-uniform: every lane sees the same 32 tokens after the group max
-        if (vmax > 0.f && (vmax > vs_ref * 16.f || vmax < vs_ref * (1.0f / 1024.f))) {
-          float alpha = vs_ref / vmax;  // 0 on the first visit
+        for (int p = 0; p < 8; ++p) vsr[p] = (p >= va && p < vb) ? vsr[p] : 0.f;  // garbage outside the span
+      }
+      float vmax = 0.f;
 #pragma unroll
-          for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) o[rt][dt] *= alpha;
+      for (int p = 0; p < 8; ++p) vmax = fmaxf(vmax, vsr[p]);
+      vmax = group_max(vmax);  // wave-uniform: the 4 lane groups hold the step's 32 tokens
+      if (vs_ref == 0.f) {
+        if (vmax > 0.f) {  // first visible scales: O is still zero
           vs_ref = vmax;
-          inv_ref = 1.0f / vmax;
+          inv_ref = __builtin_amdgcn_rcpf(vmax);
         }
+      } else if (vmax > vs_ref * VS_BAND) {
+        ovf = true;
+        vs_hi = fmaxf(vs_hi, vmax);
       }
+#pragma unroll
+      for (int p = 0; p < 8; ++p) vsr[p] *= inv_ref;
+    }
 
-      // --- scale, mask, row max
-      float x[NRT][8];
-      float mx[NRT];
+    // --- y = raw score (* k scale), masked -> -inf; row max.  The positive
+    // row scale crow is applied in the exponent: max(crow*y) = crow*max(y).
+    float y[NRW][8];
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        mx[rt] = -INFINITY;
+    for (int rt = 0; rt < NRW; ++rt) {
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        float v = sacc[rt][p >> 2][p & 3];
+        if constexpr (PT) v *= ks[p];
+        if constexpr (!IN) {
+          const int t = tv + p;
+          v = (t >= lo_r[rt] && t <= hi_r[rt]) ? v : -INFINITY;
+        }
+        y[rt][p] = v;
+      }
+      float my = y[rt][0];
+#pragma unroll
+      for (int p = 1; p < 8; ++p) my = fmaxf(my, y[rt][p]);
+      const float mx = group_max(my) * crow[rt];  // -inf stays -inf (crow > 0)
+      if (m_ref[rt] == -INFINITY) {
+        m_ref[rt] = mx;  // first visible tokens of the row: its O is still zero
+      } else if (mx > m_ref[rt] + TAU) {
+        ovf = true;
+        m_hi[rt] = fmaxf(m_hi[rt], mx);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // --- probabilities -> PV operand, in registers
+    using PFrag = typename std::conditional<FP8, half8, bf16x8>::type;
+    PFrag pf[NRW];
+    PFrag pl[NRW];  // BF16 caches: low part of a two-term split of P
+#pragma unroll
+    for (int rt = 0; rt < NRW; ++rt) {
+      const float nm = m_ref[rt] == -INFINITY ? 0.f : -m_ref[rt];
+      float pr[8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        pr[p] = __builtin_amdgcn_exp2f(__builtin_fmaf(y[rt][p], crow[rt], nm));  // exp2(-inf) = 0
+        l_part[rt] += pr[p];
+        if constexpr (PT) pr[p] *= vsr[p];
+      }
+      if constexpr (FP8) {
+#pragma unroll
+        for (int p = 0; p < 8; p += 2) {
+          h2 hp = __builtin_convertvector(f2{pr[p], pr[p + 1]}, h2);
+          pf[rt][p] = hp[0];
+          pf[rt][p + 1] = hp[1];
+        }
+      } else {
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
-          float v = sacc[rt][p >> 2][p & 3] * crow[rt];
-          if (per_token) v *= ks[p];
-          if (!interior) {
-            int t = tv + p;
-            if (t < lo_r[rt] || t > hi_r[rt]) v = -INFINITY;
-          }
-          x[rt][p] = v;
-          mx[rt] = fmaxf(mx[rt], v);
-        }
-        mx[rt] = group_max(mx[rt]);
-      }
-      // --- lazy rescale when a row max grows past the band
-      bool need = false;
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) need |= mx[rt] > m_ref[rt] + TAU;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) {
-          float alpha = 1.0f;
-          if (mx[rt] > m_ref[rt] + TAU) {
-            alpha = exp2f(m_ref[rt] - mx[rt]);  // 0 when m_ref is -inf
-            m_ref[rt] = mx[rt];
-          }
-          l_part[rt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) o[rt][dt] *= alpha;
+          __bf16 hi = (__bf16)pr[p];
+          pf[rt][p] = hi;
+          pl[rt][p] = (__bf16)(pr[p] - (float)hi);
         }
       }
-      // --- probabilities -> PV operand (registers only)
-      using PFrag = typename std::conditional<FP8, half8, bf16x8>::type;
-      PFrag pf[NRT];
-      PFrag pl[NRT];  // BF16 caches: low part of a two-term split of P
+    }
+    // --- O^T += V^T P^T: V row d = 16dt + c, tokens 8g..8g+7 of the step
+    bool vmask = false;
+    uint64_t keep8 = ~0ull;  // FP8: byte mask of visible tokens
+    if constexpr (!IN) {
+      vmask = va > 0 || vb < 8;
+      // bytes [va, vb) hold visible tokens; no shift by 64 (va or vb may be 8)
+      const uint64_t below_vb = vb >= 8 ? ~0ull : ((1ull << (8 * vb)) - 1);
+      const uint64_t below_va = va >= 8 ? ~0ull : ((1ull << (8 * va)) - 1);
+      keep8 = below_vb & ~below_va;
+    }
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        float msafe = m_ref[rt] == -INFINITY ? 0.f : m_ref[rt];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          float pr = exp2f(x[rt][p] - msafe);
-          l_part[rt] += pr;
-          float u = per_token ? pr * (vsn[p] * inv_ref) : pr;
-          if constexpr (FP8) {
-            pf[rt][p] = (_Float16)u;
-          } else {
-            __bf16 hi = (__bf16)u;
-            pf[rt][p] = hi;
-            pl[rt][p] = (__bf16)(u - (float)hi);
+    for (int dt = 0; dt < NDT; ++dt) {
+      // V fragments are read and consumed a quarter of the head dim at a time
+      if (dt % (NDT / 4) == 0) __builtin_amdgcn_sched_barrier(0);
+      const int d = 16 * dt + c;
+      const uint8_t* vrow = vl + d * T::VROW;
+      if constexpr (FP8) {
+        const int q = (2 * tg + (g >> 1)) ^ (d & 7);
+        u32x2 raw = *(const u32x2*)(vrow + q * 16 + (g & 1) * 8);
+        if constexpr (!IN) {
+          if (vmask) {
+            raw[0] &= (uint32_t)keep8;
+            raw[1] &= (uint32_t)(keep8 >> 32);
           }
         }
-      }
-      // --- O^T += V^T P^T: V row d = 16dt + c, tokens 8g..8g+7 of the wave
+        const half8 vf = fp8x8_to_half8(raw);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        int d = 16 * dt + c;
-        const uint8_t* vrow = vl + d * T::VROW;
-        if constexpr (FP8) {
-          int unit = (4 * w + g) ^ c;
-          u32x2 raw = *(const u32x2*)(vrow + unit * 8);
-          if (va > 0 || vb < 8) {
-            // bytes [va, vb) hold valid tokens; no shift by 64 (va or vb may be 8)
-            uint64_t below_vb = vb >= 8 ? ~0ull : ((1ull << (8 * vb)) - 1);
-            uint64_t below_va = va >= 8 ? ~0ull : ((1ull << (8 * va)) - 1);
-            uint64_t keep = below_vb & ~below_va;
-            raw[0] &= (uint32_t)keep;
-            raw[1] &= (uint32_t)(keep >> 32);
-          }
-          half8 vf = fp8x8_to_half8(raw);
-#pragma unroll
-          for (int rt = 0; rt < NRT; ++rt)
-            o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[rt], o[rt][dt], 0, 0, 0);
-        } else {
-          int unit = (4 * w + g) ^ c;
-          u32x4 raw = *(const u32x4*)(vrow + unit * 16);
-          if (va > 0 || vb < 8) {
+        for (int rt = 0; rt < NRW; ++rt)
+          o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[rt], o[rt][dt], 0, 0, 0);
+      } else {
+        const int q = (4 * tg + g) ^ (d & 15);
+        u32x4 raw = *(const u32x4*)(vrow + q * 16);
+        if constexpr (!IN) {
+          if (vmask) {
 #pragma unroll
             for (int q2 = 0; q2 < 4; ++q2) {
               uint32_t keep = 0;
@@ -656,67 +670,186 @@ __global__ __launch_bounds__(NTHREADS) void pa_decode_kernel(KernelArgs a) {
               raw[q2] &= keep;
             }
           }
-          bf16x8 vf = __builtin_bit_cast(bf16x8, raw);
+        }
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, raw);
 #pragma unroll
-          for (int rt = 0; rt < NRT; ++rt) {
-            o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rt], o[rt][dt], 0, 0, 0);
-            o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[rt], o[rt][dt], 0, 0, 0);
-          }
+        for (int rt = 0; rt < NRW; ++rt) {
+          o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rt], o[rt][dt], 0, 0, 0);
+          o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[rt], o[rt][dt], 0, 0, 0);
         }
       }
     }
-    if (more) store_tile(st, stage_base + (cur ^ 1) * T::STAGE);
+  };
+  // The steps of a tile run as a real (not unrolled) loop with an opaque trip
+  // count: with the PV MFMAs of several steps in one block the compiler unties
+  // their accumulators and shuffles O between registers every iteration.
+  auto compute_tile = [&](auto PTc, auto INc, int tile, const uint8_t* stg) {
+    const int ts = t0 + tile * TT;
+    int nst = R::STEPS;
+    asm volatile("" : "+s"(nst));
+#pragma unroll 1
+    for (int st = 0; st < nst; ++st) step(PTc, INc, ts, wt * R::STEPS + st, stg);
+    // publish an overflow of this wave so the whole workgroup restarts
+    if (__builtin_amdgcn_ballot_w64(ovf) && lane == 0) *restart_flag = 1;
+  };
+
+  // Tiles [ti0, ti1) are interior (no masks); the others are boundary tiles.
+  // Leading boundary, interior and trailing boundary tiles run in three
+  // separate loops so that each loop body is one straight code path.
+  int ti0 = tb, ti1 = tb;  // interior range within [tb, te)
+  {
+    // interior iff ts >= lo_max and ts + TT - 1 <= hi_min, ts = t0 + TT*tile
+    const int first = lo_max > t0 ? (lo_max - t0 + TT - 1) / TT : 0;
+    const int last = hi_min - t0 - (TT - 1) >= 0 ? (hi_min - t0 - (TT - 1)) / TT + 1 : 0;  // exclusive
+    ti0 = min(max(first, tb), te);
+    ti1 = max(min(last, te), ti0);
   }
 
-  // ---- merge the four waves' states ----
-  float l_row[NRT];
+  // ---- main loop: one attempt over the item's tiles ----
+  auto attempt = [&](auto PTc) {
+    if constexpr (!SPARSE) {
+      // NST-deep ring: tiles tb .. tb+NST-2 in flight before the first compute.
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) l_row[rt] = group_sum(l_part[rt]);
-  __syncthreads();  // all waves done with the stages (merge buffers alias them)
-  float* wm = stats;                         // [NWAVES][NRT*16] m_ref
-  float* wl = stats + NWAVES * NRT * 16;     // [NWAVES][NRT*16] l
-  float* wr = stats + 2 * NWAVES * NRT * 16; // [NWAVES] v-scale reference
-  float* rowinfo = wr + NWAVES;              // [NRT*16][4]: M, Ltot, out factor, flag
+      for (int k = 0; k < NST - 1; ++k)
+        if (tb + k < te) issue_tile(tb + k, stage_base + k * T::STAGE);
+      // returns false if an overflow stopped the attempt
+      auto tiles = [&](auto INc, int from, int to) -> bool {
+        for (int tile = from; tile < to; ++tile) {
+          const int cur = (tile - tb) % NST;
+          // wait for this tile's loads; the later tiles' loads stay in flight
+          const int ahead = min(te - 1 - tile, NST - 2);  // tiles issued after this one
+          constexpr int PER = T::KPT + T::VPT;
+          const bool extra = FP8 && decltype(PTc)::value && w == 0;  // wave 0 also loads scales
+          if (ahead <= 0) {
+            wait_vmcnt<0>();
+          } else if (ahead == 1) {
+            if (extra) wait_vmcnt<PER + 1>();
+            else wait_vmcnt<PER>();
+          } else {
+            if (extra) wait_vmcnt<2 * (PER + 1)>();
+            else wait_vmcnt<2 * PER>();
+          }
+          wait_lgkm0();  // this wave's LDS writes (restart flag) are done
+          // all waves' loads of this tile landed and tile-1 compute is done; the
+          // empty asm statements keep the compiler from moving LDS accesses across
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          if (*(volatile int*)restart_flag) return false;  // an overflow: stop this attempt
+          if (tile + NST - 1 < te)
+            issue_tile(tile + NST - 1, stage_base + ((tile - tb + NST - 1) % NST) * T::STAGE);
+          compute_tile(PTc, INc, tile, stage_base + cur * T::STAGE);
+        }
+        return true;
+      };
+      if (tiles(std::false_type{}, tb, ti0))
+        if (tiles(std::true_type{}, ti0, ti1)) tiles(std::false_type{}, ti1, te);
+      wait_vmcnt<0>();  // drain the ring (loads issued past a stop)
+    } else {
+      Staged<D, FP8, NTHREADS> st;
+      if (tb < te) {
+        load_sparse(tb, st);
+        store_sparse(st, stage_base);
+      }
+      for (int tile = tb; tile < te; ++tile) {
+        __syncthreads();
+        if (*(volatile int*)restart_flag) break;
+        const int cur = (tile - tb) & 1;
+        const bool more = tile + 1 < te;
+        if (more) load_sparse(tile + 1, st);
+        if (tile >= ti0 && tile < ti1)
+          compute_tile(PTc, std::true_type{}, tile, stage_base + cur * T::STAGE);
+        else
+          compute_tile(PTc, std::false_type{}, tile, stage_base + cur * T::STAGE);
+        if (more) store_sparse(st, stage_base + (cur ^ 1) * T::STAGE);
+      }
+    }
+  };
+  auto run = [&](auto PTc) {
+    for (;;) {
+#pragma unroll
+      for (int rt = 0; rt < NRW; ++rt) {
+        l_part[rt] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[rt][dt] = f4{0.f, 0.f, 0.f, 0.f};
+      }
+      attempt(PTc);
+      __syncthreads();
+      const bool again = *(volatile int*)restart_flag != 0;
+      if (!again) break;
+      // restart with the larger references
+      __syncthreads();
+      if (tid == 0) *restart_flag = 0;
+#pragma unroll
+      for (int rt = 0; rt < NRW; ++rt) m_ref[rt] = fmaxf(m_ref[rt], m_hi[rt]);
+      if (vs_hi > vs_ref) {
+        vs_ref = vs_hi;
+        inv_ref = 1.0f / vs_ref;
+      }
+      ovf = false;
+      __syncthreads();
+    }
+  };
+  if constexpr (FP8) {
+    if (per_token)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
+  } else {
+    run(std::false_type{});
+  }
+
+  // ---- merge the token groups' states of each row ----
+  constexpr int NR = NRT * 16;  // rows of the item (padded)
+  float l_row[NRW];
+#pragma unroll
+  for (int rt = 0; rt < NRW; ++rt) l_row[rt] = group_sum(l_part[rt]);
+  __syncthreads();  // all waves done with the stages (the merge buffer aliases them)
+  float* wm = stats;                          // [WT][NR] m_ref
+  float* wl = stats + R::WT * NR;             // [WT][NR] l
+  float* wref = stats + 2 * R::WT * NR;       // [NWAVES] v-scale reference
+  float* rowinfo = wref + NWAVES;             // [NR][4]: M, Ltot, out factor
   if (g == 0) {
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      wm[w * NRT * 16 + rt * 16 + c] = m_ref[rt];
-      wl[w * NRT * 16 + rt * 16 + c] = l_row[rt];
+    for (int rt = 0; rt < NRW; ++rt) {
+      const int r = (wr * NRW + rt) * 16 + c;
+      wm[wt * NR + r] = m_ref[rt];
+      wl[wt * NR + r] = l_row[rt];
     }
   }
-  if (lane == 0) wr[w] = vs_ref;
+  if (lane == 0) wref[w] = vs_ref;
   __syncthreads();
   // weight of this wave's O for each of its rows
-  float fw[NRT];
+  float fw[NRW];
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    int r = rt * 16 + c;
+  for (int rt = 0; rt < NRW; ++rt) {
+    const int r = (wr * NRW + rt) * 16 + c;
     float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < NWAVES; ++ww)
-      if (wl[ww * NRT * 16 + r] > 0.f) M = fmaxf(M, wm[ww * NRT * 16 + r]);
-    fw[rt] = (l_row[rt] > 0.f) ? exp2f(m_ref[rt] - M) * vs_ref : 0.f;
+    for (int k = 0; k < R::WT; ++k)
+      if (wl[k * NR + r] > 0.f) M = fmaxf(M, wm[k * NR + r]);
+    fw[rt] = (l_row[rt] > 0.f) ? __builtin_amdgcn_exp2f(m_ref[rt] - M) * vs_ref : 0.f;
   }
-  if (tid < NRT * 16) {
-    int r = tid;
+  if (tid < NR) {
+    const int r = tid;
     float M = -INFINITY, Lt = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < NWAVES; ++ww)
-      if (wl[ww * NRT * 16 + r] > 0.f) M = fmaxf(M, wm[ww * NRT * 16 + r]);
+    for (int k = 0; k < R::WT; ++k)
+      if (wl[k * NR + r] > 0.f) M = fmaxf(M, wm[k * NR + r]);
 #pragma unroll
-    for (int ww = 0; ww < NWAVES; ++ww) {
-      float lw = wl[ww * NRT * 16 + r];
-      if (lw > 0.f) Lt += lw * exp2f(wm[ww * NRT * 16 + r] - M);
+    for (int k = 0; k < R::WT; ++k) {
+      const float lw = wl[k * NR + r];
+      if (lw > 0.f) Lt += lw * __builtin_amdgcn_exp2f(wm[k * NR + r] - M);
     }
     float factor = 0.f;  // direct output: out = O * factor
     if (Lt > 0.f) {
       if (a.has_sinks) {
-        int gr = row0 + (r < nrows ? r : 0);
-        int h = kvh * a.G + gr % a.G;
-        float sk = a.sinks[h] * 1.4426950408889634f;
-        float M2 = fmaxf(M, sk);
-        float sc = exp2f(M - M2);
-        factor = sc / (Lt * sc + exp2f(sk - M2));
+        const int gr = row0 + (r < nrows ? r : 0);
+        const int h = kvh * a.G + gr % a.G;
+        const float sk = a.sinks[h] * LOG2E;
+        const float M2 = fmaxf(M, sk);
+        const float sc = __builtin_amdgcn_exp2f(M - M2);
+        factor = sc / (Lt * sc + __builtin_amdgcn_exp2f(sk - M2));
       } else {
         factor = 1.0f / Lt;
       }
@@ -725,32 +858,25 @@ __global__ __launch_bounds__(NTHREADS) void pa_decode_kernel(KernelArgs a) {
     rowinfo[r * 4 + 1] = Lt;
     rowinfo[r * 4 + 2] = factor;
   }
-  // O buffers: waves 0/1 write, waves 2/3 add
+  // O buffer [NR][D+4]: token group 0 writes its rows, the others add in turn
   constexpr int OROW = D + 4;
   float* obuf = (float*)stage_base;
-  float* mine = obuf + (w & 1) * (NRT * 16 * OROW);
-  if (w < 2) {
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
+  for (int k = 0; k < R::WT; ++k) {
+    if (wt == k) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        *(f4*)(mine + (rt * 16 + c) * OROW + 16 * dt + 4 * g) = o[rt][dt] * fw[rt];
+      for (int rt = 0; rt < NRW; ++rt)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          f4* dst = (f4*)(obuf + ((wr * NRW + rt) * 16 + c) * OROW + 16 * dt + 4 * g);
+          const f4 v = o[rt][dt] * fw[rt];
+          *dst = (k == 0) ? v : *dst + v;
+        }
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (w >= 2) {
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        f4* dst = (f4*)(mine + (rt * 16 + c) * OROW + 16 * dt + 4 * g);
-        *dst = *dst + o[rt][dt] * fw[rt];
-      }
-  }
-  __syncthreads();
 
   // ---- write: partial state or final rows ----
-  const float* ob0 = obuf;
-  const float* ob1 = obuf + NRT * 16 * OROW;
   if (it.slot >= 0) {
     float* sp = a.workspace + (size_t)it.slot * rpg * (2 + D);
     float* pm = sp;
@@ -761,17 +887,15 @@ __global__ __launch_bounds__(NTHREADS) void pa_decode_kernel(KernelArgs a) {
       pl_[tid] = rowinfo[tid * 4 + 1];
     }
     for (int e = tid; e < nrows * (D / 4); e += NTHREADS) {
-      int r = e / (D / 4), d4 = (e % (D / 4)) * 4;
-      f4 v = *(const f4*)(ob0 + r * OROW + d4) + *(const f4*)(ob1 + r * OROW + d4);
-      *(f4*)(po + (size_t)r * D + d4) = v;
+      const int r = e / (D / 4), d4 = (e % (D / 4)) * 4;
+      *(f4*)(po + (size_t)r * D + d4) = *(const f4*)(obuf + r * OROW + d4);
     }
   } else {
     for (int e = tid; e < nrows * (D / 4); e += NTHREADS) {
-      int r = e / (D / 4), d4 = (e % (D / 4)) * 4;
-      f4 v = *(const f4*)(ob0 + r * OROW + d4) + *(const f4*)(ob1 + r * OROW + d4);
-      v *= rowinfo[r * 4 + 2];
-      int gr = row0 + r, i = gr / a.G, hl = gr % a.G;
-      long ooff = (((long)s * a.QL + i) * a.Hq + (long)kvh * a.G + hl) * D + d4;
+      const int r = e / (D / 4), d4 = (e % (D / 4)) * 4;
+      const f4 v = *(const f4*)(obuf + r * OROW + d4) * rowinfo[r * 4 + 2];
+      const int gr = row0 + r, i = gr / a.G, hl = gr % a.G;
+      const long ooff = (((long)s * a.QL + i) * a.Hq + (long)kvh * a.G + hl) * D + d4;
       uint16_t hv[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -780,8 +904,8 @@ __global__ __launch_bounds__(NTHREADS) void pa_decode_kernel(KernelArgs a) {
         else
           hv[k] = __builtin_bit_cast(uint16_t, (__bf16)v[k]);
       }
-      u32x2 packed = u32x2{(uint32_t)hv[0] | ((uint32_t)hv[1] << 16), (uint32_t)hv[2] | ((uint32_t)hv[3] << 16)};
-      *(u32x2*)((uint16_t*)a.out + ooff) = packed;
+      *(u32x2*)((uint16_t*)a.out + ooff) =
+          u32x2{(uint32_t)hv[0] | ((uint32_t)hv[1] << 16), (uint32_t)hv[2] | ((uint32_t)hv[3] << 16)};
     }
   }
 }
@@ -789,54 +913,87 @@ __global__ __launch_bounds__(NTHREADS) void pa_decode_kernel(KernelArgs a) {
 // ---------------------------------------------------------------------------
 // Partition reducer: out = sum_p w_p O_p / (sum_p w_p l_p + [sink]), with
 // w_p = 2^(m_p - M), M = max(m_p over parts with l_p > 0, sink), partitions
-// added in order (deterministic).
+// added in order (deterministic).  One workgroup per (entry, 8 rows); the
+// partition weights of its rows are computed once into LDS.
 // ---------------------------------------------------------------------------
 struct ReduceArgs {
   void* out;
   const float* workspace;
   const float* sinks;
   const ReduceItem* entries;
-  int QL, Hq, G, D, rows_total, rows_per_group, q_fp16, has_sinks;
+  int QL, Hq, G, D, rows_total, rows_per_group, q_fp16, has_sinks, chunks_per_entry;
 };
 
+constexpr int RED_ROWS = 8;
+
 __global__ __launch_bounds__(256) void pa_reduce_kernel(ReduceArgs a) {
-  const ReduceItem e = a.entries[blockIdx.x];
+  __shared__ float wgt[RED_ROWS][kMaxPartitions];
+  __shared__ float rowf[RED_ROWS];
+  const ReduceItem e = a.entries[blockIdx.x / a.chunks_per_entry];
+  const int chunk = blockIdx.x % a.chunks_per_entry;
   const int D = a.D, rpg = a.rows_per_group;
   const int row0 = e.rg * kMaxRowsPerItem;
   const int nrows = min(rpg, a.rows_total - row0);
+  const int r0 = chunk * RED_ROWS;
   const size_t slot_f = (size_t)rpg * (2 + D);
-  for (int idx = threadIdx.x; idx < nrows * (D / 4); idx += blockDim.x) {
-    int r = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
-    float M = -INFINITY;
-    for (int p = 0; p < e.nparts; ++p) {
-      const float* sp = a.workspace + (size_t)(e.first_slot + p) * slot_f;
-      if (sp[rpg + r] > 0.f) M = fmaxf(M, sp[r]);
-    }
-    f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
-    if (M > -INFINITY) {
-      for (int p = 0; p < e.nparts; ++p) {
+  const int tid = threadIdx.x;
+  // per-row weights (one wave per row pair; lanes over partitions)
+  if (tid < 64 * 4) {
+    int wv = tid >> 6, lane = tid & 63;
+    for (int rr = wv; rr < RED_ROWS; rr += 4) {
+      int r = r0 + rr;
+      if (r >= nrows) continue;
+      float M = -INFINITY;
+      for (int p = lane; p < e.nparts; p += 64) {
+        const float* sp = a.workspace + (size_t)(e.first_slot + p) * slot_f;
+        if (sp[rpg + r] > 0.f) M = fmaxf(M, sp[r]);
+      }
+      for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+      float den = 0.f;
+      for (int p = lane; p < e.nparts; p += 64) {
         const float* sp = a.workspace + (size_t)(e.first_slot + p) * slot_f;
         float lp = sp[rpg + r];
-        if (!(lp > 0.f)) continue;
-        float wgt = exp2f(sp[r] - M);
-        den += wgt * lp;
-        acc += wgt * *(const f4*)(sp + 2 * rpg + (size_t)r * D + d4);
+        float wp = (lp > 0.f) ? __builtin_amdgcn_exp2f(sp[r] - M) : 0.f;
+        wgt[rr][p] = wp;
+        den += wp * lp;
+      }
+      // fixed-order sum of the denominator terms
+      for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
+      if (lane == 0) {
+        float f = 0.f;
+        if (den > 0.f) {
+          if (a.has_sinks) {
+            int gr = row0 + r, h = e.kvh * a.G + gr % a.G;
+            float sk = a.sinks[h] * LOG2E;
+            float M2 = fmaxf(M, sk);
+            float sc = __builtin_amdgcn_exp2f(M - M2);
+            f = sc / (den * sc + __builtin_amdgcn_exp2f(sk - M2));
+          } else {
+            f = 1.0f / den;
+          }
+        }
+        rowf[rr] = f;
       }
     }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < RED_ROWS * (D / 4); idx += blockDim.x) {
+    int rr = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
+    int r = r0 + rr;
+    if (r >= nrows) continue;
+    f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+    const float f = rowf[rr];
+    if (f > 0.f) {
+      for (int p = 0; p < e.nparts; ++p) {
+        float wp = wgt[rr][p];
+        if (wp == 0.f) continue;
+        const float* sp = a.workspace + (size_t)(e.first_slot + p) * slot_f;
+        acc += wp * *(const f4*)(sp + 2 * rpg + (size_t)r * D + d4);
+      }
+    }
+    f4 v = acc * f;
     int gr = row0 + r, i = gr / a.G, hl = gr % a.G;
     int h = e.kvh * a.G + hl;
-    f4 v = f4{0.f, 0.f, 0.f, 0.f};
-    if (den > 0.f) {
-      if (a.has_sinks) {
-        float sk = a.sinks[h] * 1.4426950408889634f;
-        float M2 = fmaxf(M, sk);
-        float sc = exp2f(M - M2);
-        v = acc * (sc / (den * sc + exp2f(sk - M2)));
-      } else {
-        v = acc * (1.0f / den);
-      }
-    }
     long ooff = (((long)e.seq * a.QL + i) * a.Hq + h) * D + d4;
     uint16_t hv[4];
 #pragma unroll
@@ -854,11 +1011,10 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(ReduceArgs a) {
 // ---------------------------------------------------------------------------
 // Launch selection
 // ---------------------------------------------------------------------------
-using KernelFn = void (*)(KernelArgs);
-
 template <int D, bool FP8, int NRT, bool SPARSE>
 static pa_status launch_one(const KernelArgs& args, int nblocks, hipStream_t stream) {
-  constexpr int bytes = Smem<D, FP8, NRT>::TOTAL;
+  constexpr int bytes = Smem<D, FP8, NRT, SPARSE>::TOTAL;
+  static_assert(bytes <= 160 * 1024, "LDS budget");
   static bool configured = false;
   if (!configured) {
     if (hipFuncSetAttribute((const void*)pa_decode_kernel<D, FP8, NRT, SPARSE>,
@@ -868,7 +1024,8 @@ static pa_status launch_one(const KernelArgs& args, int nblocks, hipStream_t str
     }
     configured = true;
   }
-  hipLaunchKernelGGL((pa_decode_kernel<D, FP8, NRT, SPARSE>), dim3(nblocks), dim3(NTHREADS), bytes, stream, args);
+  hipLaunchKernelGGL((pa_decode_kernel<D, FP8, NRT, SPARSE>), dim3(nblocks), dim3(Waves<NRT>::NT), bytes, stream,
+                     args);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(PA_ERR_DEVICE, std::string("decode launch failed: ") + hipGetErrorString(err));
   return PA_OK;
@@ -936,6 +1093,7 @@ extern "C" pa_status pa_decode(const pa_plan_t* plan, void* out, const void* q, 
   args.page_stride = args.head_stride * p.num_kv_heads;
   args.QL = p.query_len;
   args.Hq = p.num_q_heads;
+  args.Hkv = p.num_kv_heads;
   args.G = p.num_q_heads / p.num_kv_heads;
   args.page_size = p.page_size;
   args.table_stride = p.table_stride;
@@ -981,7 +1139,9 @@ extern "C" pa_status pa_reduce(const pa_plan_t* plan, void* out, const float* si
   ra.rows_per_group = P.rows_per_group;
   ra.q_fp16 = P.prob.q_dtype == PA_FP16;
   ra.has_sinks = P.prob.has_sinks;
-  hipLaunchKernelGGL(pa_reduce_kernel, dim3((unsigned)P.reduce.size()), dim3(256), 0, (hipStream_t)stream, ra);
+  ra.chunks_per_entry = (P.rows_per_group + RED_ROWS - 1) / RED_ROWS;
+  const unsigned grid = (unsigned)(P.reduce.size() * ra.chunks_per_entry);
+  hipLaunchKernelGGL(pa_reduce_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, ra);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(PA_ERR_DEVICE, std::string("reduce launch failed: ") + hipGetErrorString(err));
   return PA_OK;
