@@ -48,6 +48,7 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int TT = kTileTokens;  // 128 tokens per tile
@@ -62,6 +63,7 @@ struct Waves {
 constexpr float TAU = 12.0f;     // probabilities are taken against a reference max: p <= 2^12
 constexpr float VS_BAND = 8.0f;  // per-token V scales against a reference: vs/ref <= 8
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float FP8_MAX = 448.0f;  // largest finite e4m3fn value
 
 struct KernelArgs {
   void* out;
@@ -255,61 +257,84 @@ __global__ __launch_bounds__(Waves<NRT>::NT) void pa_decode_kernel(KernelArgs a)
   for (int k = tid; k < nstaged; k += NTHREADS) ids[k] = bt_row[id0 + k];
 
   // ---- query fragments of the wave's rows ----
-  // FP8 caches: d of MFMA step m, lane group g, slot p is 64(m/2)+16g+8(m%2)+p;
-  // BF16 caches: 32m+8g+p.  Both read 8 contiguous d per (m, g).
-  using QFrag = typename std::conditional<FP8, half8, bf16x8>::type;
-  QFrag qf[NRW][NM];
-  float crow[NRW];  // log2-domain score scale of the row (incl. query pre-scale)
+  // FP8 caches: QK runs on the FP8 matrix cores with K as stored.  The query
+  // row is scaled by qs = amax/448 and split into three FP8 terms,
+  // q/qs = hi + mid/16 + lo/256 (about 12 significant bits), that enter the
+  // MFMA with block scales 1, 2^-4 and 2^-8.  Lane group g of MFMA k-step kk
+  // holds d = 128kk + 32g .. +31 (K chunks 8kk+2g and 8kk+2g+1).
+  // BF16 caches: BF16 MFMA with q as given; d of step m, lane group g, slot p
+  // is 32m + 8g + p.
+  constexpr int NQ = FP8 ? D / 128 : NM;  // QK k-steps
+  using QFrag = typename std::conditional<FP8, i32x8, bf16x8>::type;
+  QFrag qf[NRW][NQ][FP8 ? 3 : 1];
+  float crow[NRW];  // log2-domain score scale of the row (incl. the query scale)
 #pragma unroll
   for (int rt = 0; rt < NRW; ++rt) {
-    int r = (wr * NRW + rt) * 16 + c;
-    bool valid = r < nrows;
-    int gr = row0 + (valid ? r : 0);
-    int i = gr / a.G, hl = gr % a.G;
-    long qoff = (((long)s * a.QL + i) * a.Hq + (long)kvh * a.G + hl) * D;
+    const int r = (wr * NRW + rt) * 16 + c;
+    const bool valid = r < nrows;
+    const int gr = row0 + (valid ? r : 0);
+    const int i = gr / a.G, hl = gr % a.G;
+    const long qoff = (((long)s * a.QL + i) * a.Hq + (long)kvh * a.G + hl) * D;
     const uint16_t* qrow = (const uint16_t*)a.q + qoff;
-    u32x4 raw[NM];
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      int d0 = FP8 ? 64 * (m >> 1) + 16 * g + 8 * (m & 1) : 32 * m + 8 * g;
-      raw[m] = valid ? *(const u32x4*)(qrow + d0) : u32x4{0, 0, 0, 0};
-    }
     if constexpr (FP8) {
-      float qv[NM][8];
-      if (a.q_fp16) {
+      float qv[NQ][32];
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
+      for (int kk = 0; kk < NQ; ++kk) {
 #pragma unroll
-          for (int p = 0; p < 8; ++p)
-            qv[m][p] = (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[m][p >> 1] >> (16 * (p & 1))));
-      } else {
+        for (int h = 0; h < 4; ++h) {
+          const u32x4 raw = valid ? *(const u32x4*)(qrow + 128 * kk + 32 * g + 8 * h) : u32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-          for (int p = 0; p < 8; ++p) qv[m][p] = __uint_as_float((raw[m][p >> 1] >> (16 * (p & 1))) << 16);
+          for (int p = 0; p < 8; ++p) {
+            const uint16_t bits = (uint16_t)(raw[p >> 1] >> (16 * (p & 1)));
+            qv[kk][8 * h + p] = a.q_fp16 ? (float)__builtin_bit_cast(_Float16, bits) : __uint_as_float((uint32_t)bits << 16);
+          }
+        }
       }
       float amax = 0.f;
 #pragma unroll
-      for (int m = 0; m < NM; ++m)
+      for (int kk = 0; kk < NQ; ++kk)
 #pragma unroll
-        for (int p = 0; p < 8; ++p) amax = fmaxf(amax, fabsf(qv[m][p]));
+        for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(qv[kk][j]));
       amax = group_max(amax);
-      // BF16 rows are scaled by 2^e so |q| lands in [2^14, 2^15): exact in FP16.
-      int e = 0;
-      if (!a.q_fp16 && amax > 0.f && amax < INFINITY) {
-        int ex;
-        frexpf(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1)
-        e = 15 - ex;
+      const float qs = (amax > 0.f && amax < INFINITY) ? amax * (1.0f / FP8_MAX) : 1.0f;
+      const float inv_qs = 1.0f / qs;
+#pragma unroll
+      for (int kk = 0; kk < NQ; ++kk) {
+#pragma unroll
+        for (int j4 = 0; j4 < 8; ++j4) {  // 4 values per 32-bit word
+          int w0 = 0, w1 = 0, w2 = 0;
+          float r1[4], r2[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r1[e] = fminf(fmaxf(qv[kk][4 * j4 + e] * inv_qs, -FP8_MAX), FP8_MAX);
+          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(r1[0], r1[1], w0, false);
+          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(r1[2], r1[3], w0, true);
+          {
+            const float h[4] = {__builtin_amdgcn_cvt_f32_fp8(w0, 0), __builtin_amdgcn_cvt_f32_fp8(w0, 1),
+                                __builtin_amdgcn_cvt_f32_fp8(w0, 2), __builtin_amdgcn_cvt_f32_fp8(w0, 3)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r2[e] = (r1[e] - h[e]) * 16.0f;
+          }
+          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(r2[0], r2[1], w1, false);
+          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(r2[2], r2[3], w1, true);
+          {
+            const float h[4] = {__builtin_amdgcn_cvt_f32_fp8(w1, 0), __builtin_amdgcn_cvt_f32_fp8(w1, 1),
+                                __builtin_amdgcn_cvt_f32_fp8(w1, 2), __builtin_amdgcn_cvt_f32_fp8(w1, 3)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r1[e] = (r2[e] - h[e]) * 16.0f;
+          }
+          w2 = __builtin_amdgcn_cvt_pk_fp8_f32(r1[0], r1[1], w2, false);
+          w2 = __builtin_amdgcn_cvt_pk_fp8_f32(r1[2], r1[3], w2, true);
+          qf[rt][kk][0][j4] = w0;
+          qf[rt][kk][1][j4] = w1;
+          qf[rt][kk][2][j4] = w2;
+        }
       }
-      const float mul = ldexpf(1.0f, e);
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int p = 0; p < 8; ++p) qf[rt][m][p] = (_Float16)(qv[m][p] * mul);
-      crow[rt] = a.scale_log2 * ldexpf(1.0f, -e);
+      crow[rt] = a.scale_log2 * qs;
     } else {
 #pragma unroll
-      for (int m = 0; m < NM; ++m) qf[rt][m] = __builtin_bit_cast(bf16x8, raw[m]);
+      for (int m = 0; m < NM; ++m)
+        qf[rt][m][0] = valid ? __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 32 * m + 8 * g))
+                             : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
       crow[rt] = a.scale_log2;
     }
   }
@@ -509,14 +534,19 @@ __global__ __launch_bounds__(Waves<NRT>::NT) void pa_decode_kernel(KernelArgs a)
       const uint8_t* krow = kl + kswz(tok) * 16;
       if constexpr (FP8) {
 #pragma unroll
-        for (int kk = 0; kk < D / 64; ++kk) {
-          u32x4 raw = *(const u32x4*)(krow + (4 * kk + g) * TT * 16);
-          half8 k0 = fp8x8_to_half8(u32x2{raw[0], raw[1]});
-          half8 k1 = fp8x8_to_half8(u32x2{raw[2], raw[3]});
+        for (int kk = 0; kk < NQ; ++kk) {
+          const u32x4 k0 = *(const u32x4*)(krow + (8 * kk + 2 * g) * TT * 16);
+          const u32x4 k1 = *(const u32x4*)(krow + (8 * kk + 2 * g + 1) * TT * 16);
+          const i32x8 kf = i32x8{(int)k0[0], (int)k0[1], (int)k0[2], (int)k0[3],
+                                 (int)k1[0], (int)k1[1], (int)k1[2], (int)k1[3]};
 #pragma unroll
           for (int rt = 0; rt < NRW; ++rt) {
-            sacc[rt][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[rt][2 * kk], sacc[rt][b], 0, 0, 0);
-            sacc[rt][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[rt][2 * kk + 1], sacc[rt][b], 0, 0, 0);
+            sacc[rt][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf[rt][kk][0], sacc[rt][b], 0, 0, 0,
+                                                                           127, 0, 127);
+            sacc[rt][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf[rt][kk][1], sacc[rt][b], 0, 0, 0,
+                                                                           127, 0, 123);
+            sacc[rt][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf[rt][kk][2], sacc[rt][b], 0, 0, 0,
+                                                                           127, 0, 119);
           }
         }
       } else {
@@ -526,7 +556,7 @@ __global__ __launch_bounds__(Waves<NRT>::NT) void pa_decode_kernel(KernelArgs a)
           bf16x8 kf = __builtin_bit_cast(bf16x8, raw);
 #pragma unroll
           for (int rt = 0; rt < NRW; ++rt)
-            sacc[rt][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rt][m], sacc[rt][b], 0, 0, 0);
+            sacc[rt][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rt][m][0], sacc[rt][b], 0, 0, 0);
         }
       }
     }
