@@ -18,7 +18,6 @@ Hkv 1, head dim 128, 4 causal query rows, page 128, lengths uniform in
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -32,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 from paged_attention_decode_plan_amd import binding as B  # noqa: E402
 from paged_attention_decode_plan_amd import workloads as W  # noqa: E402
+from paged_attention_decode_plan_amd.build import source_sha  # noqa: E402
 
 PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
 WORKLOADS = {
@@ -48,14 +48,6 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_sha() -> str:
-    h = hashlib.sha256()
-    for f in ("pa_kernels.hip", "pa_plan.cpp", "pa_internal.h"):
-        with open(os.path.join(ROOT, "paged_attention_decode_plan_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def load_traffic(workload: str, launches_kv_bytes: float):
     """HBM bytes per decode launch from committed rocprofv3 counter runs, if
     they were taken on the current kernel source."""
@@ -64,7 +56,7 @@ def load_traffic(workload: str, launches_kv_bytes: float):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_sha") != kernel_sha():
+    if t.get("kernel_sha") != source_sha():
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -123,6 +115,8 @@ def main():
     ap.add_argument("--workload", default="dense_mtp4_fp8", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run one device-to-device copy of MIB MiB first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this decode engine runs on a single MI355X; "
@@ -148,6 +142,16 @@ def main():
     def step():
         B.pa_decode(plan, out, d["q"], d["k"], d["v"], d["bt"], d["cl"], d["ks"], d["vs"], d["sk"], stream)
         B.pa_reduce(plan, out, d["sk"], stream)
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"calibration copy: {n} bytes read, {n} bytes written")
 
     for _ in range(args.warmup):
         step()
@@ -223,7 +227,7 @@ def main():
         "wall_s_timed_regions": round(warm_wall + cold_wall, 3),
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "kernel_sha": kernel_sha(),
+        "kernel_sha": source_sha(),
     }
     print(json.dumps(res), flush=True)
 

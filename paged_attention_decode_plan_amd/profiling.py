@@ -1,0 +1,142 @@
+"""Summaries of rocprofv3 output for the decode library.
+
+  stats    kernel-trace CSV -> short text table (calls, mean / min / max
+           duration per kernel, and the mean over the last N dispatches of a
+           chosen kernel, i.e. the timed launches of a bench run)
+  traffic  FETCH_SIZE / WRITE_SIZE counter CSVs -> HBM bytes per launch of a
+           kernel, each counter scaled by what it reads for a device-to-device
+           copy of known size run in the same process
+
+The counters report KiB per dispatch; the copy calibration turns them into
+bytes whatever request granularity the counter assumes.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import json
+import re
+import statistics
+import sys
+
+from .build import source_sha
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name: str, width: int = 72) -> str:
+    name = re.sub(r"\s+", " ", name)
+    return name if len(name) <= width else name[: width - 3] + "..."
+
+
+def kernel_trace_stats(trace_csv: str, focus: str, last: int):
+    rows = _rows(trace_csv)
+    by = {}
+    for r in rows:
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        by.setdefault(r["Kernel_Name"], []).append((int(r["Start_Timestamp"]), d))
+    table = []
+    for k, v in by.items():
+        ds = [d for _, d in v]
+        table.append((sum(ds), k, len(ds), statistics.mean(ds), min(ds), max(ds)))
+    table.sort(reverse=True)
+    focus_last = None
+    for k, v in by.items():
+        if re.search(focus, k):
+            v = sorted(v)
+            tail = [d for _, d in v[-last:]] if last > 0 else [d for _, d in v]
+            focus_last = (k, len(tail), statistics.mean(tail))
+            break
+    return table, focus_last
+
+
+def cmd_stats(a):
+    table, focus_last = kernel_trace_stats(a.trace, a.focus, a.last)
+    total = sum(t[0] for t in table) or 1.0
+    out = [f"# rocprofv3 kernel trace summary: {a.title}", "",
+           f"command: {a.command}", f"summary: python -m paged_attention_decode_plan_amd.profiling stats "
+           f"--trace <kernel_trace.csv> --focus '{a.focus}' --last {a.last}",
+           f"library source sha: {source_sha()}", "",
+           f"{'kernel':<74} {'calls':>6} {'mean us':>9} {'min us':>9} {'max us':>9} {'% time':>7}"]
+    for tot, k, n, mean, mn, mx in table:
+        out.append(f"{_short(k):<74} {n:>6} {mean:>9.2f} {mn:>9.2f} {mx:>9.2f} {100 * tot / total:>7.2f}")
+    if focus_last:
+        k, n, mean = focus_last
+        out += ["", f"mean of the last {n} dispatches of {_short(k, 60)}: {mean:.2f} us"]
+    text = "\n".join(out) + "\n"
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+    sys.stdout.write(text)
+
+
+def _counter_means(path, counter):
+    vals = {}
+    for r in _rows(path):
+        if r["Counter_Name"] != counter:
+            continue
+        vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def cmd_traffic(a):
+    res = {"kernel": a.kernel, "workload": a.workload, "kernel_sha": source_sha(),
+           "copy_bytes": a.copy_bytes, "command_fetch": a.command_fetch, "command_write": a.command_write}
+    per = {}
+    for counter, path in (("FETCH_SIZE", a.fetch), ("WRITE_SIZE", a.write)):
+        vals = _counter_means(path, counter)
+        kern = [v for k, vs in vals.items() if re.search(a.kernel, k) for v in vs]
+        # the calibration copy is the largest copy-kernel dispatch of the run
+        copy = [v for k, vs in vals.items() if re.search(a.copy_kernel, k) for v in vs]
+        if not kern or not copy:
+            raise SystemExit(f"{counter}: no dispatches of {a.kernel!r} or {a.copy_kernel!r} in {path}")
+        copy_kib = max(copy)
+        factor = a.copy_bytes / (copy_kib * 1024.0)
+        kib = statistics.mean(kern)
+        per[counter] = dict(kib_per_dispatch=kib, dispatches=len(kern), copy_kib=copy_kib, scale=factor,
+                            bytes_per_launch=kib * 1024.0 * factor)
+    res["counters"] = per
+    res["hbm_bytes_per_launch"] = per["FETCH_SIZE"]["bytes_per_launch"] + per["WRITE_SIZE"]["bytes_per_launch"]
+    if a.algorithmic_bytes:
+        res["algorithmic_bytes_per_launch"] = a.algorithmic_bytes
+        res["traffic_over_algorithmic"] = res["hbm_bytes_per_launch"] / a.algorithmic_bytes
+    text = json.dumps(res, indent=1)
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text + "\n")
+    print(text)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(prog="python -m paged_attention_decode_plan_amd.profiling")
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--trace", required=True, help="rocprofv3 *_kernel_trace.csv")
+    s.add_argument("--focus", default="pa_decode_kernel")
+    s.add_argument("--last", type=int, default=0, help="mean over the last N dispatches of the focus kernel")
+    s.add_argument("--title", default="")
+    s.add_argument("--command", default="")
+    s.add_argument("--out")
+    s.set_defaults(fn=cmd_stats)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True, help="counter_collection.csv of the FETCH_SIZE run")
+    t.add_argument("--write", required=True, help="counter_collection.csv of the WRITE_SIZE run")
+    t.add_argument("--kernel", default="pa_decode_kernel")
+    t.add_argument("--copy-kernel", default="copyBuffer")
+    t.add_argument("--copy-bytes", type=float, required=True)
+    t.add_argument("--algorithmic-bytes", type=float, default=0.0)
+    t.add_argument("--workload", default="")
+    t.add_argument("--command-fetch", default="")
+    t.add_argument("--command-write", default="")
+    t.add_argument("--out")
+    t.set_defaults(fn=cmd_traffic)
+    a = ap.parse_args(argv)
+    a.fn(a)
+
+
+if __name__ == "__main__":
+    main()
