@@ -1,0 +1,719 @@
+// gfx950 streaming decode kernel for FP8 caches, head dim 128, and work items
+// of 33..64 query rows (multi-token (MTP) verify rows times a GQA group).
+//
+// Same method as the tile kernel (online softmax per partition, partials
+// merged by the reducer in a fixed order: aiter PR #4332 "Add paged-attention
+// Tile kernel" and aiter PR #7079, "Launch and reducer latency"; scale before
+// mask: aiter PR #6617), laid out differently for bandwidth:
+//
+//  * a workgroup has 4 waves and owns one work item; each 128-token tile of
+//    the item is cut into four 32-token steps and wave w takes step w of every
+//    tile, for all of the item's query rows;
+//  * a wave loads its K, V and per-token scales straight into registers with
+//    16-byte global loads (no LDS staging: on this part LDS-DMA streaming
+//    tops out well below what register loads reach), two steps ahead of the
+//    step it computes (two register buffers, steps taken in pairs), so the
+//    waves never synchronise inside the loop;
+//  * QK^T runs on v_mfma_scale_f32_32x32x64_f8f6f4: the A operand is K as
+//    stored (32 tokens x 64 dims per lane half), the B operand the query
+//    split into three FP8 terms with per-row power-of-two block scales that
+//    also carry softmax_scale * log2(e), so the accumulator holds base-2
+//    logits;
+//  * the QK row of MFMA output register i in lane half h is token 16h + i of
+//    the step (the K rows are fed in that order), which is exactly the token
+//    order of the lane's slots in the PV operand: probabilities go from the
+//    QK accumulator to the PV operand in registers;
+//  * probabilities are taken against a per-row reference maximum set at
+//    the row's first visible tokens (a score more than TAU_S above it makes
+//    the wave redo its share with a larger reference, so the accumulator is
+//    only ever written by MFMAs);
+//  * PV runs on v_mfma_scale_f32_32x32x64_f8f6f4 with V as stored: each
+//    probability (times its per-token V scale) is split into two FP8 terms
+//    hi + lo/16 under a power-of-two exponent per (row, step).  Bytes 0-15 of
+//    every lane of an operand column form one E8M0-scaled k-block and bytes
+//    16-31 the other (the block scales come from lane halves 0 and 1), so a
+//    lane puts its 16 tokens' high terms in bytes 0-15, their low terms in
+//    bytes 16-31, and the V operand repeats the same 16 tokens in both: one
+//    MFMA per accumulator and step applies both terms.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+constexpr int SW = 4;  // waves per workgroup
+// Scores may exceed a row's reference maximum by this much (base 2) before
+// the wave restarts: probabilities are FP8 with a per-block exponent here, so
+// the bound only keeps them finite in FP32.
+constexpr float TAU_S = 64.0f;
+
+template <int RB>
+struct StreamSmem {
+  static constexpr int ROWS = 32 * RB;
+  static constexpr int OROW = 128 + 4;  // padded O row, floats
+  static constexpr int OBUF = ROWS * OROW * 4;
+  static constexpr int MERGE = SW * OBUF;  // one O buffer per wave
+  static constexpr int IDS = kStageCap * 4;
+  static constexpr int SCALES = SW * 64 * 4;  // per wave: 32 k scales, 32 v scales of its step
+  static constexpr int STATS = (SW * ROWS * 2 + SW + ROWS * 4) * 4;
+  static constexpr int TOTAL = MERGE + IDS + SCALES + STATS;
+};
+
+// Step data of one wave, loaded one step ahead.
+struct StepData {
+  i32x8 k[2];  // K chunks 2h, 2h+1 (dims 0..63) and 2h+4, 2h+5 (dims 64..127) of token kt
+  u32x4 v[4];  // V dim 32db + c32, tokens 16h .. 16h+15 of the step
+  float sc;    // lanes 0-31: k scale of token c32; lanes 32-63: v scale of token c32
+};
+
+__device__ __forceinline__ i32x8 load32(const uint8_t* p0, const uint8_t* p1) {
+  const u32x4 lo = *(const u32x4*)p0, hi = *(const u32x4*)p1;
+  return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// BIG: page size >= 32 (the 32 tokens of a step share one page).
+template <int RB, bool PT, bool BIG>
+__global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
+  constexpr int D = 128;
+  constexpr int TT = kTileTokens;
+  using S = StreamSmem<RB>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  float* obuf = (float*)smem;
+  int32_t* ids = (int32_t*)(smem + S::MERGE);
+  float* sbuf = (float*)(smem + S::MERGE + S::IDS);
+  float* stats = (float*)(smem + S::MERGE + S::IDS + S::SCALES);
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the same, known wave-uniform
+  const int lane = tid & 63;
+  const int c32 = lane & 31;
+  const int h = lane >> 5;
+
+  const WorkItem it = a.items[blockIdx.x];
+  const int s = it.seq, kvh = it.kvh, rg = it.rg;
+  const int ps = a.page_size;
+  const int ps_log2 = 31 - __builtin_clz(ps);
+  const long cap = (long)a.table_stride * ps;
+  const int L = (int)min(max((long)a.context_lens[s], 0L), cap);
+
+  // Visible span of the sequence (union over its query rows).
+  int lo_u = 0, hi_u = L;
+  if (L > 0 && a.window > 0) {
+    const int first_pos = a.causal ? L - a.QL : L - 1;
+    lo_u = max(0, first_pos - a.window + 1);
+  }
+  const int t0 = (lo_u >> ps_log2) << ps_log2;
+  const int ntiles = hi_u > lo_u ? (hi_u - t0 + TT - 1) / TT : 0;
+  const int tb = min(it.tile_begin, ntiles);
+  const int te = it.tile_end < 0 ? ntiles : min(it.tile_end, ntiles);
+
+  // Rows: lane holds row 32rb + c32 of the item for rb < RB.
+  const int rpg = a.rows_per_group;
+  const int row0 = rg * kMaxRowsPerItem;
+  const int nrows = min(rpg, a.rows_total - row0);
+  int lo_r[RB], hi_r[RB];
+  bool valid[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = 32 * rb + c32;
+    valid[rb] = r < nrows;
+    if (valid[rb]) {
+      const int i = (row0 + r) / a.G;
+      const int pos = a.causal ? L - a.QL + i : L - 1;
+      hi_r[rb] = min(pos, L - 1);
+      lo_r[rb] = a.window > 0 ? max(0, pos - a.window + 1) : 0;
+    } else {
+      lo_r[rb] = 1;
+      hi_r[rb] = 0;
+    }
+  }
+  // A tile inside [lo_max, hi_min] is visible to every row of the item.
+  int lo_max, hi_min;
+  {
+    const int i_first = row0 / a.G, i_last = (row0 + nrows - 1) / a.G;
+    const int pos_first = a.causal ? L - a.QL + i_first : L - 1;
+    const int pos_last = a.causal ? L - a.QL + i_last : L - 1;
+    hi_min = min(pos_first, L - 1);
+    lo_max = a.window > 0 ? max(0, pos_last - a.window + 1) : 0;
+  }
+
+  // ---- page ids of the item into LDS ----
+  const int ppt = TT >> ps_log2;  // pages per tile
+  const long id0 = ((long)t0 >> ps_log2) + (long)tb * ppt;
+  const long id_end = ((long)hi_u + ps - 1) >> ps_log2;  // one past the last page with visible tokens
+  const int nstaged = (int)max(0L, min((long)a.stage_limit, min((long)(te - tb) * ppt, id_end - id0)));
+  const int32_t* bt_row = a.block_tables + (long)s * a.table_stride;
+  for (int k = tid; k < nstaged; k += 256) ids[k] = bt_row[id0 + k];
+
+  // ---- query operand: three FP8 terms per row with a power-of-two scale ----
+  // Row r is scaled by c = softmax_scale*log2(e) (* k_scale for per-tensor
+  // scales) and by 2^-e with e chosen so that |c q / 2^e| < 448; the three
+  // terms hi + mid/16 + lo/256 carry about 12 significant bits and enter the
+  // MFMA with E8M0 block scales 2^e, 2^(e-4), 2^(e-8).  The workgroup splits
+  // the rows once into LDS (thread = row tid/4, dims 32*(tid%4) ..+31, laid
+  // out as the reading lanes want them: lane half h of k-step ks holds dims
+  // 64ks + 32h .. +31, the same dims as its K operand); every wave then keeps
+  // keeps all of the item's fragments in accumulator registers.
+  uint8_t* qlds = smem;  // [RB][2 ks][3 terms][64 lanes][32 B]; the merge buffers reuse it after the loop
+  int* qexp = (int*)(smem + RB * 2 * 3 * 64 * 32);  // [ROWS] E8M0 of the hi term
+  {
+    const float cbase = a.scale_log2 * (PT ? 1.0f : a.k_scale[0]);
+    const int r = tid >> 2, qq = tid & 3;  // 64 rows x 4 quarters
+    const bool rvalid = r < nrows && r < S::ROWS;
+    const int gr = row0 + (rvalid ? r : 0);
+    const int i = gr / a.G, hl = gr % a.G;
+    const long qoff = (((long)s * a.QL + i) * a.Hq + (long)kvh * a.G + hl) * D + 32 * qq;
+    const uint16_t* qrow = (const uint16_t*)a.q + qoff;
+    float qv[32];
+#pragma unroll
+    for (int part = 0; part < 4; ++part) {
+      const u32x4 raw = rvalid ? *(const u32x4*)(qrow + 8 * part) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const uint16_t bits = (uint16_t)(raw[p >> 1] >> (16 * (p & 1)));
+        qv[8 * part + p] =
+            a.q_fp16 ? (float)__builtin_bit_cast(_Float16, bits) : __uint_as_float((uint32_t)bits << 16);
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(qv[j]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));  // the row's four quarters are adjacent lanes
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    const float cq = amax * cbase;
+    int e = 0;
+    float mul = 0.f;
+    if (cq > 0.f && cq < INFINITY) {
+      int ex;
+      (void)frexpf(cq * (1.0f / FP8_MAX), &ex);  // cq/448 < 2^ex
+      e = min(max(ex, -119), 127);
+      mul = ldexpf(cbase, -e);
+    }
+    if (qq == 0 && r < S::ROWS) qexp[r] = 127 + e;
+    const int rb = r >> 5, ks = qq >> 1, hh = qq & 1;
+    uint8_t* dst = qlds + ((size_t)((rb * 2 + ks) * 3) * 64 + 32 * hh + (r & 31)) * 32;
+    if (r < S::ROWS) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 t0v, t1v, t2v;
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          int w0 = 0, w1 = 0, w2 = 0;
+          float r1[4], r2[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            r1[x] = fminf(fmaxf(qv[16 * half + 4 * j4 + x] * mul, -FP8_MAX), FP8_MAX);
+          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(r1[0], r1[1], w0, false);
+          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(r1[2], r1[3], w0, true);
+          {
+            const float hv[4] = {__builtin_amdgcn_cvt_f32_fp8(w0, 0), __builtin_amdgcn_cvt_f32_fp8(w0, 1),
+                                 __builtin_amdgcn_cvt_f32_fp8(w0, 2), __builtin_amdgcn_cvt_f32_fp8(w0, 3)};
+#pragma unroll
+            for (int x = 0; x < 4; ++x) r2[x] = (r1[x] - hv[x]) * 16.0f;
+          }
+          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(r2[0], r2[1], w1, false);
+          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(r2[2], r2[3], w1, true);
+          {
+            const float hv[4] = {__builtin_amdgcn_cvt_f32_fp8(w1, 0), __builtin_amdgcn_cvt_f32_fp8(w1, 1),
+                                 __builtin_amdgcn_cvt_f32_fp8(w1, 2), __builtin_amdgcn_cvt_f32_fp8(w1, 3)};
+#pragma unroll
+            for (int x = 0; x < 4; ++x) r1[x] = (r2[x] - hv[x]) * 16.0f;
+          }
+          w2 = __builtin_amdgcn_cvt_pk_fp8_f32(r1[0], r1[1], w2, false);
+          w2 = __builtin_amdgcn_cvt_pk_fp8_f32(r1[2], r1[3], w2, true);
+          t0v[j4] = (uint32_t)w0;
+          t1v[j4] = (uint32_t)w1;
+          t2v[j4] = (uint32_t)w2;
+        }
+        *(u32x4*)(dst + 0 * 64 * 32 + 16 * half) = t0v;
+        *(u32x4*)(dst + 1 * 64 * 32 + 16 * half) = t1v;
+        *(u32x4*)(dst + 2 * 64 * 32 + 16 * half) = t2v;
+      }
+    }
+  }
+  __syncthreads();
+  int qsc[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) qsc[rb] = qexp[32 * rb + c32];
+  // fragment (rb, ks, term) of this lane, read from LDS where it is used
+  auto qfrag = [&](int rb, int ks, int t) -> i32x8 {
+    const uint8_t* src = qlds + ((size_t)((rb * 2 + ks) * 3 + t) * 64 + lane) * 32;
+    const u32x4 lo = *(const u32x4*)src, hi = *(const u32x4*)(src + 16);
+    return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // ---- softmax state ----
+  // Rows that are padding start with a finite reference so that no path has
+  // to special-case them; they are never written out.  O holds
+  // sum_t p_t * v_scale(t) * v_t for per-token scales and sum_t p_t v_t for a
+  // per-tensor scale (applied at the end).
+  float m_ref[RB], m_hi[RB], l_acc[RB];
+  f32x16 o[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_ref[rb] = valid[rb] ? -INFINITY : 0.f;
+    m_hi[rb] = -INFINITY;
+  }
+  const float vs_out = PT ? 1.0f : a.v_scale[0];
+
+  const uint8_t* kbase = a.k_cache + (long long)kvh * a.head_stride;
+  const uint8_t* vbase = a.v_cache + (long long)kvh * a.head_stride;
+  float* ssl = sbuf + w * 64;  // this wave's scale slot
+
+  __syncthreads();  // staged ids visible
+
+  // ---- loads of one step ----
+  // QK A-operand row c32 is token kt of the step: MFMA output register i of
+  // lane half h is then token 16h + i, and lane (c32, h) loads V of dim
+  // 32db + c32 for exactly those 16 tokens (into both halves of its operand).
+  const int kt = ((c32 >> 2) & 1) * 16 + (c32 >> 3) * 4 + (c32 & 3);
+  auto page_ok = [&](long j) {  // id index j (relative to id0) holds visible tokens
+    const long tok0 = (long)t0 + ((j + (long)tb * ppt) << ps_log2);
+    return tok0 < hi_u && tok0 + ps > lo_u;
+  };
+  // id of page j: staged in LDS, past the staged bound from the block table;
+  // pages without visible tokens read page 0 of the head (masked later)
+  auto page_id = [&](long j) -> long {
+    if (!page_ok(j)) return 0;
+    if (j < nstaged) return (long)ids[j];
+    return (long)__builtin_nontemporal_load(bt_row + id0 + j);
+  };
+  // Lane-constant parts of the addresses (page >= 32: a step lies in one page)
+  const int slot_k = (32 * w + kt) & (ps - 1);
+  const uint32_t koff = (uint32_t)((2 * h * ps + slot_k) * 16);
+  const uint32_t kcs = (uint32_t)ps * 16;  // K chunk stride
+  const int slot_v = (32 * w + 16 * h) & (ps - 1);
+  uint32_t voff[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int dd = 32 * db + c32;
+    voff[db] = a.v_transposed ? (uint32_t)(((slot_v >> 4) * D + dd) * 16) : (uint32_t)(dd * ps + slot_v);
+  }
+  const uint32_t soff = (uint32_t)((kvh * ps + ((32 * w + c32) & (ps - 1))) * 4);
+  const float* sbase = h ? a.v_scale : a.k_scale;
+
+  // The loads of step k are issued in two parts: K and the scales once the
+  // QK MFMAs of the step before have consumed its K registers, V once its PV
+  // MFMAs have consumed its V registers; each part then has a whole step to
+  // arrive and lands in the registers it replaces.
+  auto step_page = [&](int k) -> long {  // page id of step k (page >= 32: wave-uniform)
+    const long j = (long)((k - tb) * TT + 32 * wu) >> ps_log2;
+    // each source is read and made uniform in its own branch, so waiting for
+    // the rare block-table read never waits for the K/V loads in flight
+    if (!page_ok(j)) return 0;
+    if (j < nstaged) return __builtin_amdgcn_readfirstlane(ids[j]);
+    // past the staged bound: a scalar read of the block table (the table is
+    // constant for the kernel's lifetime), counted apart from the K/V loads
+    const __attribute__((address_space(4))) int32_t* btc =
+        (const __attribute__((address_space(4))) int32_t*)bt_row;
+    return btc[id0 + j];
+  };
+  auto load_k = [&](StepData& d, int k, long id) {
+    const int ts_rel = (k - tb) * TT + 32 * w;  // step start relative to the item's first tile
+    if constexpr (BIG) {
+      const uint8_t* kp = kbase + id * a.page_stride;
+      d.k[0] = load32(kp + koff, kp + koff + kcs);
+      d.k[1] = load32(kp + koff + 4 * kcs, kp + koff + 5 * kcs);
+      if constexpr (PT) d.sc = *(const float*)((const uint8_t*)(sbase + id * a.Hkv * ps) + soff);
+    } else {
+      // page 16: the step spans two pages; addresses per lane
+      const int tk = ts_rel + kt;
+      const long idk = page_id(tk >> ps_log2);
+      const uint8_t* src = kbase + idk * a.page_stride + (long)(tk & (ps - 1)) * 16;
+      d.k[0] = load32(src + (2 * h) * kcs, src + (2 * h + 1) * kcs);
+      d.k[1] = load32(src + (2 * h + 4) * kcs, src + (2 * h + 5) * kcs);
+      if constexpr (PT) {
+        const int tsc = ts_rel + c32;
+        const long ids_ = page_id(tsc >> ps_log2);
+        d.sc = sbase[(ids_ * a.Hkv + kvh) * ps + (tsc & (ps - 1))];
+      }
+    }
+    if constexpr (!PT) d.sc = 0.f;
+  };
+  auto load_v = [&](StepData& d, int k, long id) {
+    const int ts_rel = (k - tb) * TT + 32 * w;
+    if constexpr (BIG) {
+      const uint8_t* vp = vbase + id * a.page_stride;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) d.v[db] = *(const u32x4*)(vp + voff[db]);
+    } else {
+      const long idv = page_id((ts_rel + 16 * h) >> ps_log2);  // the lane's 16 tokens: one page
+      const uint8_t* pg = vbase + idv * a.page_stride;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint8_t* src = pg + (long)(32 * db + c32) * 16;  // page 16: both V layouts put a dim's 16 bytes here
+        d.v[db] = *(const u32x4*)src;
+      }
+    }
+  };
+
+  // Tiles [ti0, ti1) are visible to every row; their steps skip the masks
+  // once every row has a reference maximum.
+  int ti0, ti1;
+  {
+    const int first = lo_max > t0 ? (lo_max - t0 + TT - 1) / TT : 0;
+    const int last = hi_min - t0 - (TT - 1) >= 0 ? (hi_min - t0 - (TT - 1)) / TT + 1 : 0;
+    ti0 = min(max(first, tb), te);
+    ti1 = max(min(last, te), ti0);
+  }
+
+  // ---- one step ----
+  // `gen` (wave-uniform): a boundary step, with masks and reference updates.
+  // The step's registers in `cur` are refilled with step k+2 (two steps of
+  // loads in flight per wave); steps past the item reload its last step's
+  // cached pages, so the loads are unconditional and the compiler's wait
+  // counts stay exact.  A step k >= te (padding an odd count) masks every
+  // token.
+  // Returns false when the wave has to restart with a larger reference.
+  bool ovf = false;
+  auto step = [&](auto GENc, StepData& cur, int k) -> bool {
+    constexpr bool gen = decltype(GENc)::value;
+    const int tsa = t0 + k * TT + 32 * w;  // first token of the step
+    const int tl = tsa + 16 * h;           // first of the lane's 16 tokens
+    const bool live = k < te;  // the empty step that pads an odd count masks everything
+    const int span_lo = live ? lo_u : 0, span_hi = live ? hi_u : 0;  // tokens whose V may be used
+    if constexpr (PT) ssl[lane] = cur.sc;
+    const int kn = min(k + 2, te - 1);
+    const long nid = BIG ? step_page(kn) : 0;
+
+    // V of the step (the operand is built where PV needs it: a copy made
+    // here would wait for the loads in flight)
+    u32x4 vv[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) vv[db] = cur.v[db];
+
+    // S^T = K Q^T
+    const i32x8 kf0 = cur.k[0], kf1 = cur.k[1];
+    f32x16 sacc[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf0, qfrag(rb, 0, t), acc, 0, 0, 0, 127, 0,
+                                                              qsc[rb] - 4 * t);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf1, qfrag(rb, 1, t), acc, 0, 0, 0, 127, 0,
+                                                              qsc[rb] - 4 * t);
+      }
+      sacc[rb] = acc;
+    }
+    load_k(cur, kn, nid);  // this step's K is in the MFMAs
+
+    // per-token scales of the lane's 16 tokens
+    float ks16[16], vs16[16];
+    float vmax = 1.0f;  // bound of the V scale (per-tensor: applied at the end)
+    if constexpr (PT) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f4 kq = *(const f4*)(ssl + 16 * h + 4 * q);
+        const f4 vq = *(const f4*)(ssl + 32 + 16 * h + 4 * q);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          ks16[4 * q + x] = kq[x];
+          vs16[4 * q + x] = vq[x];
+        }
+      }
+      if constexpr (gen) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int t = tl + i;
+          vs16[i] = (t >= span_lo && t < span_hi) ? vs16[i] : 0.f;
+        }
+      }
+      vmax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) vmax = fmaxf(vmax, vs16[i]);
+      vmax = fmax_swap32(vmax);  // over the step's 32 tokens
+    }
+
+    // tokens outside the visible span get zero V (their bytes may be
+    // anything, and 0 * NaN would reach O)
+    if constexpr (gen) {
+      const int va = min(max(span_lo - tl, 0), 16), vb = min(max(span_hi - tl, 0), 16);
+      if (va > 0 || vb < 16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t m = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int t = 4 * q + b;
+            if (t >= va && t < vb) m |= 0xFFu << (8 * b);
+          }
+#pragma unroll
+          for (int db = 0; db < 4; ++db) vv[db][q] &= m;
+        }
+      }
+    }
+
+    // probabilities -> two FP8 terms -> PV
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float y[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        y[i] = sacc[rb][i];
+        if constexpr (PT) y[i] *= ks16[i];
+      }
+      if constexpr (gen) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int t = tl + i;
+          y[i] = (live && t >= lo_r[rb] && t <= hi_r[rb]) ? y[i] : -INFINITY;
+          mx = fmaxf(mx, y[i]);
+        }
+        mx = fmax_swap32(mx);  // the partner lane holds the row's other 16 tokens
+        if (m_ref[rb] == -INFINITY) {
+          m_ref[rb] = mx;  // the row's first visible tokens: its O is still zero
+        } else if (mx > m_ref[rb] + TAU_S) {
+          ovf = true;
+          m_hi[rb] = fmaxf(m_hi[rb], mx);
+        }
+      }
+      const float nm = m_ref[rb] == -INFINITY ? 0.f : -m_ref[rb];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = __builtin_amdgcn_exp2f(y[i] + nm);  // exp2(-inf) = 0
+      float ls = y[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) ls += y[i];
+      l_acc[rb] += ls;
+      // a probability above 2^TAU_S shows in the lane's sum; the bound
+      // m_ref + log2(sum) is at least the step's maximum
+      if (ls > 0x1p64f) {
+        ovf = true;
+        m_hi[rb] = fmaxf(m_hi[rb], m_ref[rb] + __builtin_amdgcn_logf(ls));
+      }
+      if constexpr (PT) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y[i] *= vs16[i];
+      }
+      // Block exponent of the row's 32 scaled probabilities: every value is
+      // at most (sum of the row's p over the step) * (largest V scale) =
+      // bound = m 2^e with m in [0.5, 1), so value * 2^(8-e) < 256 <= 448.
+      const float bound = fadd_swap32(ls) * vmax;
+      const int a = min(max(8 - __builtin_amdgcn_frexp_expf(bound), -100), 100);
+      const float s_hi = __uint_as_float((uint32_t)(127 - a) << 23);      // 2^-a
+      const float s_lo = __uint_as_float((uint32_t)(127 - a - 4) << 23);  // 2^-(a+4)
+      typedef short s2 __attribute__((ext_vector_type(2)));
+      i32x8 pop;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        s2 hw = __builtin_nondeterministic_value(hw), lw = __builtin_nondeterministic_value(lw);
+        hw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hw, y[4 * q], y[4 * q + 1], s_hi, false);
+        hw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hw, y[4 * q + 2], y[4 * q + 3], s_hi, true);
+        const uint32_t hu = (uint32_t)(uint16_t)hw[0] | ((uint32_t)(uint16_t)hw[1] << 16);
+        const f2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hu, s_hi, false);
+        const f2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hu, s_hi, true);
+        lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw, y[4 * q] - b0[0], y[4 * q + 1] - b0[1], s_lo, false);
+        lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw, y[4 * q + 2] - b1[0], y[4 * q + 3] - b1[1], s_lo, true);
+        // bytes 0-15: high terms (block scale 2^-a from lane half 0); bytes
+        // 16-31: low terms (2^-(a+4) from lane half 1); a is the same in
+        // both lanes of the row
+        pop[q] = (int)hu;
+        pop[4 + q] = (int)((uint32_t)(uint16_t)lw[0] | ((uint32_t)(uint16_t)lw[1] << 16));
+      }
+      const int psc = (h ? 123 : 127) - a;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const i32x8 vop = __builtin_bit_cast(i32x8, __builtin_shufflevector(vv[db], vv[db], 0, 1, 2, 3, 0, 1, 2, 3));
+        o[rb][db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, o[rb][db], 0, 0, 0, 127, 0, psc);
+      }
+    }
+    load_v(cur, kn, nid);  // this step's V is in the MFMAs
+    return !__builtin_amdgcn_ballot_w64(ovf);
+  };
+
+  // One pass of this wave over the item, two steps per iteration with one
+  // load buffer each (an odd count ends with an empty step).  An overflow
+  // stops it at the top of the next pair (a single latch keeps each O
+  // accumulator in place across iterations).
+  auto attempt = [&]() -> bool {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      l_acc[rb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[rb][db] = f32x16{};
+    }
+    if (tb >= te) return true;
+    StepData ba, bb;
+    {
+      const long p0 = BIG ? step_page(tb) : 0;
+      load_k(ba, tb, p0);
+      load_v(ba, tb, p0);
+      const int k1 = min(tb + 1, te - 1);
+      const long p1 = BIG ? step_page(k1) : 0;
+      load_k(bb, k1, p1);
+      load_v(bb, k1, p1);
+    }
+    // Pairs of steps: boundary pairs (masks, reference updates) until the
+    // interior tiles are reached with every row's reference set, interior
+    // pairs, then boundary pairs again.  Each loop is entered with nothing
+    // in flight beyond its two buffers' loads, which keeps the compiler's
+    // wait counts exact inside it.
+    bool go = true;  // wave-uniform
+    int k = tb;
+    auto pair = [&](auto GENc) {
+      go = step(GENc, ba, k);
+      __builtin_amdgcn_sched_barrier(0);  // the two steps do not interleave (registers)
+      go = step(GENc, bb, k + 1) && go;
+      __builtin_amdgcn_sched_barrier(0);
+      k += 2;
+    };
+    for (; k < te && go;) {
+      bool need_ref = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) need_ref |= m_ref[rb] == -INFINITY;
+      if (k >= ti0 && k + 1 < ti1 && !__builtin_amdgcn_ballot_w64(need_ref)) break;
+      pair(std::true_type{});
+    }
+    for (; k + 1 < ti1 && go;) pair(std::false_type{});
+    for (; k < te && go;) pair(std::true_type{});
+    return go;
+  };
+  for (;;) {
+    if (attempt()) break;
+    wait_vmcnt<0>();  // loads issued past the stop
+    // restart this wave's share with references at least the maxima seen
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float mh = fmax_swap32(m_hi[rb]);
+      if (mh > m_ref[rb]) m_ref[rb] = mh;
+      m_hi[rb] = -INFINITY;
+    }
+    ovf = false;
+  }
+
+  // ---- merge the four waves' states ----
+  constexpr int NR = S::ROWS;
+  float* wm = stats;                    // [SW][NR] reference maxima
+  float* wl = stats + SW * NR;          // [SW][NR] sums
+  float* rowinfo = stats + 2 * SW * NR + SW;  // [NR][4]: M, L, direct-output factor
+  float lrow[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) lrow[rb] = fadd_swap32(l_acc[rb]);
+  if (h == 0) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      wm[w * NR + 32 * rb + c32] = m_ref[rb];
+      wl[w * NR + 32 * rb + c32] = lrow[rb];
+    }
+  }
+  __syncthreads();
+  float* ob = obuf + w * (S::OBUF / 4);
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = 32 * rb + c32;
+    float M = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < SW; ++x)
+      if (wl[x * NR + r] > 0.f) M = fmaxf(M, wm[x * NR + r]);
+    const float fw = lrow[rb] > 0.f ? __builtin_amdgcn_exp2f(m_ref[rb] - M) * vs_out : 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f4 v = f4{o[rb][db][4 * q], o[rb][db][4 * q + 1], o[rb][db][4 * q + 2], o[rb][db][4 * q + 3]} * fw;
+        *(f4*)(ob + r * S::OROW + 32 * db + 8 * q + 4 * h) = v;
+      }
+  }
+  if (tid < NR) {
+    const int r = tid;
+    float M = -INFINITY, Lt = 0.f;
+#pragma unroll
+    for (int x = 0; x < SW; ++x)
+      if (wl[x * NR + r] > 0.f) M = fmaxf(M, wm[x * NR + r]);
+#pragma unroll
+    for (int x = 0; x < SW; ++x) {
+      const float lw = wl[x * NR + r];
+      if (lw > 0.f) Lt += lw * __builtin_amdgcn_exp2f(wm[x * NR + r] - M);
+    }
+    float factor = 0.f;
+    if (Lt > 0.f) {
+      if (a.has_sinks) {
+        const int gr = row0 + (r < nrows ? r : 0);
+        const int hh = kvh * a.G + gr % a.G;
+        const float sk = a.sinks[hh] * LOG2E;
+        const float M2 = fmaxf(M, sk);
+        const float sc = __builtin_amdgcn_exp2f(M - M2);
+        factor = sc / (Lt * sc + __builtin_amdgcn_exp2f(sk - M2));
+      } else {
+        factor = 1.0f / Lt;
+      }
+    }
+    rowinfo[r * 4 + 0] = M;
+    rowinfo[r * 4 + 1] = Lt;
+    rowinfo[r * 4 + 2] = factor;
+  }
+  __syncthreads();
+
+  // ---- write: partial state or final rows ----
+  auto osum = [&](int r, int d4) {
+    f4 acc = *(const f4*)(obuf + r * S::OROW + d4);
+#pragma unroll
+    for (int x = 1; x < SW; ++x) acc += *(const f4*)(obuf + x * (S::OBUF / 4) + r * S::OROW + d4);
+    return acc;
+  };
+  if (it.slot >= 0) {
+    float* sp = a.workspace + (size_t)it.slot * rpg * (2 + D);
+    if (tid < nrows) {
+      sp[tid] = rowinfo[tid * 4 + 0];
+      sp[rpg + tid] = rowinfo[tid * 4 + 1];
+    }
+    float* po = sp + 2 * rpg;
+    for (int e = tid; e < nrows * (D / 4); e += 256) {
+      const int r = e / (D / 4), d4 = (e % (D / 4)) * 4;
+      *(f4*)(po + (size_t)r * D + d4) = osum(r, d4);
+    }
+  } else {
+    for (int e = tid; e < nrows * (D / 4); e += 256) {
+      const int r = e / (D / 4), d4 = (e % (D / 4)) * 4;
+      const f4 v = osum(r, d4) * rowinfo[r * 4 + 2];
+      const int gr = row0 + r, i = gr / a.G, hl = gr % a.G;
+      const long ooff = (((long)s * a.QL + i) * a.Hq + (long)kvh * a.G + hl) * D + d4;
+      uint16_t hv[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        hv[x] = a.q_fp16 ? __builtin_bit_cast(uint16_t, (_Float16)v[x]) : __builtin_bit_cast(uint16_t, (__bf16)v[x]);
+      *(u32x2*)((uint16_t*)a.out + ooff) =
+          u32x2{(uint32_t)hv[0] | ((uint32_t)hv[1] << 16), (uint32_t)hv[2] | ((uint32_t)hv[3] << 16)};
+    }
+  }
+}
+
+template <int RB, bool PT, bool BIG>
+static pa_status launch_stream_t(const KernelArgs& args, int nblocks, hipStream_t stream) {
+  constexpr int bytes = StreamSmem<RB>::TOTAL;
+  static_assert(bytes <= 160 * 1024, "LDS budget");
+  static bool configured = false;
+  if (!configured) {
+    if (hipFuncSetAttribute((const void*)pa_stream_kernel<RB, PT, BIG>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      return set_error(PA_ERR_DEVICE, "hipFuncSetAttribute failed");
+    }
+    configured = true;
+  }
+  hipLaunchKernelGGL((pa_stream_kernel<RB, PT, BIG>), dim3(nblocks), dim3(256), bytes, stream, args);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return set_error(PA_ERR_DEVICE, std::string("decode launch failed: ") + hipGetErrorString(err));
+  return PA_OK;
+}
+
+bool stream_kernel_applies(const Plan& P) {
+  const pa_problem& p = P.prob;
+  return p.kv_dtype == PA_FP8_E4M3FN && p.head_dim == 128 && !p.token_table && P.rows_per_group > 32;
+}
+
+pa_status launch_stream(const Plan& P, const KernelArgs& args, int nblocks, hipStream_t stream) {
+  const bool pt = P.prob.scale_mode == PA_SCALE_PER_TOKEN;
+  if (P.prob.page_size >= 32)
+    return pt ? launch_stream_t<2, true, true>(args, nblocks, stream) : launch_stream_t<2, false, true>(args, nblocks, stream);
+  return pt ? launch_stream_t<2, true, false>(args, nblocks, stream) : launch_stream_t<2, false, false>(args, nblocks, stream);
+}
+
+}  // namespace pa
