@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   // MFMA with E8M0 block scales 2^e, 2^(e-4), 2^(e-8).  The workgroup splits
   // the rows once into LDS (thread = row tid/4, dims 32*(tid%4) ..+31, laid
   // out as the reading lanes want them: lane half h of k-step ks holds dims
-  // 64ks + 32h .. +31, the same dims as its K operand); every wave then keeps
+  // 64ks + 32h .. +31, the same dims as its K operand); every wave then
   // keeps all of the item's fragments in accumulator registers.
   uint8_t* qlds = smem;  // [RB][2 ks][3 terms][64 lanes][32 B]; the merge buffers reuse it after the loop
   int* qexp = (int*)(smem + RB * 2 * 3 * 64 * 32);  // [ROWS] E8M0 of the hi term
@@ -238,14 +238,21 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   }
   __syncthreads();
   int qsc[RB];
+  i32x8 qf[RB][2][3];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) qsc[rb] = qexp[32 * rb + c32];
-  // fragment (rb, ks, term) of this lane, read from LDS where it is used
-  auto qfrag = [&](int rb, int ks, int t) -> i32x8 {
-    const uint8_t* src = qlds + ((size_t)((rb * 2 + ks) * 3 + t) * 64 + lane) * 32;
-    const u32x4 lo = *(const u32x4*)src, hi = *(const u32x4*)(src + 16);
-    return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
+  for (int rb = 0; rb < RB; ++rb) {
+    qsc[rb] = qexp[32 * rb + c32];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        const uint8_t* src = qlds + ((size_t)((rb * 2 + ks) * 3 + t) * 64 + lane) * 32;
+        const u32x4 lo = *(const u32x4*)src, hi = *(const u32x4*)(src + 16);
+        qf[rb][ks][t] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        asm volatile("" : "+a"(qf[rb][ks][t]));  // kept in accumulator registers for the whole loop
+      }
+  }
+  auto qfrag = [&](int rb, int ks, int t) -> i32x8 { return qf[rb][ks][t]; };
 
   // ---- softmax state ----
   // Rows that are padding start with a finite reference so that no path has
@@ -387,11 +394,9 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) vv[db] = cur.v[db];
 
-    // S^T = K Q^T
+    // S^T = K Q^T for one 32-row block
     const i32x8 kf0 = cur.k[0], kf1 = cur.k[1];
-    f32x16 sacc[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+    auto qk = [&](int rb) {
       f32x16 acc = {};
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
@@ -400,63 +405,46 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
         acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf1, qfrag(rb, 1, t), acc, 0, 0, 0, 127, 0,
                                                               qsc[rb] - 4 * t);
       }
-      sacc[rb] = acc;
-    }
-    load_k(cur, kn, nid);  // this step's K is in the MFMAs
+      return acc;
+    };
 
     // per-token scales of the lane's 16 tokens
     float ks16[16], vs16[16];
     float vmax = 1.0f;  // bound of the V scale (per-tensor: applied at the end)
-    if constexpr (PT) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f4 kq = *(const f4*)(ssl + 16 * h + 4 * q);
-        const f4 vq = *(const f4*)(ssl + 32 + 16 * h + 4 * q);
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          ks16[4 * q + x] = kq[x];
-          vs16[4 * q + x] = vq[x];
-        }
-      }
-      if constexpr (gen) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int t = tl + i;
-          vs16[i] = (t >= span_lo && t < span_hi) ? vs16[i] : 0.f;
-        }
-      }
-      vmax = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) vmax = fmaxf(vmax, vs16[i]);
-      vmax = fmax_swap32(vmax);  // over the step's 32 tokens
-    }
-
-    // tokens outside the visible span get zero V (their bytes may be
-    // anything, and 0 * NaN would reach O)
-    if constexpr (gen) {
-      const int va = min(max(span_lo - tl, 0), 16), vb = min(max(span_hi - tl, 0), 16);
-      if (va > 0 || vb < 16) {
+    auto scales = [&]() {
+      if constexpr (PT) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          uint32_t m = 0;
+          const f4 kq = *(const f4*)(ssl + 16 * h + 4 * q);
+          const f4 vq = *(const f4*)(ssl + 32 + 16 * h + 4 * q);
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const int t = 4 * q + b;
-            if (t >= va && t < vb) m |= 0xFFu << (8 * b);
+          for (int x = 0; x < 4; ++x) {
+            ks16[4 * q + x] = kq[x];
+            vs16[4 * q + x] = vq[x];
           }
-#pragma unroll
-          for (int db = 0; db < 4; ++db) vv[db][q] &= m;
         }
-      }
-    }
-
-    // probabilities -> two FP8 terms -> PV
+        if constexpr (gen) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+          for (int i = 0; i < 16; ++i) {
+            const int t = tl + i;
+            vs16[i] = (t >= span_lo && t < span_hi) ? vs16[i] : 0.f;
+          }
+        }
+        vmax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) vmax = fmaxf(vmax, vs16[i]);
+        vmax = fmax_swap32(vmax);  // over the step's 32 tokens
+      }
+    };
+
+    // probabilities of one row block -> PV operand (two FP8 terms) and its
+    // block scales; branch-free so that the MFMAs of the other row block can
+    // be interleaved with it
+    auto probs = [&](int rb, const f32x16& sa, i32x8& pop, int& psc) {
       float y[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        y[i] = sacc[rb][i];
+        y[i] = sa[i];
         if constexpr (PT) y[i] *= ks16[i];
       }
       if constexpr (gen) {
@@ -468,12 +456,12 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
           mx = fmaxf(mx, y[i]);
         }
         mx = fmax_swap32(mx);  // the partner lane holds the row's other 16 tokens
-        if (m_ref[rb] == -INFINITY) {
-          m_ref[rb] = mx;  // the row's first visible tokens: its O is still zero
-        } else if (mx > m_ref[rb] + TAU_S) {
-          ovf = true;
-          m_hi[rb] = fmaxf(m_hi[rb], mx);
-        }
+        // the row's first visible tokens set its reference (its O is still zero)
+        const bool first = m_ref[rb] == -INFINITY;
+        const bool over = !first && mx > m_ref[rb] + TAU_S;
+        ovf |= over;
+        m_hi[rb] = over ? fmaxf(m_hi[rb], mx) : m_hi[rb];
+        m_ref[rb] = first ? mx : m_ref[rb];
       }
       const float nm = m_ref[rb] == -INFINITY ? 0.f : -m_ref[rb];
 #pragma unroll
@@ -484,10 +472,9 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       l_acc[rb] += ls;
       // a probability above 2^TAU_S shows in the lane's sum; the bound
       // m_ref + log2(sum) is at least the step's maximum
-      if (ls > 0x1p64f) {
-        ovf = true;
-        m_hi[rb] = fmaxf(m_hi[rb], m_ref[rb] + __builtin_amdgcn_logf(ls));
-      }
+      const bool big = ls > 0x1p64f;
+      ovf |= big;
+      m_hi[rb] = big ? fmaxf(m_hi[rb], m_ref[rb] + __builtin_amdgcn_logf(ls)) : m_hi[rb];
       if constexpr (PT) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) y[i] *= vs16[i];
@@ -500,7 +487,6 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       const float s_hi = __uint_as_float((uint32_t)(127 - a) << 23);      // 2^-a
       const float s_lo = __uint_as_float((uint32_t)(127 - a - 4) << 23);  // 2^-(a+4)
       typedef short s2 __attribute__((ext_vector_type(2)));
-      i32x8 pop;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         s2 hw = __builtin_nondeterministic_value(hw), lw = __builtin_nondeterministic_value(lw);
@@ -517,13 +503,61 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
         pop[q] = (int)hu;
         pop[4 + q] = (int)((uint32_t)(uint16_t)lw[0] | ((uint32_t)(uint16_t)lw[1] << 16));
       }
-      const int psc = (h ? 123 : 127) - a;
+      psc = (h ? 123 : 127) - a;
+    };
+    auto pv = [&](int rb, const i32x8& pop, int psc) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const i32x8 vop = __builtin_bit_cast(i32x8, __builtin_shufflevector(vv[db], vv[db], 0, 1, 2, 3, 0, 1, 2, 3));
         o[rb][db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, o[rb][db], 0, 0, 0, 127, 0, psc);
       }
+    };
+
+    // tokens outside the visible span get zero V (their bytes may be
+    // anything, and 0 * NaN would reach O)
+    if constexpr (gen) {
+      const int va = min(max(span_lo - tl, 0), 16), vb = min(max(span_hi - tl, 0), 16);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int t = 4 * q + b;
+          if (t >= va && t < vb) m |= 0xFFu << (8 * b);
+        }
+#pragma unroll
+        for (int db = 0; db < 4; ++db) vv[db][q] &= m;
+      }
     }
+
+    // Schedule (one wave per SIMD, so the overlap has to come from within
+    // the wave): QK of row block 0; QK of row block 1 interleaved with the
+    // probabilities of block 0; PV of block 0 interleaved with the
+    // probabilities of block 1; PV of block 1.
+    static_assert(RB == 2, "the schedule below is written for two row blocks");
+    i32x8 pop0, pop1;
+    int psc0, psc1;
+    const f32x16 sa0 = qk(0);
+    __builtin_amdgcn_sched_barrier(0);
+    const f32x16 sa1 = qk(1);
+    load_k(cur, kn, nid);  // this step's K is in the MFMAs
+    scales();
+    probs(0, sa0, pop0, psc0);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 22, 0); // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    pv(0, pop0, psc0);
+    probs(1, sa1, pop1, psc1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 32, 1); // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    pv(1, pop1, psc1);
     load_v(cur, kn, nid);  // this step's V is in the MFMAs
     return !__builtin_amdgcn_ballot_w64(ovf);
   };
