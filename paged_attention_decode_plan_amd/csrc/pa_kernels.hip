@@ -937,11 +937,19 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(ReduceArgs a) {
     f4 acc = f4{0.f, 0.f, 0.f, 0.f};
     const float f = rowf[rr];
     if (f > 0.f) {
-      for (int p = 0; p < e.nparts; ++p) {
-        float wp = wgt[rr][p];
-        if (wp == 0.f) continue;
-        const float* sp = a.workspace + (size_t)(e.first_slot + p) * slot_f;
-        acc += wp * *(const f4*)(sp + 2 * rpg + (size_t)r * D + d4);
+      // eight partitions' loads in flight at a time (a load per partition
+      // and round trip would make the merge latency-bound); partitions
+      // without visible tokens are skipped by a select, not a branch
+      const float* base = a.workspace + (size_t)e.first_slot * slot_f + 2 * rpg + (size_t)r * D + d4;
+      for (int p0 = 0; p0 < e.nparts; p0 += 8) {
+        f4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = *(const f4*)(base + (size_t)min(p0 + j, e.nparts - 1) * slot_f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float wp = p0 + j < e.nparts ? wgt[rr][p0 + j] : 0.f;
+          if (wp != 0.f) acc += wp * v[j];
+        }
       }
     }
     f4 v = acc * f;

@@ -14,11 +14,12 @@
 //    tops out well below what register loads reach), two steps ahead of the
 //    step it computes (two register buffers, steps taken in pairs), so the
 //    waves never synchronise inside the loop;
-//  * QK^T runs on v_mfma_scale_f32_32x32x64_f8f6f4: the A operand is K as
-//    stored (32 tokens x 64 dims per lane half), the B operand the query
-//    split into three FP8 terms with per-row power-of-two block scales that
-//    also carry softmax_scale * log2(e), so the accumulator holds base-2
-//    logits;
+//  * QK^T runs on v_mfma_f32_32x32x16_f16: K converts exactly to FP16 in
+//    registers, the query is FP16 with softmax_scale * log2(e) (and a
+//    per-tensor k scale) folded in, so the accumulator holds base-2 logits;
+//    per-token k scales multiply them in the FMA that also subtracts the
+//    reference maximum (the scaled conversions take only a power-of-two
+//    scale);
 //  * the QK row of MFMA output register i in lane half h is token 16h + i of
 //    the step (the K rows are fed in that order), which is exactly the token
 //    order of the lane's slots in the PV operand: probabilities go from the
@@ -27,14 +28,10 @@
 //    the row's first visible tokens (a score more than TAU_S above it makes
 //    the wave redo its share with a larger reference, so the accumulator is
 //    only ever written by MFMAs);
-//  * PV runs on v_mfma_scale_f32_32x32x64_f8f6f4 with V as stored: each
-//    probability (times its per-token V scale) is split into two FP8 terms
-//    hi + lo/16 under a power-of-two exponent per (row, step).  Bytes 0-15 of
-//    every lane of an operand column form one E8M0-scaled k-block and bytes
-//    16-31 the other (the block scales come from lane halves 0 and 1), so a
-//    lane puts its 16 tokens' high terms in bytes 0-15, their low terms in
-//    bytes 16-31, and the V operand repeats the same 16 tokens in both: one
-//    MFMA per accumulator and step applies both terms.
+//  * PV runs on v_mfma_f32_32x32x16_f16: with per-token scales, the step's
+//    largest V scale sets a power of two 2^E; V converts exactly to FP16 as
+//    v * 2^E, and each probability times its token's V scale * 2^-E (at most
+//    1) is rounded once to FP16 (11 significant bits).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -47,9 +44,13 @@ namespace pa {
 
 constexpr int SW = 4;  // waves per workgroup
 // Scores may exceed a row's reference maximum by this much (base 2) before
-// the wave restarts: probabilities are FP8 with a per-block exponent here, so
-// the bound only keeps them finite in FP32.
-constexpr float TAU_S = 64.0f;
+// the wave restarts: a probability (times a V scale normalised to below 1)
+// then stays below 2^15, inside FP16.
+constexpr float TAU_S = 15.0f;
+// The V conversion scale 2^E of a step is clamped to [2^-15, 2^6]: every FP8
+// value times it is exact in FP16 (the smallest subnormal lands on 2^-24, the
+// largest finite value stays below 2^15).
+constexpr int VEXP_MIN = -15, VEXP_MAX = 6;
 
 template <int RB>
 struct StreamSmem {
@@ -63,12 +64,18 @@ struct StreamSmem {
   static constexpr int TOTAL = MERGE + IDS + SCALES + STATS;
 };
 
-// Step data of one wave, loaded one step ahead.
+// Step data of one wave, loaded two steps ahead.
 struct StepData {
   i32x8 k[2];  // K chunks 2h, 2h+1 (dims 0..63) and 2h+4, 2h+5 (dims 64..127) of token kt
   u32x4 v[4];  // V dim 32db + c32, tokens 16h .. 16h+15 of the step
   float sc;    // lanes 0-31: k scale of token c32; lanes 32-63: v scale of token c32
 };
+
+// x of another lane of the 16-lane row (DPP control CTRL: quad permutes, mirrors)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
 
 __device__ __forceinline__ i32x8 load32(const uint8_t* p0, const uint8_t* p1) {
   const u32x4 lo = *(const u32x4*)p0, hi = *(const u32x4*)p1;
@@ -150,17 +157,17 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   const int32_t* bt_row = a.block_tables + (long)s * a.table_stride;
   for (int k = tid; k < nstaged; k += 256) ids[k] = bt_row[id0 + k];
 
-  // ---- query operand: three FP8 terms per row with a power-of-two scale ----
-  // Row r is scaled by c = softmax_scale*log2(e) (* k_scale for per-tensor
-  // scales) and by 2^-e with e chosen so that |c q / 2^e| < 448; the three
-  // terms hi + mid/16 + lo/256 carry about 12 significant bits and enter the
-  // MFMA with E8M0 block scales 2^e, 2^(e-4), 2^(e-8).  The workgroup splits
-  // the rows once into LDS (thread = row tid/4, dims 32*(tid%4) ..+31, laid
-  // out as the reading lanes want them: lane half h of k-step ks holds dims
-  // 64ks + 32h .. +31, the same dims as its K operand); every wave then
-  // keeps all of the item's fragments in accumulator registers.
-  uint8_t* qlds = smem;  // [RB][2 ks][3 terms][64 lanes][32 B]; the merge buffers reuse it after the loop
-  int* qexp = (int*)(smem + RB * 2 * 3 * 64 * 32);  // [ROWS] E8M0 of the hi term
+  // ---- query operand: FP16 ----
+  // Rows are scaled by c = softmax_scale*log2(e) (* k_scale for per-tensor
+  // scales) and, should the item's largest |c q| reach 2^14, by 2^-e for the
+  // whole item, e undone by the K conversion (K * 2^e), so that FP16 never
+  // overflows.  The workgroup converts the rows once into LDS (thread = row
+  // tid/4, dims 32*(tid%4) ..+31), laid out as the reading lanes want them:
+  // MFMA k-step j takes, in lane half h, the 8 dims 64(j/4) + 32h + 8(j%4)
+  // ..+7, the same dims as the lane's K operand; every wave then keeps all of
+  // the item's fragments in accumulator registers.
+  uint8_t* qlds = smem;  // [RB][8 k-steps][64 lanes][16 B]; the merge buffers reuse it after the loop
+  float kmul;            // 2^e
   {
     const float cbase = a.scale_log2 * (PT ? 1.0f : a.k_scale[0]);
     const int r = tid >> 2, qq = tid & 3;  // 64 rows x 4 quarters
@@ -183,76 +190,40 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     float amax = 0.f;
 #pragma unroll
     for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(qv[j]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1));  // the row's four quarters are adjacent lanes
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    const float cq = amax * cbase;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if (lane == 0) stats[w] = amax;
+    __syncthreads();
+    const float cq = fmaxf(fmaxf(stats[0], stats[1]), fmaxf(stats[2], stats[3])) * cbase;
     int e = 0;
-    float mul = 0.f;
-    if (cq > 0.f && cq < INFINITY) {
+    if (cq >= 0x1p14f && cq < INFINITY) {
       int ex;
-      (void)frexpf(cq * (1.0f / FP8_MAX), &ex);  // cq/448 < 2^ex
-      e = min(max(ex, -119), 127);
-      mul = ldexpf(cbase, -e);
+      (void)frexpf(cq * 0x1p-14f, &ex);  // cq * 2^-14 < 2^ex
+      e = min(ex, 100);
     }
-    if (qq == 0 && r < S::ROWS) qexp[r] = 127 + e;
-    const int rb = r >> 5, ks = qq >> 1, hh = qq & 1;
-    uint8_t* dst = qlds + ((size_t)((rb * 2 + ks) * 3) * 64 + 32 * hh + (r & 31)) * 32;
+    const float mul = ldexpf(cbase, -e);
+    kmul = ldexpf(1.0f, e);
     if (r < S::ROWS) {
+      const int rb = r >> 5;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        u32x4 t0v, t1v, t2v;
+      for (int x = 0; x < 4; ++x) {
+        half8 hv;
 #pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) {
-          int w0 = 0, w1 = 0, w2 = 0;
-          float r1[4], r2[4];
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-            r1[x] = fminf(fmaxf(qv[16 * half + 4 * j4 + x] * mul, -FP8_MAX), FP8_MAX);
-          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(r1[0], r1[1], w0, false);
-          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(r1[2], r1[3], w0, true);
-          {
-            const float hv[4] = {__builtin_amdgcn_cvt_f32_fp8(w0, 0), __builtin_amdgcn_cvt_f32_fp8(w0, 1),
-                                 __builtin_amdgcn_cvt_f32_fp8(w0, 2), __builtin_amdgcn_cvt_f32_fp8(w0, 3)};
-#pragma unroll
-            for (int x = 0; x < 4; ++x) r2[x] = (r1[x] - hv[x]) * 16.0f;
-          }
-          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(r2[0], r2[1], w1, false);
-          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(r2[2], r2[3], w1, true);
-          {
-            const float hv[4] = {__builtin_amdgcn_cvt_f32_fp8(w1, 0), __builtin_amdgcn_cvt_f32_fp8(w1, 1),
-                                 __builtin_amdgcn_cvt_f32_fp8(w1, 2), __builtin_amdgcn_cvt_f32_fp8(w1, 3)};
-#pragma unroll
-            for (int x = 0; x < 4; ++x) r1[x] = (r2[x] - hv[x]) * 16.0f;
-          }
-          w2 = __builtin_amdgcn_cvt_pk_fp8_f32(r1[0], r1[1], w2, false);
-          w2 = __builtin_amdgcn_cvt_pk_fp8_f32(r1[2], r1[3], w2, true);
-          t0v[j4] = (uint32_t)w0;
-          t1v[j4] = (uint32_t)w1;
-          t2v[j4] = (uint32_t)w2;
-        }
-        *(u32x4*)(dst + 0 * 64 * 32 + 16 * half) = t0v;
-        *(u32x4*)(dst + 1 * 64 * 32 + 16 * half) = t1v;
-        *(u32x4*)(dst + 2 * 64 * 32 + 16 * half) = t2v;
+        for (int p = 0; p < 8; ++p) hv[p] = (_Float16)(qv[8 * x + p] * mul);
+        const int j = 4 * (qq >> 1) + x;
+        *(half8*)(qlds + ((size_t)((rb * 8 + j) * 64 + 32 * (qq & 1) + (r & 31))) * 16) = hv;
       }
     }
   }
   __syncthreads();
-  int qsc[RB];
-  i32x8 qf[RB][2][3];
+  half8 qf[RB][8];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    qsc[rb] = qexp[32 * rb + c32];
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int t = 0; t < 3; ++t) {
-        const uint8_t* src = qlds + ((size_t)((rb * 2 + ks) * 3 + t) * 64 + lane) * 32;
-        const u32x4 lo = *(const u32x4*)src, hi = *(const u32x4*)(src + 16);
-        qf[rb][ks][t] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        asm volatile("" : "+a"(qf[rb][ks][t]));  // kept in accumulator registers for the whole loop
-      }
-  }
-  auto qfrag = [&](int rb, int ks, int t) -> i32x8 { return qf[rb][ks][t]; };
+    for (int j = 0; j < 8; ++j) {
+      qf[rb][j] = *(const half8*)(qlds + ((size_t)((rb * 8 + j) * 64 + lane)) * 16);
+      asm volatile("" : "+a"(qf[rb][j]));  // kept in accumulator registers for the whole loop
+    }
 
   // ---- softmax state ----
   // Rows that are padding start with a finite reference so that no path has
@@ -384,33 +355,85 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     const int tl = tsa + 16 * h;           // first of the lane's 16 tokens
     const bool live = k < te;  // the empty step that pads an odd count masks everything
     const int span_lo = live ? lo_u : 0, span_hi = live ? hi_u : 0;  // tokens whose V may be used
-    if constexpr (PT) ssl[lane] = cur.sc;
     const int kn = min(k + 2, te - 1);
     const long nid = BIG ? step_page(kn) : 0;
 
-    // V of the step (the operand is built where PV needs it: a copy made
-    // here would wait for the loads in flight)
+    // K of the step in FP16 (k-step j = bytes 8j..8j+7 of the lane's 64),
+    // times the query's 2^e (exact); per-token k scales multiply the logits
+    half8 kf[8];
+    {
+      const float kscale = kmul;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t d0 = (uint32_t)cur.k[j >> 2][2 * (j & 3)], d1 = (uint32_t)cur.k[j >> 2][2 * (j & 3) + 1];
+        const h2 x0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, kscale, false);
+        const h2 x1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, kscale, true);
+        const h2 x2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, kscale, false);
+        const h2 x3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, kscale, true);
+        kf[j] = half8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+      }
+    }
+    // Per-token scales: 2^E from the step's largest V scale (lanes 32-63 hold
+    // the 32 V scales); the V scales go to LDS divided by 2^E.
+    float vconv = 1.0f;
+    if constexpr (PT) {
+      float x = fmax_swap32(h ? cur.sc : 0.f);  // every lane: v scale of token c32
+      x = fmaxf(x, dpp_f<0xB1>(x));             // quad: lanes ^1
+      x = fmaxf(x, dpp_f<0x4E>(x));             // quad: lanes ^2
+      x = fmaxf(x, dpp_f<0x141>(x));            // half-row mirror
+      x = fmaxf(x, dpp_f<0x140>(x));            // row mirror
+      x = fmax_swap16(x);                       // both 16-lane rows: the step's 32 tokens
+      const int e = min(max(__builtin_amdgcn_frexp_expf(x), VEXP_MIN), VEXP_MAX);
+      vconv = __uint_as_float((uint32_t)(127 + e) << 23);
+      ssl[lane] = h ? cur.sc * __uint_as_float((uint32_t)(127 - e) << 23) : cur.sc;
+    }
+    load_k(cur, kn, nid);  // this step's K and scales are in registers
+
+    // V of the step; tokens outside the visible span get zero V (their bytes
+    // may be anything, and 0 * NaN would reach O)
     u32x4 vv[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) vv[db] = cur.v[db];
+    if constexpr (gen) {
+      const int va = min(max(span_lo - tl, 0), 16), vb = min(max(span_hi - tl, 0), 16);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int t = 4 * q + b;
+          if (t >= va && t < vb) m |= 0xFFu << (8 * b);
+        }
+#pragma unroll
+        for (int db = 0; db < 4; ++db) vv[db][q] &= m;
+      }
+    }
 
     // S^T = K Q^T for one 32-row block
-    const i32x8 kf0 = cur.k[0], kf1 = cur.k[1];
     auto qk = [&](int rb) {
       f32x16 acc = {};
 #pragma unroll
-      for (int t = 0; t < 3; ++t) {
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf0, qfrag(rb, 0, t), acc, 0, 0, 0, 127, 0,
-                                                              qsc[rb] - 4 * t);
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf1, qfrag(rb, 1, t), acc, 0, 0, 0, 127, 0,
-                                                              qsc[rb] - 4 * t);
-      }
+      for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[j], qf[rb][j], acc, 0, 0, 0);
       return acc;
     };
-
-    // per-token scales of the lane's 16 tokens
+    // V in FP16 (times 2^E): k-block kb of dim 32db + c32 = tokens 16h + 8kb .. +7
+    half8 vb[4][2];
+    auto vcvt = [&]() {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const uint32_t d0 = vv[db][2 * kb], d1 = vv[db][2 * kb + 1];
+          const h2 x0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, vconv, false);
+          const h2 x1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, vconv, true);
+          const h2 x2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, vconv, false);
+          const h2 x3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, vconv, true);
+          vb[db][kb] = half8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+        }
+    };
+    // per-token scales of the lane's 16 tokens (per-tensor: folded into the
+    // query and applied at the end)
     float ks16[16], vs16[16];
-    float vmax = 1.0f;  // bound of the V scale (per-tensor: applied at the end)
     auto scales = [&]() {
       if constexpr (PT) {
 #pragma unroll
@@ -423,31 +446,16 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
             vs16[4 * q + x] = vq[x];
           }
         }
-        if constexpr (gen) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int t = tl + i;
-            vs16[i] = (t >= span_lo && t < span_hi) ? vs16[i] : 0.f;
-          }
-        }
-        vmax = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) vmax = fmaxf(vmax, vs16[i]);
-        vmax = fmax_swap32(vmax);  // over the step's 32 tokens
       }
     };
 
-    // probabilities of one row block -> PV operand (two FP8 terms) and its
-    // block scales; branch-free so that the MFMAs of the other row block can
-    // be interleaved with it
-    auto probs = [&](int rb, const f32x16& sa, i32x8& pop, int& psc) {
+    // probabilities of one row block -> PV operand (FP16); branch-free so
+    // that the MFMAs of the other row block can be interleaved with it
+    auto probs = [&](int rb, const f32x16& sa, half8 (&pb)[2]) {
       float y[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        y[i] = sa[i];
-        if constexpr (PT) y[i] *= ks16[i];
-      }
       if constexpr (gen) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y[i] = PT ? sa[i] * ks16[i] : sa[i];
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -465,100 +473,75 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       }
       const float nm = m_ref[rb] == -INFINITY ? 0.f : -m_ref[rb];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) y[i] = __builtin_amdgcn_exp2f(y[i] + nm);  // exp2(-inf) = 0
-      float ls = y[0];
+      for (int i = 0; i < 16; ++i) {
+        if constexpr (gen) y[i] = y[i] + nm;
+        else y[i] = PT ? __builtin_fmaf(sa[i], ks16[i], nm) : sa[i] + nm;
+        y[i] = __builtin_amdgcn_exp2f(y[i]);  // exp2(-inf) = 0
+      }
+      float t8[8];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) ls += y[i];
+      for (int i = 0; i < 8; ++i) t8[i] = y[2 * i] + y[2 * i + 1];
+      const float ls = ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
       l_acc[rb] += ls;
       // a probability above 2^TAU_S shows in the lane's sum; the bound
       // m_ref + log2(sum) is at least the step's maximum
-      const bool big = ls > 0x1p64f;
+      const bool big = ls > 0x1p15f;
       ovf |= big;
       m_hi[rb] = big ? fmaxf(m_hi[rb], m_ref[rb] + __builtin_amdgcn_logf(ls)) : m_hi[rb];
       if constexpr (PT) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) y[i] *= vs16[i];
       }
-      // Block exponent of the row's 32 scaled probabilities: every value is
-      // at most (sum of the row's p over the step) * (largest V scale) =
-      // bound = m 2^e with m in [0.5, 1), so value * 2^(8-e) < 256 <= 448.
-      const float bound = fadd_swap32(ls) * vmax;
-      const int a = min(max(8 - __builtin_amdgcn_frexp_expf(bound), -100), 100);
-      const float s_hi = __uint_as_float((uint32_t)(127 - a) << 23);      // 2^-a
-      const float s_lo = __uint_as_float((uint32_t)(127 - a - 4) << 23);  // 2^-(a+4)
-      typedef short s2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        s2 hw = __builtin_nondeterministic_value(hw), lw = __builtin_nondeterministic_value(lw);
-        hw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hw, y[4 * q], y[4 * q + 1], s_hi, false);
-        hw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hw, y[4 * q + 2], y[4 * q + 3], s_hi, true);
-        const uint32_t hu = (uint32_t)(uint16_t)hw[0] | ((uint32_t)(uint16_t)hw[1] << 16);
-        const f2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hu, s_hi, false);
-        const f2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hu, s_hi, true);
-        lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw, y[4 * q] - b0[0], y[4 * q + 1] - b0[1], s_lo, false);
-        lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw, y[4 * q + 2] - b1[0], y[4 * q + 3] - b1[1], s_lo, true);
-        // bytes 0-15: high terms (block scale 2^-a from lane half 0); bytes
-        // 16-31: low terms (2^-(a+4) from lane half 1); a is the same in
-        // both lanes of the row
-        pop[q] = (int)hu;
-        pop[4 + q] = (int)((uint32_t)(uint16_t)lw[0] | ((uint32_t)(uint16_t)lw[1] << 16));
-      }
-      psc = (h ? 123 : 127) - a;
-    };
-    auto pv = [&](int rb, const i32x8& pop, int psc) {
+      for (int kb = 0; kb < 2; ++kb) {
+        h2 c[4];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const i32x8 vop = __builtin_bit_cast(i32x8, __builtin_shufflevector(vv[db], vv[db], 0, 1, 2, 3, 0, 1, 2, 3));
-        o[rb][db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, o[rb][db], 0, 0, 0, 127, 0, psc);
+        for (int x = 0; x < 4; ++x) c[x] = __builtin_convertvector(f2{y[8 * kb + 2 * x], y[8 * kb + 2 * x + 1]}, h2);
+        pb[kb] = half8{c[0][0], c[0][1], c[1][0], c[1][1], c[2][0], c[2][1], c[3][0], c[3][1]};
       }
     };
-
-    // tokens outside the visible span get zero V (their bytes may be
-    // anything, and 0 * NaN would reach O)
-    if constexpr (gen) {
-      const int va = min(max(span_lo - tl, 0), 16), vb = min(max(span_hi - tl, 0), 16);
+    auto pv = [&](int rb, const half8 (&pb)[2]) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t m = 0;
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int t = 4 * q + b;
-          if (t >= va && t < vb) m |= 0xFFu << (8 * b);
-        }
-#pragma unroll
-        for (int db = 0; db < 4; ++db) vv[db][q] &= m;
-      }
-    }
+        for (int kb = 0; kb < 2; ++kb)
+          o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[db][kb], pb[kb], o[rb][db], 0, 0, 0);
+    };
 
     // Schedule (one wave per SIMD, so the overlap has to come from within
-    // the wave): QK of row block 0; QK of row block 1 interleaved with the
-    // probabilities of block 0; PV of block 0 interleaved with the
-    // probabilities of block 1; PV of block 1.
+    // the wave): QK of row block 0 with the V conversion; QK of row block 1
+    // with the probabilities of block 0; PV of block 0 with the probabilities
+    // of block 1; PV of block 1 (its MFMAs run on while the next step converts
+    // its K).
     static_assert(RB == 2, "the schedule below is written for two row blocks");
-    i32x8 pop0, pop1;
-    int psc0, psc1;
-    const f32x16 sa0 = qk(0);
-    __builtin_amdgcn_sched_barrier(0);
-    const f32x16 sa1 = qk(1);
-    load_k(cur, kn, nid);  // this step's K is in the MFMAs
-    scales();
-    probs(0, sa0, pop0, psc0);
+    half8 p0[2], p1[2];
+    const f32x16 s0 = qk(0);
+    vcvt();
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
+    for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 22, 0); // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
     }
     __builtin_amdgcn_sched_barrier(0);
-    pv(0, pop0, psc0);
-    probs(1, sa1, pop1, psc1);
+    load_v(cur, kn, nid);  // this step's V is converted
+    const f32x16 s1 = qk(1);
+    scales();
+    probs(0, s0, p0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 32, 1); // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 1);  // VALU
     }
     __builtin_amdgcn_sched_barrier(0);
-    pv(1, pop1, psc1);
-    load_v(cur, kn, nid);  // this step's V is in the MFMAs
+    pv(0, p0);
+    probs(1, s1, p1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 2);  // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    pv(1, p1);
     return !__builtin_amdgcn_ballot_w64(ovf);
   };
 
