@@ -890,25 +890,52 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(ReduceArgs a) {
   const int r0 = chunk * RED_ROWS;
   const size_t slot_f = (size_t)rpg * (2 + D);
   const int tid = threadIdx.x;
-  // per-row weights (one wave per row pair; lanes over partitions)
-  if (tid < 64 * 4) {
-    int wv = tid >> 6, lane = tid & 63;
-    for (int rr = wv; rr < RED_ROWS; rr += 4) {
-      int r = r0 + rr;
-      if (r >= nrows) continue;
-      float M = -INFINITY;
-      for (int p = lane; p < e.nparts; p += 64) {
-        const float* sp = a.workspace + (size_t)(e.first_slot + p) * slot_f;
-        if (sp[rpg + r] > 0.f) M = fmaxf(M, sp[r]);
+  const int np = e.nparts;
+  const float* base = a.workspace + (size_t)e.first_slot * slot_f;
+  const int q4 = D / 4;
+  // The partial O of the thread's first output (row, 4 dims) for the first
+  // eight partitions is loaded before the weights are known, so that the
+  // merge costs one round trip to memory for up to eight partitions.
+  f4 v0[8];
+  {
+    const int rr = tid / q4, d4 = (tid % q4) * 4;
+    const int r = min(r0 + min(rr, RED_ROWS - 1), nrows - 1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v0[j] = *(const f4*)(base + (size_t)min(j, np - 1) * slot_f + 2 * rpg + (size_t)r * D + d4);
+  }
+  // per-row weights: wave w takes rows w and w + 4, lanes over partitions
+  // (p = lane + 64k); both rows' (max, sum) loads are issued together
+  {
+    const int wv = tid >> 6, lane = tid & 63;
+    float mv[2][4], lv[2][4];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int r = min(r0 + wv + 4 * x, nrows - 1);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float* sp = base + (size_t)min(lane + 64 * k, np - 1) * slot_f;
+        mv[x][k] = sp[r];
+        lv[x][k] = sp[rpg + r];
       }
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int rr = wv + 4 * x, r = r0 + rr;
+      if (r >= nrows) continue;  // wave-uniform
+      float M = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (lane + 64 * k < np && lv[x][k] > 0.f) M = fmaxf(M, mv[x][k]);
       for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
       float den = 0.f;
-      for (int p = lane; p < e.nparts; p += 64) {
-        const float* sp = a.workspace + (size_t)(e.first_slot + p) * slot_f;
-        float lp = sp[rpg + r];
-        float wp = (lp > 0.f) ? __builtin_amdgcn_exp2f(sp[r] - M) : 0.f;
-        wgt[rr][p] = wp;
-        den += wp * lp;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int p = lane + 64 * k;
+        if (p < np) {
+          const float wp = lv[x][k] > 0.f ? __builtin_amdgcn_exp2f(mv[x][k] - M) : 0.f;
+          wgt[rr][p] = wp;
+          den += wp * lv[x][k];
+        }
       }
       // fixed-order sum of the denominator terms
       for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
@@ -916,10 +943,10 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(ReduceArgs a) {
         float f = 0.f;
         if (den > 0.f) {
           if (a.has_sinks) {
-            int gr = row0 + r, h = e.kvh * a.G + gr % a.G;
-            float sk = a.sinks[h] * LOG2E;
-            float M2 = fmaxf(M, sk);
-            float sc = __builtin_amdgcn_exp2f(M - M2);
+            const int h = e.kvh * a.G + (row0 + r) % a.G;
+            const float sk = a.sinks[h] * LOG2E;
+            const float M2 = fmaxf(M, sk);
+            const float sc = __builtin_amdgcn_exp2f(M - M2);
             f = sc / (den * sc + __builtin_amdgcn_exp2f(sk - M2));
           } else {
             f = 1.0f / den;
@@ -930,32 +957,37 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(ReduceArgs a) {
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < RED_ROWS * (D / 4); idx += blockDim.x) {
-    int rr = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
-    int r = r0 + rr;
+  for (int idx = tid; idx < RED_ROWS * q4; idx += blockDim.x) {
+    const int rr = idx / q4, d4 = (idx % q4) * 4;
+    const int r = r0 + rr;
     if (r >= nrows) continue;
     f4 acc = f4{0.f, 0.f, 0.f, 0.f};
     const float f = rowf[rr];
     if (f > 0.f) {
-      // eight partitions' loads in flight at a time (a load per partition
-      // and round trip would make the merge latency-bound); partitions
-      // without visible tokens are skipped by a select, not a branch
-      const float* base = a.workspace + (size_t)e.first_slot * slot_f + 2 * rpg + (size_t)r * D + d4;
-      for (int p0 = 0; p0 < e.nparts; p0 += 8) {
+      // eight partitions' loads in flight at a time (the first eight of the
+      // thread's first output are already in v0); partitions without visible
+      // tokens are skipped by a select, not a branch
+      const float* po = base + 2 * rpg + (size_t)r * D + d4;
+      for (int p0 = 0; p0 < np; p0 += 8) {
         f4 v[8];
+        if (p0 == 0 && idx == tid) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = *(const f4*)(base + (size_t)min(p0 + j, e.nparts - 1) * slot_f);
+          for (int j = 0; j < 8; ++j) v[j] = v0[j];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = *(const f4*)(po + (size_t)min(p0 + j, np - 1) * slot_f);
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float wp = p0 + j < e.nparts ? wgt[rr][p0 + j] : 0.f;
+          const float wp = p0 + j < np ? wgt[rr][p0 + j] : 0.f;
           if (wp != 0.f) acc += wp * v[j];
         }
       }
     }
-    f4 v = acc * f;
-    int gr = row0 + r, i = gr / a.G, hl = gr % a.G;
-    int h = e.kvh * a.G + hl;
-    long ooff = (((long)e.seq * a.QL + i) * a.Hq + h) * D + d4;
+    const f4 v = acc * f;
+    const int gr = row0 + r, i = gr / a.G, hl = gr % a.G;
+    const int h = e.kvh * a.G + hl;
+    const long ooff = (((long)e.seq * a.QL + i) * a.Hq + h) * D + d4;
     uint16_t hv[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {

@@ -606,48 +606,55 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   }
 
   // ---- merge the four waves' states ----
+  // Each wave writes its (max, sum) per row and its unscaled O to LDS; one
+  // wave then turns the (max, sum) pairs into per-wave weights
+  // 2^(m_w - M) (the per-tensor V scale folded in) and the row's (M, L,
+  // output factor); every thread finally sums the four weighted O buffers.
   constexpr int NR = S::ROWS;
-  float* wm = stats;                    // [SW][NR] reference maxima
-  float* wl = stats + SW * NR;          // [SW][NR] sums
+  float* wm = stats;                          // [SW][NR] reference maxima, then weights
+  float* wl = stats + SW * NR;                // [SW][NR] sums
   float* rowinfo = stats + 2 * SW * NR + SW;  // [NR][4]: M, L, direct-output factor
-  float lrow[RB];
+  {
+    float lrow[RB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) lrow[rb] = fadd_swap32(l_acc[rb]);
-  if (h == 0) {
+    for (int rb = 0; rb < RB; ++rb) lrow[rb] = fadd_swap32(l_acc[rb]);
+    if (h == 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        wm[w * NR + 32 * rb + c32] = m_ref[rb];
+        wl[w * NR + 32 * rb + c32] = lrow[rb];
+      }
+    }
+    float* ob = obuf + w * (S::OBUF / 4);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      wm[w * NR + 32 * rb + c32] = m_ref[rb];
-      wl[w * NR + 32 * rb + c32] = lrow[rb];
+      const int r = 32 * rb + c32;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *(f4*)(ob + r * S::OROW + 32 * db + 8 * q + 4 * h) =
+              f4{o[rb][db][4 * q], o[rb][db][4 * q + 1], o[rb][db][4 * q + 2], o[rb][db][4 * q + 3]};
     }
   }
   __syncthreads();
-  float* ob = obuf + w * (S::OBUF / 4);
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = 32 * rb + c32;
-    float M = -INFINITY;
-#pragma unroll
-    for (int x = 0; x < SW; ++x)
-      if (wl[x * NR + r] > 0.f) M = fmaxf(M, wm[x * NR + r]);
-    const float fw = lrow[rb] > 0.f ? __builtin_amdgcn_exp2f(m_ref[rb] - M) * vs_out : 0.f;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f4 v = f4{o[rb][db][4 * q], o[rb][db][4 * q + 1], o[rb][db][4 * q + 2], o[rb][db][4 * q + 3]} * fw;
-        *(f4*)(ob + r * S::OROW + 32 * db + 8 * q + 4 * h) = v;
-      }
-  }
   if (tid < NR) {
     const int r = tid;
-    float M = -INFINITY, Lt = 0.f;
-#pragma unroll
-    for (int x = 0; x < SW; ++x)
-      if (wl[x * NR + r] > 0.f) M = fmaxf(M, wm[x * NR + r]);
+    float mv[SW], lv[SW];
 #pragma unroll
     for (int x = 0; x < SW; ++x) {
-      const float lw = wl[x * NR + r];
-      if (lw > 0.f) Lt += lw * __builtin_amdgcn_exp2f(wm[x * NR + r] - M);
+      mv[x] = wm[x * NR + r];
+      lv[x] = wl[x * NR + r];
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < SW; ++x) M = lv[x] > 0.f ? fmaxf(M, mv[x]) : M;
+    float Lt = 0.f;
+#pragma unroll
+    for (int x = 0; x < SW; ++x) {
+      const float fx = lv[x] > 0.f ? __builtin_amdgcn_exp2f(mv[x] - M) : 0.f;
+      Lt += lv[x] * fx;
+      wm[x * NR + r] = fx * vs_out;
     }
     float factor = 0.f;
     if (Lt > 0.f) {
@@ -670,9 +677,9 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
 
   // ---- write: partial state or final rows ----
   auto osum = [&](int r, int d4) {
-    f4 acc = *(const f4*)(obuf + r * S::OROW + d4);
+    f4 acc = *(const f4*)(obuf + r * S::OROW + d4) * wm[r];
 #pragma unroll
-    for (int x = 1; x < SW; ++x) acc += *(const f4*)(obuf + x * (S::OBUF / 4) + r * S::OROW + d4);
+    for (int x = 1; x < SW; ++x) acc += *(const f4*)(obuf + x * (S::OBUF / 4) + r * S::OROW + d4) * wm[x * NR + r];
     return acc;
   };
   if (it.slot >= 0) {
