@@ -63,6 +63,28 @@ __device__ __forceinline__ float fadd_swap32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// x of another lane of the 16-lane row (DPP control CTRL: quad permutes, mirrors)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// max / sum over the whole wave, in registers (butterflies: quad lane ^1 and
+// ^2, half-row and row mirrors, then the 16- and 32-lane swaps); every lane
+// gets the same result
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));
+  x = fmaxf(x, dpp_f<0x4E>(x));
+  x = fmaxf(x, dpp_f<0x141>(x));
+  x = fmaxf(x, dpp_f<0x140>(x));
+  return fmax_swap32(fmax_swap16(x));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x141>(x);
+  x += dpp_f<0x140>(x);
+  return fadd_swap32(fadd_swap16(x));
+}
 // max / sum over the four 16-lane groups (lanes c, c+16, c+32, c+48)
 __device__ __forceinline__ float group_max(float x) { return fmax_swap32(fmax_swap16(x)); }
 __device__ __forceinline__ float group_sum(float x) { return fadd_swap32(fadd_swap16(x)); }

@@ -907,9 +907,10 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(ReduceArgs a) {
   // (p = lane + 64k); both rows' (max, sum) loads are issued together
   {
     const int wv = tid >> 6, lane = tid & 63;
-    float mv[2][4], lv[2][4];
+    float mv[2][4], lv[2][4], skv[2] = {0.f, 0.f};
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
+      if (a.has_sinks) skv[x] = a.sinks[e.kvh * a.G + (row0 + min(r0 + wv + 4 * x, nrows - 1)) % a.G];
       const int r = min(r0 + wv + 4 * x, nrows - 1);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -926,7 +927,7 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(ReduceArgs a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         if (lane + 64 * k < np && lv[x][k] > 0.f) M = fmaxf(M, mv[x][k]);
-      for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+      M = wave_max(M);
       float den = 0.f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -937,14 +938,12 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(ReduceArgs a) {
           den += wp * lv[x][k];
         }
       }
-      // fixed-order sum of the denominator terms
-      for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
+      den = wave_sum(den);  // fixed-order sum of the denominator terms
       if (lane == 0) {
         float f = 0.f;
         if (den > 0.f) {
           if (a.has_sinks) {
-            const int h = e.kvh * a.G + (row0 + r) % a.G;
-            const float sk = a.sinks[h] * LOG2E;
+            const float sk = skv[x] * LOG2E;
             const float M2 = fmaxf(M, sk);
             const float sc = __builtin_amdgcn_exp2f(M - M2);
             f = sc / (den * sc + __builtin_amdgcn_exp2f(sk - M2));

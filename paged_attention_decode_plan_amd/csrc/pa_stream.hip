@@ -71,11 +71,6 @@ struct StepData {
   float sc;    // lanes 0-31: k scale of token c32; lanes 32-63: v scale of token c32
 };
 
-// x of another lane of the 16-lane row (DPP control CTRL: quad permutes, mirrors)
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
 
 __device__ __forceinline__ i32x8 load32(const uint8_t* p0, const uint8_t* p1) {
   const u32x4 lo = *(const u32x4*)p0, hi = *(const u32x4*)p1;
@@ -279,11 +274,13 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   // QK MFMAs of the step before have consumed its K registers, V once its PV
   // MFMAs have consumed its V registers; each part then has a whole step to
   // arrive and lands in the registers it replaces.
+  const int idv = lane < nstaged ? ids[lane] : 0;  // the first 64 staged ids, one per lane
   auto step_page = [&](int k) -> long {  // page id of step k (page >= 32: wave-uniform)
     const long j = (long)((k - tb) * TT + 32 * wu) >> ps_log2;
     // each source is read and made uniform in its own branch, so waiting for
     // the rare block-table read never waits for the K/V loads in flight
     if (!page_ok(j)) return 0;
+    if (j < 64 && j < nstaged) return __builtin_amdgcn_readlane(idv, (int)j);  // no memory access
     if (j < nstaged) return __builtin_amdgcn_readfirstlane(ids[j]);
     // past the staged bound: a scalar read of the block table (the table is
     // constant for the kernel's lifetime), counted apart from the K/V loads
@@ -349,7 +346,26 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   // token.
   // Returns false when the wave has to restart with a larger reference.
   bool ovf = false;
-  auto step = [&](auto GENc, StepData& cur, int k) -> bool {
+  // V conversion scale of the next step: with per-token scales, 2^E comes
+  // from the step's largest V scale (lanes 32-63 hold its 32 V scales), and
+  // the scales go to LDS with the V scales divided by 2^E.  Done at the end
+  // of the step before, under its last MFMAs.
+  float vconv = 1.0f;
+  auto prep = [&](const StepData& nb) {
+    if constexpr (PT) {
+      float x = fmax_swap32(h ? nb.sc : 0.f);  // every lane: v scale of token c32
+      x = fmaxf(x, dpp_f<0xB1>(x));            // quad: lanes ^1
+      x = fmaxf(x, dpp_f<0x4E>(x));            // quad: lanes ^2
+      x = fmaxf(x, dpp_f<0x141>(x));           // half-row mirror
+      x = fmaxf(x, dpp_f<0x140>(x));           // row mirror
+      x = fmax_swap16(x);                      // both 16-lane rows: the step's 32 tokens
+      const int e = min(max(__builtin_amdgcn_frexp_expf(x), VEXP_MIN), VEXP_MAX);
+      vconv = __uint_as_float((uint32_t)(127 + e) << 23);
+      ssl[lane] = h ? nb.sc * __uint_as_float((uint32_t)(127 - e) << 23) : nb.sc;
+    }
+  };
+
+  auto step = [&](auto GENc, StepData& cur, const StepData& nxt, int k) -> bool {
     constexpr bool gen = decltype(GENc)::value;
     const int tsa = t0 + k * TT + 32 * w;  // first token of the step
     const int tl = tsa + 16 * h;           // first of the lane's 16 tokens
@@ -361,33 +377,16 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     // K of the step in FP16 (k-step j = bytes 8j..8j+7 of the lane's 64),
     // times the query's 2^e (exact); per-token k scales multiply the logits
     half8 kf[8];
-    {
-      const float kscale = kmul;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t d0 = (uint32_t)cur.k[j >> 2][2 * (j & 3)], d1 = (uint32_t)cur.k[j >> 2][2 * (j & 3) + 1];
-        const h2 x0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, kscale, false);
-        const h2 x1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, kscale, true);
-        const h2 x2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, kscale, false);
-        const h2 x3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, kscale, true);
-        kf[j] = half8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
-      }
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t d0 = (uint32_t)cur.k[j >> 2][2 * (j & 3)], d1 = (uint32_t)cur.k[j >> 2][2 * (j & 3) + 1];
+      const h2 x0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, kmul, false);
+      const h2 x1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, kmul, true);
+      const h2 x2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, kmul, false);
+      const h2 x3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, kmul, true);
+      kf[j] = half8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
     }
-    // Per-token scales: 2^E from the step's largest V scale (lanes 32-63 hold
-    // the 32 V scales); the V scales go to LDS divided by 2^E.
-    float vconv = 1.0f;
-    if constexpr (PT) {
-      float x = fmax_swap32(h ? cur.sc : 0.f);  // every lane: v scale of token c32
-      x = fmaxf(x, dpp_f<0xB1>(x));             // quad: lanes ^1
-      x = fmaxf(x, dpp_f<0x4E>(x));             // quad: lanes ^2
-      x = fmaxf(x, dpp_f<0x141>(x));            // half-row mirror
-      x = fmaxf(x, dpp_f<0x140>(x));            // row mirror
-      x = fmax_swap16(x);                       // both 16-lane rows: the step's 32 tokens
-      const int e = min(max(__builtin_amdgcn_frexp_expf(x), VEXP_MIN), VEXP_MAX);
-      vconv = __uint_as_float((uint32_t)(127 + e) << 23);
-      ssl[lane] = h ? cur.sc * __uint_as_float((uint32_t)(127 - e) << 23) : cur.sc;
-    }
-    load_k(cur, kn, nid);  // this step's K and scales are in registers
+    load_k(cur, kn, nid);  // this step's K is converted, its scales are in LDS
 
     // V of the step; tokens outside the visible span get zero V (their bytes
     // may be anything, and 0 * NaN would reach O)
@@ -509,10 +508,9 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     };
 
     // Schedule (one wave per SIMD, so the overlap has to come from within
-    // the wave): QK of row block 0 with the V conversion; QK of row block 1
-    // with the probabilities of block 0; PV of block 0 with the probabilities
-    // of block 1; PV of block 1 (its MFMAs run on while the next step converts
-    // its K).
+    // the wave): QK of row block 0 with the K and V conversions; QK of row
+    // block 1 with the probabilities of block 0; PV of block 0 with the
+    // probabilities of block 1; PV of block 1 with the next step's scales.
     static_assert(RB == 2, "the schedule below is written for two row blocks");
     half8 p0[2], p1[2];
     const f32x16 s0 = qk(0);
@@ -520,7 +518,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
     }
     __builtin_amdgcn_sched_barrier(0);
     load_v(cur, kn, nid);  // this step's V is converted
@@ -542,6 +540,13 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
     pv(1, p1);
+    prep(nxt);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 3);  // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
     return !__builtin_amdgcn_ballot_w64(ovf);
   };
 
@@ -567,6 +572,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       load_k(bb, k1, p1);
       load_v(bb, k1, p1);
     }
+    prep(ba);
     // Pairs of steps: boundary pairs (masks, reference updates) until the
     // interior tiles are reached with every row's reference set, interior
     // pairs, then boundary pairs again.  Each loop is entered with nothing
@@ -575,9 +581,9 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     bool go = true;  // wave-uniform
     int k = tb;
     auto pair = [&](auto GENc) {
-      go = step(GENc, ba, k);
+      go = step(GENc, ba, bb, k);
       __builtin_amdgcn_sched_barrier(0);  // the two steps do not interleave (registers)
-      go = step(GENc, bb, k + 1) && go;
+      go = step(GENc, bb, ba, k + 1) && go;
       __builtin_amdgcn_sched_barrier(0);
       k += 2;
     };
