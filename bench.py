@@ -52,14 +52,14 @@ def log(msg):
 def load_traffic(workload: str, launches_kv_bytes: float):
     """HBM bytes per decode launch from committed rocprofv3 counter runs, if
     they were taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"pa_decode_kernel_{workload}_traffic.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        t = json.load(f)
-    if t.get("kernel_sha") != source_sha():
-        return None
-    return t.get("hbm_bytes_per_launch")
+    import glob
+
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}_traffic.json"))):
+        with open(path) as f:
+            t = json.load(f)
+        if t.get("kernel_sha") == source_sha():
+            return t.get("hbm_bytes_per_launch")
+    return None
 
 
 def make_inputs(workload: str):

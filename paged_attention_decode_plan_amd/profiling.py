@@ -116,7 +116,7 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("--trace", required=True, help="rocprofv3 *_kernel_trace.csv")
-    s.add_argument("--focus", default="pa_decode_kernel")
+    s.add_argument("--focus", default="pa_stream_kernel|pa_decode_kernel")
     s.add_argument("--last", type=int, default=0, help="mean over the last N dispatches of the focus kernel")
     s.add_argument("--title", default="")
     s.add_argument("--command", default="")
@@ -125,7 +125,7 @@ def main(argv=None):
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True, help="counter_collection.csv of the FETCH_SIZE run")
     t.add_argument("--write", required=True, help="counter_collection.csv of the WRITE_SIZE run")
-    t.add_argument("--kernel", default="pa_decode_kernel")
+    t.add_argument("--kernel", default="pa_stream_kernel|pa_decode_kernel")
     t.add_argument("--copy-kernel", default="copyBuffer")
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--algorithmic-bytes", type=float, default=0.0)
