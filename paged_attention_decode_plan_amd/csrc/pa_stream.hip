@@ -31,7 +31,8 @@
 //  * PV runs on v_mfma_f32_32x32x16_f16: with per-token scales, the step's
 //    largest V scale sets a power of two 2^E; V converts exactly to FP16 as
 //    v * 2^E, and each probability times its token's V scale * 2^-E (at most
-//    1) is rounded once to FP16 (11 significant bits).
+//    1 unless E hit its clamp) is rounded once to FP16 (11 significant bits);
+//    an operand that would reach 2^15 makes the wave restart.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -155,14 +156,15 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   // ---- query operand: FP16 ----
   // Rows are scaled by c = softmax_scale*log2(e) (* k_scale for per-tensor
   // scales) and, should the item's largest |c q| reach 2^14, by 2^-e for the
-  // whole item, e undone by the K conversion (K * 2^e), so that FP16 never
-  // overflows.  The workgroup converts the rows once into LDS (thread = row
+  // whole item, so that FP16 never overflows; the logits get the 2^e back
+  // (folded into the per-token k scales, or the multiplier of the FMA that
+  // subtracts the reference maximum).  The workgroup converts the rows once into LDS (thread = row
   // tid/4, dims 32*(tid%4) ..+31), laid out as the reading lanes want them:
   // MFMA k-step j takes, in lane half h, the 8 dims 64(j/4) + 32h + 8(j%4)
   // ..+7, the same dims as the lane's K operand; every wave then keeps all of
   // the item's fragments in accumulator registers.
   uint8_t* qlds = smem;  // [RB][8 k-steps][64 lanes][16 B]; the merge buffers reuse it after the loop
-  float kmul;            // 2^e
+  float lmul;            // 2^e: logit multiplier
   {
     const float cbase = a.scale_log2 * (PT ? 1.0f : a.k_scale[0]);
     const int r = tid >> 2, qq = tid & 3;  // 64 rows x 4 quarters
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       e = min(ex, 100);
     }
     const float mul = ldexpf(cbase, -e);
-    kmul = ldexpf(1.0f, e);
+    lmul = ldexpf(1.0f, e);
     if (r < S::ROWS) {
       const int rb = r >> 5;
 #pragma unroll
@@ -348,20 +350,29 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   bool ovf = false;
   // V conversion scale of the next step: with per-token scales, 2^E comes
   // from the step's largest V scale (lanes 32-63 hold its 32 V scales), and
-  // the scales go to LDS with the V scales divided by 2^E.  Done at the end
-  // of the step before, under its last MFMAs.
-  float vconv = 1.0f;
-  auto prep = [&](const StepData& nb) {
+  // the scales go to LDS with the V scales divided by 2^E (and the k scales
+  // times the query's 2^e).  E is clamped so that every V value is exact in
+  // FP16; above the clamp the normalised V scales exceed 1, and vsmax (their
+  // largest) enters the overflow check of the probabilities.  Done at the
+  // end of the step before, under its last MFMAs.
+  float vconv = 1.0f, vsmax = 1.0f;
+  // V scales of tokens outside the visible span (their bytes may be
+  // anything) count as 0, in the maximum and in LDS.
+  auto prep = [&](const StepData& nb, int kk) {
     if constexpr (PT) {
-      float x = fmax_swap32(h ? nb.sc : 0.f);  // every lane: v scale of token c32
+      const int t = t0 + kk * TT + 32 * w + c32;
+      const float vsc = (kk < te && t >= lo_u && t < hi_u) ? nb.sc : 0.f;
+      float x = fmax_swap32(h ? vsc : 0.f);  // every lane: v scale of token c32
       x = fmaxf(x, dpp_f<0xB1>(x));            // quad: lanes ^1
       x = fmaxf(x, dpp_f<0x4E>(x));            // quad: lanes ^2
       x = fmaxf(x, dpp_f<0x141>(x));           // half-row mirror
       x = fmaxf(x, dpp_f<0x140>(x));           // row mirror
       x = fmax_swap16(x);                      // both 16-lane rows: the step's 32 tokens
       const int e = min(max(__builtin_amdgcn_frexp_expf(x), VEXP_MIN), VEXP_MAX);
+      const float inv = __uint_as_float((uint32_t)(127 - e) << 23);
       vconv = __uint_as_float((uint32_t)(127 + e) << 23);
-      ssl[lane] = h ? nb.sc * __uint_as_float((uint32_t)(127 - e) << 23) : nb.sc;
+      vsmax = x * inv;
+      ssl[lane] = h ? vsc * inv : nb.sc * lmul;
     }
   };
 
@@ -380,10 +391,10 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t d0 = (uint32_t)cur.k[j >> 2][2 * (j & 3)], d1 = (uint32_t)cur.k[j >> 2][2 * (j & 3) + 1];
-      const h2 x0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, kmul, false);
-      const h2 x1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, kmul, true);
-      const h2 x2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, kmul, false);
-      const h2 x3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, kmul, true);
+      const h2 x0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false);
+      const h2 x1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true);
+      const h2 x2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
+      const h2 x3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
       kf[j] = half8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
     }
     load_k(cur, kn, nid);  // this step's K is converted, its scales are in LDS
@@ -454,7 +465,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       float y[16];
       if constexpr (gen) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) y[i] = PT ? sa[i] * ks16[i] : sa[i];
+        for (int i = 0; i < 16; ++i) y[i] = sa[i] * (PT ? ks16[i] : lmul);
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -474,7 +485,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if constexpr (gen) y[i] = y[i] + nm;
-        else y[i] = PT ? __builtin_fmaf(sa[i], ks16[i], nm) : sa[i] + nm;
+        else y[i] = __builtin_fmaf(sa[i], PT ? ks16[i] : lmul, nm);
         y[i] = __builtin_amdgcn_exp2f(y[i]);  // exp2(-inf) = 0
       }
       float t8[8];
@@ -482,11 +493,13 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       for (int i = 0; i < 8; ++i) t8[i] = y[2 * i] + y[2 * i + 1];
       const float ls = ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
       l_acc[rb] += ls;
-      // a probability above 2^TAU_S shows in the lane's sum; the bound
-      // m_ref + log2(sum) is at least the step's maximum
-      const bool big = ls > 0x1p15f;
+      // a PV operand p * (normalised V scale) of 2^15 or more shows in the
+      // lane's sum times the largest normalised V scale; a reference raised
+      // by log2 of that product brings every operand to at most 1
+      const float bnd = ls * vsmax;
+      const bool big = bnd > 0x1p15f;
       ovf |= big;
-      m_hi[rb] = big ? fmaxf(m_hi[rb], m_ref[rb] + __builtin_amdgcn_logf(ls)) : m_hi[rb];
+      m_hi[rb] = big ? fmaxf(m_hi[rb], m_ref[rb] + __builtin_amdgcn_logf(bnd)) : m_hi[rb];
       if constexpr (PT) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) y[i] *= vs16[i];
@@ -540,7 +553,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
     pv(1, p1);
-    prep(nxt);
+    prep(nxt, k + 1);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);  // MFMA
@@ -572,7 +585,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       load_k(bb, k1, p1);
       load_v(bb, k1, p1);
     }
-    prep(ba);
+    prep(ba, tb);
     // Pairs of steps: boundary pairs (masks, reference updates) until the
     // interior tiles are reached with every row's reference set, interior
     // pairs, then boundary pairs again.  Each loop is entered with nothing
@@ -598,8 +611,11 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     for (; k < te && go;) pair(std::true_type{});
     return go;
   };
-  for (;;) {
-    if (attempt()) break;
+  // A restart raises every reference to at least the maxima seen, so a second
+  // attempt normally completes; the bound only guards against inputs (NaN,
+  // infinities) for which no reference helps.
+  for (int tries = 1;; ++tries) {
+    if (attempt() || tries == 8) break;
     wait_vmcnt<0>();  // loads issued past the stop
     // restart this wave's share with references at least the maxima seen
 #pragma unroll

@@ -181,3 +181,25 @@ def test_uniform_attention_census():
     got, _ = run(inp, cu_count=16, partition_tokens=128)
     counts = np.bincount(np.arange(L) % 128, minlength=128)
     np.testing.assert_allclose(got[0] * L, np.broadcast_to(counts, (8, 128)), rtol=0.004, atol=0.0)
+
+
+@pytest.mark.parametrize("page", [64, 128])
+def test_wide_scales_64_rows(page):
+    """64-row FP8 items: queries of magnitude 2^24 with per-token k scales
+    2^24 smaller (the whole-item power-of-two rescaling of the query, folded
+    back into the logits), and V scales 2^30 larger (the clamped V exponent
+    and its overflow restart), against the oracle.  The output is linear in
+    the V scales, so the second case is compared after dividing both sides
+    by 2^30: the absolute part of the tolerance keeps its meaning."""
+    for name, qmul, kmul, vmul in [("q x 2^24, k scales x 2^-24", 2.0**24, 2.0**-24, 1.0),
+                                   ("v scales x 2^30", 1.0, 1.0, 2.0**30)]:
+        inp = W.make_dense_case(48 + page, LENS, query_len=4, num_q_heads=16, num_kv_heads=1, head_dim=128,
+                                page_size=page, scale_mode="token")
+        inp.q.mul_(qmul)
+        real = inp.k_scale < 1e29  # poisoned slots keep their poison
+        inp.k_scale[real] *= kmul
+        real = inp.v_scale < 1e29
+        inp.v_scale[real] *= vmul
+        announce(f"wide scales page={page}: {name}")
+        got, _ = run(inp, cu_count=64)
+        compare(got / vmul, O.attend(inp) / vmul, name)
