@@ -145,103 +145,31 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     lo_max = a.window > 0 ? max(0, pos_last - a.window + 1) : 0;
   }
 
-  // ---- page ids of the item into LDS ----
+  // ---- the item's page-id range ----
   const int ppt = TT >> ps_log2;  // pages per tile
   const long id0 = ((long)t0 >> ps_log2) + (long)tb * ppt;
   const long id_end = ((long)hi_u + ps - 1) >> ps_log2;  // one past the last page with visible tokens
   const int nstaged = (int)max(0L, min((long)a.stage_limit, min((long)(te - tb) * ppt, id_end - id0)));
   const int32_t* bt_row = a.block_tables + (long)s * a.table_stride;
-  for (int k = tid; k < nstaged; k += 256) ids[k] = bt_row[id0 + k];
 
-  // ---- query operand: FP16 ----
-  // Rows are scaled by c = softmax_scale*log2(e) (* k_scale for per-tensor
-  // scales) and, should the item's largest |c q| reach 2^14, by 2^-e for the
-  // whole item, so that FP16 never overflows; the logits get the 2^e back
-  // (folded into the per-token k scales, or the multiplier of the FMA that
-  // subtracts the reference maximum).  The workgroup converts the rows once into LDS (thread = row
-  // tid/4, dims 32*(tid%4) ..+31), laid out as the reading lanes want them:
-  // MFMA k-step j takes, in lane half h, the 8 dims 64(j/4) + 32h + 8(j%4)
-  // ..+7, the same dims as the lane's K operand; every wave then keeps all of
-  // the item's fragments in accumulator registers.
-  uint8_t* qlds = smem;  // [RB][8 k-steps][64 lanes][16 B]; the merge buffers reuse it after the loop
-  float lmul;            // 2^e: logit multiplier
+  // ---- the query rows' raw bits (issued first: their wait does not cover the K/V loads) ----
+  const int q_r = tid >> 2, q_qq = tid & 3;  // 64 rows x 4 quarters
+  const bool q_valid = q_r < nrows && q_r < StreamSmem<RB>::ROWS;
+  u32x4 qraw[4];
   {
-    const float cbase = a.scale_log2 * (PT ? 1.0f : a.k_scale[0]);
-    const int r = tid >> 2, qq = tid & 3;  // 64 rows x 4 quarters
-    const bool rvalid = r < nrows && r < S::ROWS;
-    const int gr = row0 + (rvalid ? r : 0);
+    const int gr = row0 + (q_valid ? q_r : 0);
     const int i = gr / a.G, hl = gr % a.G;
-    const long qoff = (((long)s * a.QL + i) * a.Hq + (long)kvh * a.G + hl) * D + 32 * qq;
+    const long qoff = (((long)s * a.QL + i) * a.Hq + (long)kvh * a.G + hl) * D + 32 * q_qq;
     const uint16_t* qrow = (const uint16_t*)a.q + qoff;
-    float qv[32];
 #pragma unroll
-    for (int part = 0; part < 4; ++part) {
-      const u32x4 raw = rvalid ? *(const u32x4*)(qrow + 8 * part) : u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const uint16_t bits = (uint16_t)(raw[p >> 1] >> (16 * (p & 1)));
-        qv[8 * part + p] =
-            a.q_fp16 ? (float)__builtin_bit_cast(_Float16, bits) : __uint_as_float((uint32_t)bits << 16);
-      }
-    }
-    float amax = 0.f;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(qv[j]));
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    if (lane == 0) stats[w] = amax;
-    __syncthreads();
-    const float cq = fmaxf(fmaxf(stats[0], stats[1]), fmaxf(stats[2], stats[3])) * cbase;
-    int e = 0;
-    if (cq >= 0x1p14f && cq < INFINITY) {
-      int ex;
-      (void)frexpf(cq * 0x1p-14f, &ex);  // cq * 2^-14 < 2^ex
-      e = min(ex, 100);
-    }
-    const float mul = ldexpf(cbase, -e);
-    lmul = ldexpf(1.0f, e);
-    if (r < S::ROWS) {
-      const int rb = r >> 5;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        half8 hv;
-#pragma unroll
-        for (int p = 0; p < 8; ++p) hv[p] = (_Float16)(qv[8 * x + p] * mul);
-        const int j = 4 * (qq >> 1) + x;
-        *(half8*)(qlds + ((size_t)((rb * 8 + j) * 64 + 32 * (qq & 1) + (r & 31))) * 16) = hv;
-      }
-    }
+    for (int part = 0; part < 4; ++part) qraw[part] = *(const u32x4*)(qrow + 8 * part);  // padding rows read row 0
   }
-  __syncthreads();
-  half8 qf[RB][8];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      qf[rb][j] = *(const half8*)(qlds + ((size_t)((rb * 8 + j) * 64 + lane)) * 16);
-      asm volatile("" : "+a"(qf[rb][j]));  // kept in accumulator registers for the whole loop
-    }
 
-  // ---- softmax state ----
-  // Rows that are padding start with a finite reference so that no path has
-  // to special-case them; they are never written out.  O holds
-  // sum_t p_t * v_scale(t) * v_t for per-token scales and sum_t p_t v_t for a
-  // per-tensor scale (applied at the end).
-  float m_ref[RB], m_hi[RB], l_acc[RB];
-  f32x16 o[RB][4];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_ref[rb] = valid[rb] ? -INFINITY : 0.f;
-    m_hi[rb] = -INFINITY;
-  }
-  const float vs_out = PT ? 1.0f : a.v_scale[0];
-
+  // ---- the first three steps' loads ----
+  // Issued before the query is prepared, with page ids read straight from
+  // the block table, so that their latency overlaps the query work.
   const uint8_t* kbase = a.k_cache + (long long)kvh * a.head_stride;
   const uint8_t* vbase = a.v_cache + (long long)kvh * a.head_stride;
-  float* ssl = sbuf + w * 64;  // this wave's scale slot
-
-  __syncthreads();  // staged ids visible
-
   // ---- loads of one step ----
   // QK A-operand row c32 is token kt of the step: MFMA output register i of
   // lane half h is then token 16h + i, and lane (c32, h) loads V of dim
@@ -253,9 +181,9 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   };
   // id of page j: staged in LDS, past the staged bound from the block table;
   // pages without visible tokens read page 0 of the head (masked later)
-  auto page_id = [&](long j) -> long {
+  auto page_id = [&](long j, auto DIRECT) -> long {
     if (!page_ok(j)) return 0;
-    if (j < nstaged) return (long)ids[j];
+    if (!decltype(DIRECT)::value && j < nstaged) return (long)ids[j];
     return (long)__builtin_nontemporal_load(bt_row + id0 + j);
   };
   // Lane-constant parts of the addresses (page >= 32: a step lies in one page)
@@ -272,6 +200,182 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   const uint32_t soff = (uint32_t)((kvh * ps + ((32 * w + c32) & (ps - 1))) * 4);
   const float* sbase = h ? a.v_scale : a.k_scale;
 
+  auto load_k = [&](StepData& d, int k, long id, auto DIRECT) {
+    const int ts_rel = (k - tb) * TT + 32 * w;  // step start relative to the item's first tile
+    if constexpr (BIG) {
+      const uint8_t* kp = kbase + id * a.page_stride;
+      d.k[0] = load32(kp + koff, kp + koff + kcs);
+      d.k[1] = load32(kp + koff + 4 * kcs, kp + koff + 5 * kcs);
+      if constexpr (PT) d.sc = *(const float*)((const uint8_t*)(sbase + id * a.Hkv * ps) + soff);
+    } else {
+      // page 16: the step spans two pages; addresses per lane
+      const int tk = ts_rel + kt;
+      const long idk = page_id(tk >> ps_log2, DIRECT);
+      const uint8_t* src = kbase + idk * a.page_stride + (long)(tk & (ps - 1)) * 16;
+      d.k[0] = load32(src + (2 * h) * kcs, src + (2 * h + 1) * kcs);
+      d.k[1] = load32(src + (2 * h + 4) * kcs, src + (2 * h + 5) * kcs);
+      if constexpr (PT) {
+        const int tsc = ts_rel + c32;
+        const long ids_ = page_id(tsc >> ps_log2, DIRECT);
+        d.sc = sbase[(ids_ * a.Hkv + kvh) * ps + (tsc & (ps - 1))];
+      }
+    }
+    if constexpr (!PT) d.sc = 0.f;
+  };
+  auto load_v = [&](StepData& d, int k, long id, auto DIRECT) {
+    const int ts_rel = (k - tb) * TT + 32 * w;
+    if constexpr (BIG) {
+      const uint8_t* vp = vbase + id * a.page_stride;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) d.v[db] = *(const u32x4*)(vp + voff[db]);
+    } else {
+      const long idv = page_id((ts_rel + 16 * h) >> ps_log2, DIRECT);  // the lane's 16 tokens: one page
+      const uint8_t* pg = vbase + idv * a.page_stride;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint8_t* src = pg + (long)(32 * db + c32) * 16;  // page 16: both V layouts put a dim's 16 bytes here
+        d.v[db] = *(const u32x4*)src;
+      }
+    }
+  };
+
+  const __attribute__((address_space(4))) int32_t* btc =
+      (const __attribute__((address_space(4))) int32_t*)bt_row;
+  auto step_page_direct = [&](int k) -> long {  // page id of step k from the block table (page >= 32)
+    const long j = (long)((k - tb) * TT + 32 * wu) >> ps_log2;
+    if (!page_ok(j)) return 0;
+    return btc[id0 + j];
+  };
+  // Unconditional, so that the compiler's wait counts stay exact: an empty
+  // item (tb >= te) reads page 0 of its head, which exists (the host routes
+  // caches without pages elsewhere), and never uses the data.
+  StepData ba, bb, bc;
+  {
+    const int k1 = min(tb + 1, te - 1), k2 = min(tb + 2, te - 1);
+    const long p0 = BIG ? step_page_direct(tb) : 0;
+    const long p1 = BIG ? step_page_direct(k1) : 0;
+    const long p2 = BIG ? step_page_direct(k2) : 0;
+    load_k(ba, tb, p0, std::true_type{});
+    load_v(ba, tb, p0, std::true_type{});
+    load_k(bb, k1, p1, std::true_type{});
+    load_v(bb, k1, p1, std::true_type{});
+    load_k(bc, k2, p2, std::true_type{});
+    load_v(bc, k2, p2, std::true_type{});
+  }
+
+  // ---- query operand: two FP8 terms per row with a power-of-two scale ----
+  // Row r is scaled by c = softmax_scale*log2(e) (* k_scale for per-tensor
+  // scales) and by 2^-e, e chosen so that |c q / 2^e| <= 448; the terms
+  // hi = fp8(c q / 2^e) and lo = fp8(16 (c q / 2^e - hi)) carry the row to
+  // within 2^-8 of each element (RNE: half an FP8 ulp of the residual) and
+  // enter the MFMA with the E8M0 block scales 2^e and 2^(e-4), so the
+  // accumulator holds base-2 logits in FP32 with K taken exactly as stored.
+  // The workgroup splits the rows once into LDS (thread = row tid/4, dims
+  // 32*(tid%4) ..+31), laid out as the reading lanes want them: lane half h
+  // of k-step ks holds dims 64ks + 32h .. +31, the same dims as its K
+  // operand; every wave then keeps all of the item's fragments in
+  // accumulator registers.
+  uint8_t* qlds = smem;  // [RB][2 ks][2 terms][64 lanes][32 B]; the merge buffers reuse it after the loop
+  int* qexp = (int*)(smem + RB * 2 * 2 * 64 * 32);  // [ROWS] E8M0 of the hi term
+  {
+    const float cbase = a.scale_log2 * (PT ? 1.0f : a.k_scale[0]);
+    const int r = q_r, qq = q_qq;
+    float qv[32];
+#pragma unroll
+    for (int part = 0; part < 4; ++part) {
+      const u32x4 raw = q_valid ? qraw[part] : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const uint16_t bits = (uint16_t)(raw[p >> 1] >> (16 * (p & 1)));
+        qv[8 * part + p] =
+            a.q_fp16 ? (float)__builtin_bit_cast(_Float16, bits) : __uint_as_float((uint32_t)bits << 16);
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(qv[j]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));  // the row's four quarters are adjacent lanes
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    const float cq = amax * cbase;
+    int e = 0;
+    float mul = 0.f;
+    if (cq > 0.f && cq < INFINITY) {
+      int ex;
+      (void)frexpf(cq * (1.0f / FP8_MAX), &ex);  // cq/448 < 2^ex
+      e = min(max(ex, -119), 127);
+      mul = ldexpf(cbase, -e);
+    }
+    if (qq == 0 && r < S::ROWS) qexp[r] = 127 + e;
+    const int rb = r >> 5, ks = qq >> 1, hh = qq & 1;
+    uint8_t* dst = qlds + ((size_t)((rb * 2 + ks) * 2) * 64 + 32 * hh + (r & 31)) * 32;
+    if (r < S::ROWS) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 t0v, t1v;
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          int w0 = 0, w1 = 0;
+          float r1[4], r2[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            r1[x] = fminf(fmaxf(qv[16 * half + 4 * j4 + x] * mul, -FP8_MAX), FP8_MAX);
+          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(r1[0], r1[1], w0, false);
+          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(r1[2], r1[3], w0, true);
+          {
+            const float hv[4] = {__builtin_amdgcn_cvt_f32_fp8(w0, 0), __builtin_amdgcn_cvt_f32_fp8(w0, 1),
+                                 __builtin_amdgcn_cvt_f32_fp8(w0, 2), __builtin_amdgcn_cvt_f32_fp8(w0, 3)};
+#pragma unroll
+            for (int x = 0; x < 4; ++x) r2[x] = (r1[x] - hv[x]) * 16.0f;
+          }
+          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(r2[0], r2[1], w1, false);
+          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(r2[2], r2[3], w1, true);
+          t0v[j4] = (uint32_t)w0;
+          t1v[j4] = (uint32_t)w1;
+        }
+        *(u32x4*)(dst + 16 * half) = t0v;
+        *(u32x4*)(dst + 64 * 32 + 16 * half) = t1v;
+      }
+    }
+  }
+  __syncthreads();
+  int qsc[RB];
+  i32x8 qf[RB][2][2];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    qsc[rb] = qexp[32 * rb + c32];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint8_t* src = qlds + ((size_t)((rb * 2 + ks) * 2 + t) * 64 + lane) * 32;
+        const u32x4 lo = *(const u32x4*)src, hi = *(const u32x4*)(src + 16);
+        qf[rb][ks][t] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        asm volatile("" : "+a"(qf[rb][ks][t]));  // kept in accumulator registers for the whole loop
+      }
+  }
+
+  // ---- page ids of the item into LDS (read after the first K/V loads: the
+  // loop needs them from its fourth step on) ----
+  for (int k = tid; k < nstaged; k += 256) ids[k] = bt_row[id0 + k];
+
+  // ---- softmax state ----
+  // Rows that are padding start with a finite reference so that no path has
+  // to special-case them; they are never written out.  O holds
+  // sum_t p_t * v_scale(t) * v_t for per-token scales and sum_t p_t v_t for a
+  // per-tensor scale (applied at the end).
+  float m_ref[RB], m_hi[RB], l_acc[RB];
+  f32x16 o[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_ref[rb] = valid[rb] ? -INFINITY : 0.f;
+    m_hi[rb] = -INFINITY;
+  }
+  const float vs_out = PT ? 1.0f : a.v_scale[0];
+
+  float* ssl = sbuf + w * 64;  // this wave's scale slot
+
+  __syncthreads();  // staged ids visible
+
   // The loads of step k are issued in two parts: K and the scales once the
   // QK MFMAs of the step before have consumed its K registers, V once its PV
   // MFMAs have consumed its V registers; each part then has a whole step to
@@ -286,47 +390,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     if (j < nstaged) return __builtin_amdgcn_readfirstlane(ids[j]);
     // past the staged bound: a scalar read of the block table (the table is
     // constant for the kernel's lifetime), counted apart from the K/V loads
-    const __attribute__((address_space(4))) int32_t* btc =
-        (const __attribute__((address_space(4))) int32_t*)bt_row;
     return btc[id0 + j];
-  };
-  auto load_k = [&](StepData& d, int k, long id) {
-    const int ts_rel = (k - tb) * TT + 32 * w;  // step start relative to the item's first tile
-    if constexpr (BIG) {
-      const uint8_t* kp = kbase + id * a.page_stride;
-      d.k[0] = load32(kp + koff, kp + koff + kcs);
-      d.k[1] = load32(kp + koff + 4 * kcs, kp + koff + 5 * kcs);
-      if constexpr (PT) d.sc = *(const float*)((const uint8_t*)(sbase + id * a.Hkv * ps) + soff);
-    } else {
-      // page 16: the step spans two pages; addresses per lane
-      const int tk = ts_rel + kt;
-      const long idk = page_id(tk >> ps_log2);
-      const uint8_t* src = kbase + idk * a.page_stride + (long)(tk & (ps - 1)) * 16;
-      d.k[0] = load32(src + (2 * h) * kcs, src + (2 * h + 1) * kcs);
-      d.k[1] = load32(src + (2 * h + 4) * kcs, src + (2 * h + 5) * kcs);
-      if constexpr (PT) {
-        const int tsc = ts_rel + c32;
-        const long ids_ = page_id(tsc >> ps_log2);
-        d.sc = sbase[(ids_ * a.Hkv + kvh) * ps + (tsc & (ps - 1))];
-      }
-    }
-    if constexpr (!PT) d.sc = 0.f;
-  };
-  auto load_v = [&](StepData& d, int k, long id) {
-    const int ts_rel = (k - tb) * TT + 32 * w;
-    if constexpr (BIG) {
-      const uint8_t* vp = vbase + id * a.page_stride;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) d.v[db] = *(const u32x4*)(vp + voff[db]);
-    } else {
-      const long idv = page_id((ts_rel + 16 * h) >> ps_log2);  // the lane's 16 tokens: one page
-      const uint8_t* pg = vbase + idv * a.page_stride;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint8_t* src = pg + (long)(32 * db + c32) * 16;  // page 16: both V layouts put a dim's 16 bytes here
-        d.v[db] = *(const u32x4*)src;
-      }
-    }
   };
 
   // Tiles [ti0, ti1) are visible to every row; their steps skip the masks
@@ -372,32 +436,18 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       const float inv = __uint_as_float((uint32_t)(127 - e) << 23);
       vconv = __uint_as_float((uint32_t)(127 + e) << 23);
       vsmax = x * inv;
-      ssl[lane] = h ? vsc * inv : nb.sc * lmul;
+      ssl[lane] = h ? vsc * inv : nb.sc;
     }
   };
 
   auto step = [&](auto GENc, StepData& cur, const StepData& nxt, int k) -> bool {
     constexpr bool gen = decltype(GENc)::value;
+    if (k >= te) return true;  // padding of the last group of three: nothing to do
     const int tsa = t0 + k * TT + 32 * w;  // first token of the step
     const int tl = tsa + 16 * h;           // first of the lane's 16 tokens
-    const bool live = k < te;  // the empty step that pads an odd count masks everything
-    const int span_lo = live ? lo_u : 0, span_hi = live ? hi_u : 0;  // tokens whose V may be used
-    const int kn = min(k + 2, te - 1);
+    const int span_lo = lo_u, span_hi = hi_u;  // tokens whose V may be used
+    const int kn = min(k + 3, te - 1);
     const long nid = BIG ? step_page(kn) : 0;
-
-    // K of the step in FP16 (k-step j = bytes 8j..8j+7 of the lane's 64),
-    // times the query's 2^e (exact); per-token k scales multiply the logits
-    half8 kf[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t d0 = (uint32_t)cur.k[j >> 2][2 * (j & 3)], d1 = (uint32_t)cur.k[j >> 2][2 * (j & 3) + 1];
-      const h2 x0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false);
-      const h2 x1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true);
-      const h2 x2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
-      const h2 x3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
-      kf[j] = half8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
-    }
-    load_k(cur, kn, nid);  // this step's K is converted, its scales are in LDS
 
     // V of the step; tokens outside the visible span get zero V (their bytes
     // may be anything, and 0 * NaN would reach O)
@@ -419,11 +469,16 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       }
     }
 
-    // S^T = K Q^T for one 32-row block
+    // S^T = K Q^T for one 32-row block: K as stored against the two query
+    // terms, each k-step with its own E8M0 scale
     auto qk = [&](int rb) {
       f32x16 acc = {};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[j], qf[rb][j], acc, 0, 0, 0);
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.k[ks], qf[rb][ks][t], acc, 0, 0, 0, 127, 0,
+                                                                qsc[rb] - 4 * t);
       return acc;
     };
     // V in FP16 (times 2^E): k-block kb of dim 32db + c32 = tokens 16h + 8kb .. +7
@@ -465,12 +520,12 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       float y[16];
       if constexpr (gen) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) y[i] = sa[i] * (PT ? ks16[i] : lmul);
+        for (int i = 0; i < 16; ++i) y[i] = PT ? sa[i] * ks16[i] : sa[i];
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int t = tl + i;
-          y[i] = (live && t >= lo_r[rb] && t <= hi_r[rb]) ? y[i] : -INFINITY;
+          y[i] = (t >= lo_r[rb] && t <= hi_r[rb]) ? y[i] : -INFINITY;
           mx = fmaxf(mx, y[i]);
         }
         mx = fmax_swap32(mx);  // the partner lane holds the row's other 16 tokens
@@ -485,7 +540,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if constexpr (gen) y[i] = y[i] + nm;
-        else y[i] = __builtin_fmaf(sa[i], PT ? ks16[i] : lmul, nm);
+        else y[i] = PT ? __builtin_fmaf(sa[i], ks16[i], nm) : sa[i] + nm;
         y[i] = __builtin_amdgcn_exp2f(y[i]);  // exp2(-inf) = 0
       }
       float t8[8];
@@ -521,29 +576,32 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     };
 
     // Schedule (one wave per SIMD, so the overlap has to come from within
-    // the wave): QK of row block 0 with the K and V conversions; QK of row
-    // block 1 with the probabilities of block 0; PV of block 0 with the
+    // the wave): QK of row block 0 with the V conversion; QK of row block 1
+    // with the probabilities of block 0; PV of block 0 with the
     // probabilities of block 1; PV of block 1 with the next step's scales.
+    // V is reloaded (three steps ahead) once converted, K once both row
+    // blocks' QK MFMAs have read it.
     static_assert(RB == 2, "the schedule below is written for two row blocks");
     half8 p0[2], p1[2];
     const f32x16 s0 = qk(0);
     vcvt();
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA (FP8, 16 passes)
+      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // VALU
     }
     __builtin_amdgcn_sched_barrier(0);
-    load_v(cur, kn, nid);  // this step's V is converted
+    load_v(cur, kn, nid, std::false_type{});  // this step's V is converted
     const f32x16 s1 = qk(1);
     scales();
     probs(0, s0, p0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 1);  // VALU
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // MFMA (FP8, 16 passes)
+      __builtin_amdgcn_sched_group_barrier(0x002, 16, 1);  // VALU
     }
     __builtin_amdgcn_sched_barrier(0);
+    load_k(cur, kn, nid, std::false_type{});  // both row blocks' QK have read this step's K
     pv(0, p0);
     probs(1, s1, p1);
 #pragma unroll
@@ -563,11 +621,12 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     return !__builtin_amdgcn_ballot_w64(ovf);
   };
 
-  // One pass of this wave over the item, two steps per iteration with one
-  // load buffer each (an odd count ends with an empty step).  An overflow
-  // stops it at the top of the next pair (a single latch keeps each O
-  // accumulator in place across iterations).
-  auto attempt = [&]() -> bool {
+  // One pass of this wave over the item, three steps per iteration with one
+  // load buffer each (a count that is not a multiple of three ends with one
+  // or two steps that return at once).  An overflow stops it at the top of
+  // the next group (a single latch keeps each O accumulator in place across
+  // iterations).
+  auto attempt = [&](bool first) -> bool {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       l_acc[rb] = 0.f;
@@ -575,47 +634,52 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       for (int db = 0; db < 4; ++db) o[rb][db] = f32x16{};
     }
     if (tb >= te) return true;
-    StepData ba, bb;
-    {
+    if (!first) {  // a restart: the first three steps' loads again
       const long p0 = BIG ? step_page(tb) : 0;
-      load_k(ba, tb, p0);
-      load_v(ba, tb, p0);
+      load_k(ba, tb, p0, std::false_type{});
+      load_v(ba, tb, p0, std::false_type{});
       const int k1 = min(tb + 1, te - 1);
       const long p1 = BIG ? step_page(k1) : 0;
-      load_k(bb, k1, p1);
-      load_v(bb, k1, p1);
+      load_k(bb, k1, p1, std::false_type{});
+      load_v(bb, k1, p1, std::false_type{});
+      const int k2 = min(tb + 2, te - 1);
+      const long p2 = BIG ? step_page(k2) : 0;
+      load_k(bc, k2, p2, std::false_type{});
+      load_v(bc, k2, p2, std::false_type{});
     }
     prep(ba, tb);
-    // Pairs of steps: boundary pairs (masks, reference updates) until the
-    // interior tiles are reached with every row's reference set, interior
-    // pairs, then boundary pairs again.  Each loop is entered with nothing
-    // in flight beyond its two buffers' loads, which keeps the compiler's
-    // wait counts exact inside it.
+    // Groups of three steps: boundary groups (masks, reference updates)
+    // until the interior tiles are reached with every row's reference set,
+    // interior groups, then boundary groups again.  Each loop is entered with
+    // nothing in flight beyond its three buffers' loads, which keeps the
+    // compiler's wait counts exact inside it.
     bool go = true;  // wave-uniform
     int k = tb;
-    auto pair = [&](auto GENc) {
+    auto triple = [&](auto GENc) {
       go = step(GENc, ba, bb, k);
-      __builtin_amdgcn_sched_barrier(0);  // the two steps do not interleave (registers)
-      go = step(GENc, bb, ba, k + 1) && go;
+      __builtin_amdgcn_sched_barrier(0);  // the steps do not interleave (registers)
+      go = step(GENc, bb, bc, k + 1) && go;
       __builtin_amdgcn_sched_barrier(0);
-      k += 2;
+      go = step(GENc, bc, ba, k + 2) && go;
+      __builtin_amdgcn_sched_barrier(0);
+      k += 3;
     };
     for (; k < te && go;) {
       bool need_ref = false;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) need_ref |= m_ref[rb] == -INFINITY;
-      if (k >= ti0 && k + 1 < ti1 && !__builtin_amdgcn_ballot_w64(need_ref)) break;
-      pair(std::true_type{});
+      if (k >= ti0 && k + 2 < ti1 && !__builtin_amdgcn_ballot_w64(need_ref)) break;
+      triple(std::true_type{});
     }
-    for (; k + 1 < ti1 && go;) pair(std::false_type{});
-    for (; k < te && go;) pair(std::true_type{});
+    for (; k + 2 < ti1 && go;) triple(std::false_type{});
+    for (; k < te && go;) triple(std::true_type{});
     return go;
   };
   // A restart raises every reference to at least the maxima seen, so a second
   // attempt normally completes; the bound only guards against inputs (NaN,
   // infinities) for which no reference helps.
   for (int tries = 1;; ++tries) {
-    if (attempt() || tries == 8) break;
+    if (attempt(tries == 1) || tries == 8) break;
     wait_vmcnt<0>();  // loads issued past the stop
     // restart this wave's share with references at least the maxima seen
 #pragma unroll
@@ -752,7 +816,8 @@ static pa_status launch_stream_t(const KernelArgs& args, int nblocks, hipStream_
 
 bool stream_kernel_applies(const Plan& P) {
   const pa_problem& p = P.prob;
-  return p.kv_dtype == PA_FP8_E4M3FN && p.head_dim == 128 && !p.token_table && P.rows_per_group > 32;
+  return p.kv_dtype == PA_FP8_E4M3FN && p.head_dim == 128 && !p.token_table && P.rows_per_group > 32 &&
+         p.num_pages > 0;
 }
 
 pa_status launch_stream(const Plan& P, const KernelArgs& args, int nblocks, hipStream_t stream) {
