@@ -203,3 +203,19 @@ def test_wide_scales_64_rows(page):
         announce(f"wide scales page={page}: {name}")
         got, _ = run(inp, cu_count=64)
         compare(got / vmul, O.attend(inp) / vmul, name)
+
+
+@pytest.mark.parametrize("page", [64, 128])
+def test_stream_kernel_run_to_run_bit_exact(page):
+    """64-row FP8 items (the streaming kernel, several partitions per
+    sequence, merged in partition order): against the oracle, and two calls
+    with one plan give identical bytes."""
+    inp = W.make_dense_case(60 + page, [5000, 3, 0, 1, 2600, 700], query_len=4, num_q_heads=16, num_kv_heads=1,
+                            head_dim=128, page_size=page, scale_mode="token", sliding_window=0, has_sinks=True)
+    dev = to_device(inp)
+    announce(f"stream kernel twice page={page}")
+    a, plan = run(inp, dev=dev, cu_count=64)
+    assert plan.info().num_reduce > 0
+    compare(a, O.attend(inp), "stream kernel")
+    b, _ = run(inp, dev=dev, plan=plan)
+    assert np.array_equal(a, b)
