@@ -44,11 +44,13 @@ namespace pa {
 
 constexpr int TT = kTileTokens;  // 128 tokens per tile
 // Waves per workgroup: 16-row items use 4 waves (and two workgroups share a
-// CU); 32- and 64-row items use 8 waves so that each SIMD runs two waves of
-// one workgroup.  Every wave owns one 16-row tile of the item.
-template <int NRT>
+// CU); 32- and 64-row items of head dim 128 use 8 waves so that each SIMD
+// runs two waves of one workgroup.  Head dim 256 keeps 4 waves (one per
+// SIMD, up to 512 registers each: two waves of 256 registers spill there).
+// Every wave owns one 16-row tile of the item.
+template <int NRT, int D>
 struct Waves {
-  static constexpr int NW = NRT >= 2 ? 8 : 4;
+  static constexpr int NW = (NRT >= 2 && D <= 128) ? 8 : 4;
   static constexpr int NT = 64 * NW;
 };
 template <int D, bool FP8, int NT>
@@ -73,7 +75,7 @@ struct Tile {
 // tiles per wave, D 256 one.
 template <int D, int NRT>
 struct Roles {
-  static constexpr int NW = Waves<NRT>::NW;
+  static constexpr int NW = Waves<NRT, D>::NW;
   static constexpr int NRW = 1;         // row tiles per wave
   static constexpr int WR = NRT;        // row groups
   static constexpr int WT = NW / WR;    // token groups
@@ -85,7 +87,7 @@ template <int D, bool FP8, int NRT, bool SPARSE>
 struct Smem {
   using R = Roles<D, NRT>;
   static constexpr int STAGES = (!SPARSE && FP8 && D == 128 && NRT >= 2) ? 4 : 2;
-  static constexpr int STAGE = Tile<D, FP8, Waves<NRT>::NT>::STAGE;
+  static constexpr int STAGE = Tile<D, FP8, Waves<NRT, D>::NT>::STAGE;
   static constexpr int MERGE = NRT * 16 * (D + 4) * 4;  // one O buffer with padded rows
   static constexpr int MAIN = (STAGES * STAGE > MERGE) ? STAGES * STAGE : MERGE;
   static constexpr int IDS = kStageCap * 4;
@@ -102,9 +104,9 @@ struct Staged {
 };
 
 template <int D, bool FP8, int NRT, bool SPARSE>
-__global__ __launch_bounds__(Waves<NRT>::NT) void pa_decode_kernel(KernelArgs a) {
-  constexpr int NTHREADS = Waves<NRT>::NT;
-  constexpr int NWAVES = Waves<NRT>::NW;
+__global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelArgs a) {
+  constexpr int NTHREADS = Waves<NRT, D>::NT;
+  constexpr int NWAVES = Waves<NRT, D>::NW;
   using T = Tile<D, FP8, NTHREADS>;
   using S = Smem<D, FP8, NRT, SPARSE>;
   using R = Roles<D, NRT>;
@@ -1016,7 +1018,7 @@ static pa_status launch_one(const KernelArgs& args, int nblocks, hipStream_t str
     }
     configured = true;
   }
-  hipLaunchKernelGGL((pa_decode_kernel<D, FP8, NRT, SPARSE>), dim3(nblocks), dim3(Waves<NRT>::NT), bytes, stream,
+  hipLaunchKernelGGL((pa_decode_kernel<D, FP8, NRT, SPARSE>), dim3(nblocks), dim3((Waves<NRT, D>::NT)), bytes, stream,
                      args);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(PA_ERR_DEVICE, std::string("decode launch failed: ") + hipGetErrorString(err));

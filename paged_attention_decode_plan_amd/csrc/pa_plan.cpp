@@ -151,6 +151,11 @@ extern "C" pa_status pa_plan(const pa_problem* problem, const int32_t* context_l
     const double tile_bytes = kTileTokens * (2.0 * p.head_dim * elem + 8.0);
     const double partial_bytes = P.rows_per_group * (p.head_dim + 2.0) * 4.0;
     const double cost_per_item = 2.0 * partial_bytes / (tile_bytes * cu);  // in tile-times
+    // The reducer takes a unit's partitions eight at a time, one memory
+    // round trip (about one tile-time) each: an eighth of a tile-time per
+    // partition on the merge's critical path, which does not add up over the
+    // units it runs for in parallel.
+    const double reduce_per_part = 0.125;
     long items = nunits;
     using E = std::pair<long, int>;  // (current longest item tiles, seq)
     std::priority_queue<E> pq;
@@ -159,16 +164,21 @@ extern "C" pa_status pa_plan(const pa_problem* problem, const int32_t* context_l
     while (!pq.empty()) {
       auto [len, s] = pq.top();
       pq.pop();
-      int np = parts[s] + 1;
+      if (len <= 1) continue;
+      // the smallest partition count that shortens this sequence's longest
+      // item (one more partition may not, when the tiles do not divide)
+      const int np = (int)ceil_div(seq_tiles[s], len - 1);
       if (np > maxp || np > seq_tiles[s]) continue;
-      if (items + units_per_seq > slots_budget) break;
+      const long add = (long)(np - parts[s]) * units_per_seq;
+      if (items + add > slots_budget) break;
       long newlen = ceil_div(seq_tiles[s], np);
       // the first split of a sequence also creates its first partial slots
-      double added = cost_per_item * units_per_seq * (parts[s] == 1 ? 2 : 1);
+      double added = cost_per_item * units_per_seq * ((np - parts[s]) + (parts[s] == 1 ? 1 : 0)) +
+                     reduce_per_part * (np - parts[s]);
       if ((double)(len - newlen) < added) continue;
       parts[s] = np;
-      items += units_per_seq;
-      pq.push({ceil_div(seq_tiles[s], np), s});
+      items += add;
+      pq.push({newlen, s});
     }
   }
 
