@@ -165,6 +165,16 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     for (int part = 0; part < 4; ++part) qraw[part] = *(const u32x4*)(qrow + 8 * part);  // padding rows read row 0
   }
 
+  // ---- the item's page ids, read before the K/V loads (their wait does not
+  // cover those), staged in LDS once the query is prepared ----
+  static_assert(kStageCap == 4 * 256, "four ids per thread");
+  int32_t idr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const long k = min((long)(tid + 256 * j), (long)max(nstaged - 1, 0));
+    idr[j] = bt_row[min(max(id0 + k, 0L), (long)a.table_stride - 1)];  // in the row whatever the item
+  }
+
   // ---- the first three steps' loads ----
   // Issued before the query is prepared, with page ids read straight from
   // the block table, so that their latency overlaps the query work.
@@ -354,9 +364,11 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       }
   }
 
-  // ---- page ids of the item into LDS (read after the first K/V loads: the
-  // loop needs them from its fourth step on) ----
-  for (int k = tid; k < nstaged; k += 256) ids[k] = bt_row[id0 + k];
+  // ---- page ids of the item into LDS (the loop needs them from its fourth
+  // step on) ----
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (tid + 256 * j < nstaged) ids[tid + 256 * j] = idr[j];
 
   // ---- softmax state ----
   // Rows that are padding start with a finite reference so that no path has
@@ -440,7 +452,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     }
   };
 
-  auto step = [&](auto GENc, StepData& cur, const StepData& nxt, int k) -> bool {
+  auto step = [&](auto GENc, StepData& cur, const StepData& nxt, int k) __attribute__((always_inline)) -> bool {
     constexpr bool gen = decltype(GENc)::value;
     if (k >= te) return true;  // padding of the last group of three: nothing to do
     const int tsa = t0 + k * TT + 32 * w;  // first token of the step
@@ -626,7 +638,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   // or two steps that return at once).  An overflow stops it at the top of
   // the next group (a single latch keeps each O accumulator in place across
   // iterations).
-  auto attempt = [&](bool first) -> bool {
+  auto attempt = [&](bool first) __attribute__((always_inline)) -> bool {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       l_acc[rb] = 0.f;
@@ -655,7 +667,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     // compiler's wait counts exact inside it.
     bool go = true;  // wave-uniform
     int k = tb;
-    auto triple = [&](auto GENc) {
+    auto triple = [&](auto GENc) __attribute__((always_inline)) {
       go = step(GENc, ba, bb, k);
       __builtin_amdgcn_sched_barrier(0);  // the steps do not interleave (registers)
       go = step(GENc, bb, bc, k + 1) && go;
@@ -664,22 +676,26 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       k += 3;
     };
-    for (; k < te && go;) {
-      bool need_ref = false;
+    if (first) {
+      for (; k < te && go;) {
+        bool need_ref = false;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) need_ref |= m_ref[rb] == -INFINITY;
-      if (k >= ti0 && k + 2 < ti1 && !__builtin_amdgcn_ballot_w64(need_ref)) break;
-      triple(std::true_type{});
+        for (int rb = 0; rb < RB; ++rb) need_ref |= m_ref[rb] == -INFINITY;
+        if (k >= ti0 && k + 2 < ti1 && !__builtin_amdgcn_ballot_w64(need_ref)) break;
+        triple(std::true_type{});
+      }
+      for (; k + 2 < ti1 && go;) triple(std::false_type{});
     }
-    for (; k + 2 < ti1 && go;) triple(std::false_type{});
-    for (; k < te && go;) triple(std::true_type{});
+    for (; k < te && go;) triple(std::true_type{});  // a restart runs every step with the masks
     return go;
   };
   // A restart raises every reference to at least the maxima seen, so a second
   // attempt normally completes; the bound only guards against inputs (NaN,
   // infinities) for which no reference helps.
-  for (int tries = 1;; ++tries) {
-    if (attempt(tries == 1) || tries == 8) break;
+  // The first attempt is its own copy of the loop, entered straight from the
+  // early loads (no join with the restart path, whose different load history
+  // would make the compiler wait for all three steps before the first).
+  auto raise_refs = [&]() __attribute__((always_inline)) {
     wait_vmcnt<0>();  // loads issued past the stop
     // restart this wave's share with references at least the maxima seen
 #pragma unroll
@@ -689,6 +705,12 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       m_hi[rb] = -INFINITY;
     }
     ovf = false;
+  };
+  if (!attempt(true)) {
+    for (int tries = 2;; ++tries) {
+      raise_refs();
+      if (attempt(false) || tries == 8) break;
+    }
   }
 
   // ---- merge the four waves' states ----
