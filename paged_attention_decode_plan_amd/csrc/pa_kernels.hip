@@ -868,8 +868,9 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
 // ---------------------------------------------------------------------------
 // Partition reducer: out = sum_p w_p O_p / (sum_p w_p l_p + [sink]), with
 // w_p = 2^(m_p - M), M = max(m_p over parts with l_p > 0, sink), partitions
-// added in order (deterministic).  One workgroup per (entry, 8 rows); the
-// partition weights of its rows are computed once into LDS.
+// added in order (deterministic).  One workgroup per (entry, 1024/D rows:
+// one output of 4 dims per thread); the partition weights of its rows are
+// computed once into LDS.
 // ---------------------------------------------------------------------------
 struct ReduceArgs {
   void* out;
@@ -879,52 +880,58 @@ struct ReduceArgs {
   int QL, Hq, G, D, rows_total, rows_per_group, q_fp16, has_sinks, chunks_per_entry;
 };
 
-constexpr int RED_ROWS = 8;
+// Rows per reducer workgroup: one (row, 4-dim) output per thread of 256.
+template <int D>
+constexpr int red_rows() { return 1024 / D; }
 
+template <int D>
 __global__ __launch_bounds__(256) void pa_reduce_kernel(ReduceArgs a) {
-  __shared__ float wgt[RED_ROWS][kMaxPartitions];
-  __shared__ float rowf[RED_ROWS];
+  constexpr int RR = red_rows<D>();
+  constexpr int Q4 = D / 4;
+  constexpr int RCH = 16;  // partitions' loads in flight per round trip
+  static_assert(RR * Q4 == 256 && RR % 4 == 0, "one output per thread");
+  __shared__ float wgt[RR][kMaxPartitions];
+  __shared__ float rowf[RR];
   const ReduceItem e = a.entries[blockIdx.x / a.chunks_per_entry];
   const int chunk = blockIdx.x % a.chunks_per_entry;
-  const int D = a.D, rpg = a.rows_per_group;
+  const int rpg = a.rows_per_group;
   const int row0 = e.rg * kMaxRowsPerItem;
   const int nrows = min(rpg, a.rows_total - row0);
-  const int r0 = chunk * RED_ROWS;
+  const int r0 = chunk * RR;
   const size_t slot_f = (size_t)rpg * (2 + D);
   const int tid = threadIdx.x;
   const int np = e.nparts;
   const float* base = a.workspace + (size_t)e.first_slot * slot_f;
-  const int q4 = D / 4;
-  // The partial O of the thread's first output (row, 4 dims) for the first
-  // eight partitions is loaded before the weights are known, so that the
-  // merge costs one round trip to memory for up to eight partitions.
-  f4 v0[8];
-  {
-    const int rr = tid / q4, d4 = (tid % q4) * 4;
-    const int r = min(r0 + min(rr, RED_ROWS - 1), nrows - 1);
+  // The thread's output (row rr, 4 dims d4).  Its partial O for the first RCH
+  // partitions is loaded before the weights are known, so that the merge
+  // costs one round trip to memory for up to RCH partitions.
+  const int rr = tid / Q4, d4 = (tid % Q4) * 4;
+  const int r = r0 + rr;
+  const float* po = base + 2 * rpg + (size_t)min(r, nrows - 1) * D + d4;
+  f4 v0[RCH];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v0[j] = *(const f4*)(base + (size_t)min(j, np - 1) * slot_f + 2 * rpg + (size_t)r * D + d4);
-  }
-  // per-row weights: wave w takes rows w and w + 4, lanes over partitions
-  // (p = lane + 64k); both rows' (max, sum) loads are issued together
+  for (int j = 0; j < RCH; ++j) v0[j] = *(const f4*)(po + (size_t)min(j, np - 1) * slot_f);
+  // per-row weights: wave w takes rows w, w + 4, ..., lanes over partitions
+  // (p = lane + 64k); the rows' (max, sum) loads are issued together
   {
+    constexpr int XR = RR / 4;
     const int wv = tid >> 6, lane = tid & 63;
-    float mv[2][4], lv[2][4], skv[2] = {0.f, 0.f};
+    float mv[XR][4], lv[XR][4], skv[XR];
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      if (a.has_sinks) skv[x] = a.sinks[e.kvh * a.G + (row0 + min(r0 + wv + 4 * x, nrows - 1)) % a.G];
-      const int r = min(r0 + wv + 4 * x, nrows - 1);
+    for (int x = 0; x < XR; ++x) {
+      const int rx = min(r0 + wv + 4 * x, nrows - 1);
+      skv[x] = a.has_sinks ? a.sinks[e.kvh * a.G + (row0 + rx) % a.G] : 0.f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float* sp = base + (size_t)min(lane + 64 * k, np - 1) * slot_f;
-        mv[x][k] = sp[r];
-        lv[x][k] = sp[rpg + r];
+        mv[x][k] = sp[rx];
+        lv[x][k] = sp[rpg + rx];
       }
     }
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int rr = wv + 4 * x, r = r0 + rr;
-      if (r >= nrows) continue;  // wave-uniform
+    for (int x = 0; x < XR; ++x) {
+      const int rw = wv + 4 * x;
+      if (r0 + rw >= nrows) continue;  // wave-uniform
       float M = -INFINITY;
 #pragma unroll
       for (int k = 0; k < 4; ++k)
@@ -936,7 +943,7 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(ReduceArgs a) {
         const int p = lane + 64 * k;
         if (p < np) {
           const float wp = lv[x][k] > 0.f ? __builtin_amdgcn_exp2f(mv[x][k] - M) : 0.f;
-          wgt[rr][p] = wp;
+          wgt[rw][p] = wp;
           den += wp * lv[x][k];
         }
       }
@@ -953,53 +960,48 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(ReduceArgs a) {
             f = 1.0f / den;
           }
         }
-        rowf[rr] = f;
+        rowf[rw] = f;
       }
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < RED_ROWS * q4; idx += blockDim.x) {
-    const int rr = idx / q4, d4 = (idx % q4) * 4;
-    const int r = r0 + rr;
-    if (r >= nrows) continue;
-    f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-    const float f = rowf[rr];
-    if (f > 0.f) {
-      // eight partitions' loads in flight at a time (the first eight of the
-      // thread's first output are already in v0); partitions without visible
-      // tokens are skipped by a select, not a branch
-      const float* po = base + 2 * rpg + (size_t)r * D + d4;
-      for (int p0 = 0; p0 < np; p0 += 8) {
-        f4 v[8];
-        if (p0 == 0 && idx == tid) {
+  if (r >= nrows) return;
+  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+  const float f = rowf[rr];
+  if (f > 0.f) {
+    // partitions in order, RCH loads in flight at a time (the first RCH are
+    // already in v0); partitions without visible tokens are skipped by a
+    // select, not a branch
+    for (int p0 = 0; p0 < np; p0 += RCH) {
+      f4 v[RCH];
+      if (p0 == 0) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] = v0[j];
-        } else {
+        for (int j = 0; j < RCH; ++j) v[j] = v0[j];
+      } else {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] = *(const f4*)(po + (size_t)min(p0 + j, np - 1) * slot_f);
-        }
+        for (int j = 0; j < RCH; ++j) v[j] = *(const f4*)(po + (size_t)min(p0 + j, np - 1) * slot_f);
+      }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float wp = p0 + j < np ? wgt[rr][p0 + j] : 0.f;
-          if (wp != 0.f) acc += wp * v[j];
-        }
+      for (int j = 0; j < RCH; ++j) {
+        const float wp = p0 + j < np ? wgt[rr][p0 + j] : 0.f;
+        if (wp != 0.f) acc += wp * v[j];
       }
     }
-    const f4 v = acc * f;
-    const int gr = row0 + r, i = gr / a.G, hl = gr % a.G;
-    const int h = e.kvh * a.G + hl;
-    const long ooff = (((long)e.seq * a.QL + i) * a.Hq + h) * D + d4;
-    uint16_t hv[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (a.q_fp16)
-        hv[k] = __builtin_bit_cast(uint16_t, (_Float16)v[k]);
-      else
-        hv[k] = __builtin_bit_cast(uint16_t, (__bf16)v[k]);
-    }
-    *(u32x2*)((uint16_t*)a.out + ooff) =
-        u32x2{(uint32_t)hv[0] | ((uint32_t)hv[1] << 16), (uint32_t)hv[2] | ((uint32_t)hv[3] << 16)};
   }
+  const f4 v = acc * f;
+  const int gr = row0 + r, i = gr / a.G, hl = gr % a.G;
+  const int h = e.kvh * a.G + hl;
+  const long ooff = (((long)e.seq * a.QL + i) * a.Hq + h) * D + d4;
+  uint16_t hv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (a.q_fp16)
+      hv[k] = __builtin_bit_cast(uint16_t, (_Float16)v[k]);
+    else
+      hv[k] = __builtin_bit_cast(uint16_t, (__bf16)v[k]);
+  }
+  *(u32x2*)((uint16_t*)a.out + ooff) =
+      u32x2{(uint32_t)hv[0] | ((uint32_t)hv[1] << 16), (uint32_t)hv[2] | ((uint32_t)hv[3] << 16)};
 }
 
 // ---------------------------------------------------------------------------
@@ -1134,9 +1136,13 @@ extern "C" pa_status pa_reduce(const pa_plan_t* plan, void* out, const float* si
   ra.rows_per_group = P.rows_per_group;
   ra.q_fp16 = P.prob.q_dtype == PA_FP16;
   ra.has_sinks = P.prob.has_sinks;
-  ra.chunks_per_entry = (P.rows_per_group + RED_ROWS - 1) / RED_ROWS;
+  const int rr = P.prob.head_dim == 256 ? red_rows<256>() : red_rows<128>();
+  ra.chunks_per_entry = (P.rows_per_group + rr - 1) / rr;
   const unsigned grid = (unsigned)(P.reduce.size() * ra.chunks_per_entry);
-  hipLaunchKernelGGL(pa_reduce_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, ra);
+  if (P.prob.head_dim == 256)
+    hipLaunchKernelGGL(pa_reduce_kernel<256>, dim3(grid), dim3(256), 0, (hipStream_t)stream, ra);
+  else
+    hipLaunchKernelGGL(pa_reduce_kernel<128>, dim3(grid), dim3(256), 0, (hipStream_t)stream, ra);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(PA_ERR_DEVICE, std::string("reduce launch failed: ") + hipGetErrorString(err));
   return PA_OK;
