@@ -62,6 +62,19 @@ def load_traffic(workload: str, launches_kv_bytes: float):
     return None
 
 
+def load_mfma(workload: str):
+    """MFMA busy fraction of the decode kernel from a committed rocprofv3
+    counter run, if it was taken on the current kernel source."""
+    import glob
+
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}_mfma.json"))):
+        with open(path) as f:
+            t = json.load(f)
+        if t.get("kernel_sha") == source_sha():
+            return round(t.get("mfma_busy_fraction"), 4)
+    return None
+
+
 def make_inputs(workload: str):
     if workload == "sparse":
         return W.config_sparse(), dict(partition_tokens=512)
@@ -224,6 +237,7 @@ def main():
         "frac_of_peak_cold": round(gbps / PEAK_GBPS, 4),
         "wall_s_timed_regions": round(timed_wall, 3),
         "roofline": roofline,
+        "mfma_busy_fraction": load_mfma(args.workload),
         "cpu_baseline": cpu,
         "kernel_sha": source_sha(),
     }

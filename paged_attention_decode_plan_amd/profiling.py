@@ -6,6 +6,10 @@
   traffic  FETCH_SIZE / WRITE_SIZE counter CSVs -> HBM bytes per launch of a
            kernel, each counter scaled by what it reads for a device-to-device
            copy of known size run in the same process
+  mfma     one counter CSV with SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE and
+           instruction counts -> MFMA busy fraction of the kernel (busy cycles
+           summed over SIMDs / (GPU-active cycles x SIMDs), GRBM_GUI_ACTIVE
+           being summed over the XCDs) and MFMA / VALU instructions per launch
 
 The counters report KiB per dispatch; the copy calibration turns them into
 bytes whatever request granularity the counter assumes.
@@ -111,6 +115,31 @@ def cmd_traffic(a):
     print(text)
 
 
+def cmd_mfma(a):
+    rows = [r for r in _rows(a.csv) if re.search(a.kernel, r["Kernel_Name"])]
+    if not rows:
+        raise SystemExit(f"no dispatches of {a.kernel!r} in {a.csv}")
+    per = {}
+    for r in rows:
+        per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    means = {k: statistics.mean(v) for k, v in per.items()}
+    simds = a.cu_count * 4
+    res = {"kernel": a.kernel, "workload": a.workload, "kernel_sha": source_sha(), "command": a.command,
+           "dispatches": len(per.get("GRBM_GUI_ACTIVE", [])), "counters_per_dispatch": means, "simds": simds,
+           "xcds": a.xcds}
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in means and "GRBM_GUI_ACTIVE" in means:
+        active = means["GRBM_GUI_ACTIVE"] / a.xcds  # GPU-active cycles of the dispatch
+        res["active_cycles"] = active
+        res["mfma_busy_fraction"] = means["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * simds)
+    if a.expected_mfma:
+        res["expected_mfma_per_launch"] = a.expected_mfma
+    text = json.dumps(res, indent=1)
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text + "\n")
+    print(text)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(prog="python -m paged_attention_decode_plan_amd.profiling")
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -134,6 +163,16 @@ def main(argv=None):
     t.add_argument("--command-write", default="")
     t.add_argument("--out")
     t.set_defaults(fn=cmd_traffic)
+    m = sub.add_parser("mfma")
+    m.add_argument("--csv", required=True, help="counter_collection.csv of the MFMA counter run")
+    m.add_argument("--kernel", default="pa_stream_kernel|pa_decode_kernel")
+    m.add_argument("--cu-count", type=int, default=256)
+    m.add_argument("--xcds", type=int, default=8, help="XCDs whose GRBM_GUI_ACTIVE the counter sums")
+    m.add_argument("--expected-mfma", type=float, default=0.0, help="MFMA instructions per launch by the algorithm")
+    m.add_argument("--workload", default="")
+    m.add_argument("--command", default="")
+    m.add_argument("--out")
+    m.set_defaults(fn=cmd_mfma)
     a = ap.parse_args(argv)
     a.fn(a)
 
