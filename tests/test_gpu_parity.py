@@ -219,3 +219,41 @@ def test_stream_kernel_run_to_run_bit_exact(page):
     compare(a, O.attend(inp), "stream kernel")
     b, _ = run(inp, dev=dev, plan=plan)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("ql,hq,page", [(4, 16, 128), (1, 8, 16)])
+def test_pages_past_4gib(ql, hq, page):
+    """Caches of more than 4 GiB (the pages' 200 000-token MI355 shape needs
+    64-bit page offsets): the sequences' pages are moved to page ids whose
+    byte offset in K and V is past 2^32, in the streaming (64-row) and the
+    tile (8-row) kernels, against the oracle on the compact original."""
+    inp = W.make_dense_case(70 + page, [3000, 700, 1], query_len=ql, num_q_heads=hq, num_kv_heads=1, head_dim=128,
+                            page_size=page, scale_mode="token", sliding_window=0)
+    p = inp.problem
+    page_bytes = 128 * page  # FP8, one KV head
+    big = (4 << 30) // page_bytes + 4 * p.num_pages  # more than 4 GiB of K (and of V)
+    rng = np.random.default_rng(71)
+    remap = torch.as_tensor(rng.choice(np.arange(big - 4 * p.num_pages, big), size=p.num_pages, replace=False))
+    assert int(remap.min()) * page_bytes >= 1 << 32
+    dev = to_device(inp)
+    kb = torch.zeros((big,) + tuple(dev["k_cache"].shape[1:]), dtype=dev["k_cache"].dtype, device="cuda")
+    vb = torch.zeros((big,) + tuple(dev["v_cache"].shape[1:]), dtype=dev["v_cache"].dtype, device="cuda")
+    ksb = torch.ones((big,) + tuple(dev["k_scale"].shape[1:]), dtype=torch.float32, device="cuda")
+    vsb = torch.ones_like(ksb)
+    rd = remap.to("cuda")
+    kb[rd] = dev["k_cache"]
+    vb[rd] = dev["v_cache"]
+    ksb[rd] = dev["k_scale"]
+    vsb[rd] = dev["v_scale"]
+    bt = remap[inp.block_tables.long()].to(torch.int32).to("cuda")
+    prob = B.problem_of(p)
+    prob.num_pages = big
+    announce(f"pages past 4 GiB ql={ql} hq={hq} page={page} ({big} pages)")
+    plan = B.Plan(prob, inp.context_lens, cu_count=64).allocate("cuda")
+    plan.workspace.fill_(float("nan"))
+    out = torch.full_like(dev["q"], float("nan"))
+    B.attend(plan, out, dev["q"], kb, vb, bt, dev["context_lens"], ksb, vsb, None)
+    torch.cuda.synchronize()
+    compare(out.float().cpu().numpy(), O.attend(inp), "pages past 4 GiB")
+    del kb, vb, ksb, vsb
+    torch.cuda.empty_cache()
