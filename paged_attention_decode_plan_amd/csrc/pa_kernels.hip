@@ -179,7 +179,141 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   const long id_end = SPARSE ? (long)hi_u : ((long)hi_u + ps - 1) / ps;  // one past the last valid id
   const int nstaged = (int)max(0L, min((long)a.stage_limit, min((long)(te - tb) * ppt, id_end - id0)));
   const int32_t* bt_row = a.block_tables + (long)s * a.table_stride;
-  for (int k = tid; k < nstaged; k += NTHREADS) ids[k] = bt_row[id0 + k];
+  // ---- the item's first reads, issued before the query is prepared ----
+  // The page ids (staged in LDS after the query split), the query rows'
+  // raw bits and then the first tiles' DMA with page ids read straight from
+  // the block table: the DMA latency overlaps the query split.
+  constexpr int IDR = kStageCap / NTHREADS;
+  int32_t idr[IDR];
+#pragma unroll
+  for (int j = 0; j < IDR; ++j) {
+    const long k = min((long)(tid + NTHREADS * j), (long)max(nstaged - 1, 0));
+    idr[j] = bt_row[min(max(id0 + k, 0L), (long)a.table_stride - 1)];  // in the row whatever the item
+  }
+  constexpr int NQR = FP8 ? (D / 128) * 4 : D / 32;  // 16-byte query loads per row tile
+  u32x4 qraw[NRW][NQR];
+#pragma unroll
+  for (int rt = 0; rt < NRW; ++rt) {
+    const int r = (wr * NRW + rt) * 16 + c;
+    const int gr = row0 + (r < nrows ? r : 0);  // padding rows read row 0 (zeroed at use)
+    const int i = gr / a.G, hl = gr % a.G;
+    const uint16_t* qrow = (const uint16_t*)a.q + (((long)s * a.QL + i) * a.Hq + (long)kvh * a.G + hl) * D;
+#pragma unroll
+    for (int x = 0; x < NQR; ++x)
+      qraw[rt][x] = FP8 ? *(const u32x4*)(qrow + 128 * (x / 4) + 32 * g + 8 * (x % 4))
+                        : *(const u32x4*)(qrow + 32 * x + 8 * g);
+  }
+  const bool per_token = FP8 && a.scale_mode == PA_SCALE_PER_TOKEN;
+  const float kscale0 = (FP8 && !per_token) ? a.k_scale[0] : 1.0f;  // per-tensor scales
+  const float vscale0 = (FP8 && !per_token) ? a.v_scale[0] : 1.0f;
+  const uint8_t* kbase = a.k_cache + (long long)kvh * a.head_stride;
+  const uint8_t* vbase = a.v_cache + (long long)kvh * a.head_stride;
+  // ---- dense: DMA of one tile into an LDS stage ----
+  // K unit u = tid + k*NTHREADS holds chunk tid/TT + 2k of token kswz(tid%TT);
+  // V unit u holds 16 bytes of row tid/VUPR + k*(NTHREADS/VUPR) at position
+  // tid%VUPR.  So each thread's K units share one page (likewise V), and its
+  // k-th unit sits a constant stride after the first.  Every thread issues
+  // the same number of loads per tile (a page outside the visible span is
+  // replaced by page 0 of the head: those LDS bytes are masked), so a
+  // constant vmcnt tracks the tiles in flight.
+  constexpr int KCH = NTHREADS / TT;       // chunks covered per k step
+  constexpr int VRS = NTHREADS / T::VUPR;  // V rows covered per k step
+  const int k_tok = kswz(tid % TT);
+  const int k_pg = k_tok / ps;
+  const long k_off = ((long)(tid / TT) * ps + k_tok % ps) * 16;
+  const long k_step = (long)KCH * ps * 16;
+  const int v_row = tid / T::VUPR;
+  const int v_tok = ((tid % T::VUPR) ^ (v_row & (T::VUPR - 1))) * T::X;  // first token of the unit
+  const int v_pg = v_tok / ps;
+  const int v_sx = (v_tok % ps) / T::X;
+  const long v_off = a.v_transposed ? ((long)v_sx * D + v_row) * 16 : (long)v_row * ps * T::E + v_sx * 16;
+  const long v_step = a.v_transposed ? (long)VRS * 16 : (long)VRS * ps * T::E;
+  const int s_tok = (lane & 31) * 4;  // scales: wave 0, lanes 0-31 K, 32-63 V
+  const int s_pg = s_tok / ps;
+  const float* s_src0 = (lane >> 5) ? a.v_scale : a.k_scale;
+
+  // The page ids a thread's DMA of one tile uses (K, V, scales); a page
+  // without visible tokens gets -1 and is replaced by page 0 of the head
+  // (its LDS bytes are masked).
+  auto tile_ids = [&](int tile, auto get_id, long (&id)[3]) {
+    const int ts = t0 + tile * TT;
+    const long jt = (long)(tile - tb) * ppt;
+    auto page_ok = [&](int j) {
+      int tok0 = ts + j * ps;
+      return tok0 < hi_u && tok0 + ps > lo_u;
+    };
+    id[0] = page_ok(k_pg) ? get_id(jt + k_pg) : -1;
+    id[1] = page_ok(v_pg) ? get_id(jt + v_pg) : -1;
+    id[2] = (FP8 && per_token && w == 0 && page_ok(s_pg)) ? get_id(jt + s_pg) : -1;
+  };
+  // The block-table entries of those pages, read unconditionally (an index
+  // kept inside the row) so that all of them go out together.
+  auto tile_entries = [&](int tile, long (&e)[3]) {
+    const long jt = (long)(tile - tb) * ppt;
+    auto entry = [&](long j) -> long { return (long)bt_row[min(max(id0 + j, 0L), (long)a.table_stride - 1)]; };
+    e[0] = entry(jt + k_pg);
+    e[1] = entry(jt + v_pg);
+    e[2] = entry(jt + s_pg);
+  };
+  auto tile_ids_from = [&](int tile, const long (&e)[3], long (&id)[3]) {
+    const int ts = t0 + tile * TT;
+    auto page_ok = [&](int j) {
+      int tok0 = ts + j * ps;
+      return tok0 < hi_u && tok0 + ps > lo_u;
+    };
+    id[0] = page_ok(k_pg) ? e[0] : -1;
+    id[1] = page_ok(v_pg) ? e[1] : -1;
+    id[2] = (FP8 && per_token && w == 0 && page_ok(s_pg)) ? e[2] : -1;
+  };
+  auto issue_tile_at = [&](uint8_t* stg, const long (&id)[3]) {
+    const uint8_t* ksrc = kbase + k_off + (id[0] >= 0 ? id[0] * a.page_stride : 0);
+    uint8_t* kdst = stg + (tid - lane) * 16;
+#pragma unroll
+    for (int k = 0; k < T::KPT; ++k)
+      __builtin_amdgcn_global_load_lds((const void*)(ksrc + k * k_step), (lds_void*)(kdst + k * NTHREADS * 16), 16,
+                                       0, 0);
+    const uint8_t* vsrc = vbase + v_off + (id[1] >= 0 ? id[1] * a.page_stride : 0);
+    uint8_t* vdst = stg + T::KBYTES + (tid - lane) * 16;
+#pragma unroll
+    for (int k = 0; k < T::VPT; ++k)
+      __builtin_amdgcn_global_load_lds((const void*)(vsrc + k * v_step), (lds_void*)(vdst + k * NTHREADS * 16), 16,
+                                       0, 0);
+    if (FP8 && per_token && w == 0) {
+      const float* src = s_src0 + (id[2] >= 0 ? (id[2] * a.Hkv + kvh) * ps + s_tok % ps : 0);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(stg + T::KBYTES + T::VBYTES), 16, 0, 0);
+    }
+  };
+  auto issue_tile_ids = [&](int tile, uint8_t* stg, auto get_id) {
+    long id[3];
+    tile_ids(tile, get_id, id);
+    issue_tile_at(stg, id);
+  };
+  if constexpr (!SPARSE) {
+    // The first tiles' page ids straight from the block table, read with the
+    // query rows and the staged ids; one wait covers them all (the empty
+    // statement makes the compiler take it here), so that the DMA issue and
+    // the query split after it wait for nothing else.
+    long pe[NST - 1][3];
+#pragma unroll
+    for (int k = 0; k < NST - 1; ++k) tile_entries(tb + k, pe[k]);
+    asm volatile("" ::"v"(kscale0), "v"(vscale0));
+#pragma unroll
+    for (int rt = 0; rt < NRW; ++rt)
+#pragma unroll
+      for (int x = 0; x < NQR; ++x) asm volatile("" ::"v"(qraw[rt][x]));
+#pragma unroll
+    for (int j = 0; j < IDR; ++j) asm volatile("" ::"v"(idr[j]));
+#pragma unroll
+    for (int k = 0; k < NST - 1; ++k) asm volatile("" ::"v"(pe[k][0]), "v"(pe[k][1]), "v"(pe[k][2]));
+#pragma unroll
+    for (int k = 0; k < NST - 1; ++k)
+      if (tb + k < te) {
+        long id[3];
+        tile_ids_from(tb + k, pe[k], id);
+        issue_tile_at(stage_base + k * T::STAGE, id);
+      }
+  }
+
 
   // ---- query fragments of the wave's rows ----
   // FP8 caches: QK runs on the FP8 matrix cores with K as stored.  The query
@@ -207,7 +341,7 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
       for (int kk = 0; kk < NQ; ++kk) {
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-          const u32x4 raw = valid ? *(const u32x4*)(qrow + 128 * kk + 32 * g + 8 * h) : u32x4{0, 0, 0, 0};
+          const u32x4 raw = valid ? qraw[rt][4 * kk + h] : u32x4{0, 0, 0, 0};
 #pragma unroll
           for (int p = 0; p < 8; ++p) {
             const uint16_t bits = (uint16_t)(raw[p >> 1] >> (16 * (p & 1)));
@@ -258,17 +392,16 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
     } else {
 #pragma unroll
       for (int m = 0; m < NM; ++m)
-        qf[rt][m][0] = valid ? __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 32 * m + 8 * g))
+        qf[rt][m][0] = valid ? __builtin_bit_cast(bf16x8, qraw[rt][m])
                              : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
       crow[rt] = a.scale_log2;
     }
   }
-  const bool per_token = FP8 && a.scale_mode == PA_SCALE_PER_TOKEN;
   float vs_ref = 1.0f;  // O holds sum p*v / vs_ref
   if (FP8 && !per_token) {
 #pragma unroll
-    for (int rt = 0; rt < NRW; ++rt) crow[rt] *= a.k_scale[0];
-    vs_ref = a.v_scale[0];
+    for (int rt = 0; rt < NRW; ++rt) crow[rt] *= kscale0;
+    vs_ref = vscale0;
   }
   if (per_token) vs_ref = 0.f;
   float inv_ref = per_token ? 0.f : 1.0f;
@@ -292,10 +425,19 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   int* restart_flag = (int*)(stats + S::STATS / 4 - 4);
   if (tid == 0) *restart_flag = 0;
 
-  const uint8_t* kbase = a.k_cache + (long long)kvh * a.head_stride;
-  const uint8_t* vbase = a.v_cache + (long long)kvh * a.head_stride;
 
-  __syncthreads();  // staged ids visible
+  // ---- page ids of the item into LDS ----
+#pragma unroll
+  for (int j = 0; j < IDR; ++j)
+    if (tid + NTHREADS * j < nstaged) ids[tid + NTHREADS * j] = idr[j];
+
+  // Staged ids (and the cleared restart flag) visible to every wave: a bare
+  // barrier after this wave's LDS writes, since a full __syncthreads would
+  // also wait for the first tiles' DMA issued above.
+  wait_lgkm0();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 
   // Page id (dense) or token slot (sparse) number j of the item: from the LDS
   // list, or past the staged bound from the block table.  The two readers are
@@ -304,57 +446,6 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   auto staged_id = [&](long j) -> long { return (long)ids[j]; };
   auto item_id = [&](long j) -> long { return j < nstaged ? (long)ids[j] : (long)bt_row[id0 + j]; };
 
-  // ---- dense: DMA of one tile into an LDS stage ----
-  // K unit u = tid + k*NTHREADS holds chunk tid/TT + 2k of token kswz(tid%TT);
-  // V unit u holds 16 bytes of row tid/VUPR + k*(NTHREADS/VUPR) at position
-  // tid%VUPR.  So each thread's K units share one page (likewise V), and its
-  // k-th unit sits a constant stride after the first.  Every thread issues
-  // the same number of loads per tile (a page outside the visible span is
-  // replaced by page 0 of the head: those LDS bytes are masked), so a
-  // constant vmcnt tracks the tiles in flight.
-  constexpr int KCH = NTHREADS / TT;       // chunks covered per k step
-  constexpr int VRS = NTHREADS / T::VUPR;  // V rows covered per k step
-  const int k_tok = kswz(tid % TT);
-  const int k_pg = k_tok / ps;
-  const long k_off = ((long)(tid / TT) * ps + k_tok % ps) * 16;
-  const long k_step = (long)KCH * ps * 16;
-  const int v_row = tid / T::VUPR;
-  const int v_tok = ((tid % T::VUPR) ^ (v_row & (T::VUPR - 1))) * T::X;  // first token of the unit
-  const int v_pg = v_tok / ps;
-  const int v_sx = (v_tok % ps) / T::X;
-  const long v_off = a.v_transposed ? ((long)v_sx * D + v_row) * 16 : (long)v_row * ps * T::E + v_sx * 16;
-  const long v_step = a.v_transposed ? (long)VRS * 16 : (long)VRS * ps * T::E;
-  const int s_tok = (lane & 31) * 4;  // scales: wave 0, lanes 0-31 K, 32-63 V
-  const int s_pg = s_tok / ps;
-  const float* s_src0 = (lane >> 5) ? a.v_scale : a.k_scale;
-
-  auto issue_tile_ids = [&](int tile, uint8_t* stg, auto get_id) {
-    const int ts = t0 + tile * TT;
-    const long jt = (long)(tile - tb) * ppt;
-    auto page_ok = [&](int j) {
-      int tok0 = ts + j * ps;
-      return tok0 < hi_u && tok0 + ps > lo_u;
-    };
-    const uint8_t* ksrc = kbase + k_off;
-    if (page_ok(k_pg)) ksrc += get_id(jt + k_pg) * a.page_stride;
-    uint8_t* kdst = stg + (tid - lane) * 16;
-#pragma unroll
-    for (int k = 0; k < T::KPT; ++k)
-      __builtin_amdgcn_global_load_lds((const void*)(ksrc + k * k_step), (lds_void*)(kdst + k * NTHREADS * 16), 16,
-                                       0, 0);
-    const uint8_t* vsrc = vbase + v_off;
-    if (page_ok(v_pg)) vsrc += get_id(jt + v_pg) * a.page_stride;
-    uint8_t* vdst = stg + T::KBYTES + (tid - lane) * 16;
-#pragma unroll
-    for (int k = 0; k < T::VPT; ++k)
-      __builtin_amdgcn_global_load_lds((const void*)(vsrc + k * v_step), (lds_void*)(vdst + k * NTHREADS * 16), 16,
-                                       0, 0);
-    if (FP8 && per_token && w == 0) {
-      const float* src = s_src0;
-      if (page_ok(s_pg)) src += (get_id(jt + s_pg) * a.Hkv + kvh) * ps + s_tok % ps;
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(stg + T::KBYTES + T::VBYTES), 16, 0, 0);
-    }
-  };
   auto issue_tile = [&](int tile, uint8_t* stg) {
     if (min((long)(tile - tb + 1) * ppt, id_end - id0) <= (long)nstaged)
       issue_tile_ids(tile, stg, staged_id);  // every id the tile needs is in LDS
@@ -661,12 +752,16 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   }
 
   // ---- main loop: one attempt over the item's tiles ----
+  bool first_attempt = true;
   auto attempt = [&](auto PTc) {
     if constexpr (!SPARSE) {
-      // NST-deep ring: tiles tb .. tb+NST-2 in flight before the first compute.
+      // NST-deep ring: tiles tb .. tb+NST-2 in flight before the first compute
+      // (the first attempt's were issued before the query split).
+      if (!first_attempt) {
 #pragma unroll
-      for (int k = 0; k < NST - 1; ++k)
-        if (tb + k < te) issue_tile(tb + k, stage_base + k * T::STAGE);
+        for (int k = 0; k < NST - 1; ++k)
+          if (tb + k < te) issue_tile(tb + k, stage_base + k * T::STAGE);
+      }
       // returns false if an overflow stopped the attempt
       auto tiles = [&](auto INc, int from, int to) -> bool {
         for (int tile = from; tile < to; ++tile) {
@@ -721,7 +816,7 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
     }
   };
   auto run = [&](auto PTc) {
-    for (;;) {
+    for (;; first_attempt = false) {
 #pragma unroll
       for (int rt = 0; rt < NRW; ++rt) {
         l_part[rt] = 0.f;
