@@ -130,6 +130,7 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   const WorkItem it = a.items[blockIdx.x];
   const int s = it.seq, kvh = it.kvh, rg = it.rg;
   const int ps = a.page_size;
+  const int ps_log2 = 31 - __builtin_clz(ps);
   const long cap = SPARSE ? (long)a.table_stride : (long)a.table_stride * ps;
   const int L = (int)min(max((long)a.context_lens[s], 0L), cap);
 
@@ -464,27 +465,39 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
       st.k[k] = u32x4{0, 0, 0, 0};
       if (ts + t < hi_u) {
         long Sl = item_id(jt + t);
-        long pid = Sl / ps;
-        int slot = (int)(Sl % ps);
+        long pid = Sl >> ps_log2;  // page sizes are powers of two
+        int slot = (int)Sl & (ps - 1);
         st.k[k] = *(const u32x4*)(kbase + pid * a.page_stride + ((long)cc * ps + slot) * 16);
       }
     }
+    // V unit k of this thread: dim d = tid / VUPR + k * (NTHREADS / VUPR),
+    // tokens tfirst .. tfirst + X - 1, where tfirst is the same for every k
+    // (NTHREADS / VUPR is a multiple of VUPR): the tokens' slots and page
+    // addresses are worked out once per tile.
+    static_assert((NTHREADS / T::VUPR) % T::VUPR == 0, "one token group per thread");
+    const int d0 = tid / T::VUPR;
+    const int tfirst = ((tid % T::VUPR) ^ (d0 & (T::VUPR - 1))) * T::X;
+    const long dstride = a.v_transposed ? 16 : (long)ps * T::E;  // bytes between dims of one token
+    const uint8_t* tok[T::X];
+    bool tvis[T::X];
+#pragma unroll
+    for (int e = 0; e < T::X; ++e) {
+      const int t = tfirst + e;
+      tvis[e] = ts + t < hi_u;
+      const long Sl = tvis[e] ? item_id(jt + t) : 0;
+      const long pid = Sl >> ps_log2;
+      const int slot = (int)Sl & (ps - 1);
+      const long off = a.v_transposed ? (long)(slot / T::X) * D * 16 + (slot % T::X) * T::E : (long)slot * T::E;
+      tok[e] = vbase + pid * a.page_stride + off + (long)d0 * dstride;
+    }
 #pragma unroll
     for (int k = 0; k < T::VPT; ++k) {
-      int u = tid + k * NTHREADS;
-      int d = u / T::VUPR, q = u % T::VUPR;
-      int tfirst = (q ^ (d & (T::VUPR - 1))) * T::X;
+      const long dk = (long)k * (NTHREADS / T::VUPR) * dstride;
       uint8_t bytes[16];
 #pragma unroll
       for (int e = 0; e < T::X; ++e) {
-        int t = tfirst + e;
-        if (ts + t < hi_u) {
-          long Sl = item_id(jt + t);
-          long pid = Sl / ps;
-          int slot = (int)(Sl % ps);
-          long off = a.v_transposed ? ((long)(slot / T::X) * D + d) * 16 + (slot % T::X) * T::E
-                                    : ((long)d * ps + slot) * T::E;
-          const uint8_t* src = vbase + pid * a.page_stride + off;
+        if (tvis[e]) {
+          const uint8_t* src = tok[e] + dk;
 #pragma unroll
           for (int b = 0; b < T::E; ++b) bytes[e * T::E + b] = src[b];
         } else {
@@ -502,8 +515,8 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
         f[e] = 0.f;
         if (ts + s_tok + e < hi_u) {
           long Sl = item_id(jt + s_tok + e);
-          long pid = Sl / ps;
-          int slot = (int)(Sl % ps);
+          long pid = Sl >> ps_log2;
+          int slot = (int)Sl & (ps - 1);
           f[e] = sc[(pid * a.Hkv + kvh) * ps + slot];
         }
       }
