@@ -458,17 +458,19 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   auto load_sparse = [&](int tile, Staged<D, FP8, NTHREADS>& st) {
     const int ts = t0 + tile * TT;
     const long jt = (long)(tile - tb) * ppt;
+    // K unit k of this thread: token kswz(tid % TT) (the same for every k,
+    // NTHREADS being a multiple of TT), chunk tid / TT + k * (NTHREADS / TT)
+    {
+      static_assert(NTHREADS % TT == 0, "one K token per thread");
+      const int t = kswz(tid % TT);
+      const bool vis = ts + t < hi_u;
+      const long Sl = vis ? item_id(jt + t) : 0;
+      const long pid = Sl >> ps_log2;  // page sizes are powers of two
+      const int slot = (int)Sl & (ps - 1);
+      const uint8_t* kt = kbase + pid * a.page_stride + ((long)(tid / TT) * ps + slot) * 16;
 #pragma unroll
-    for (int k = 0; k < T::KPT; ++k) {
-      int u = tid + k * NTHREADS;
-      int cc = u / TT, t = kswz(u % TT);
-      st.k[k] = u32x4{0, 0, 0, 0};
-      if (ts + t < hi_u) {
-        long Sl = item_id(jt + t);
-        long pid = Sl >> ps_log2;  // page sizes are powers of two
-        int slot = (int)Sl & (ps - 1);
-        st.k[k] = *(const u32x4*)(kbase + pid * a.page_stride + ((long)cc * ps + slot) * 16);
-      }
+      for (int k = 0; k < T::KPT; ++k)
+        st.k[k] = vis ? *(const u32x4*)(kt + (long)k * (NTHREADS / TT) * ps * 16) : u32x4{0, 0, 0, 0};
     }
     // V unit k of this thread: dim d = tid / VUPR + k * (NTHREADS / VUPR),
     // tokens tfirst .. tfirst + X - 1, where tfirst is the same for every k
