@@ -257,3 +257,15 @@ def test_pages_past_4gib(ql, hq, page):
     compare(out.float().cpu().numpy(), O.attend(inp), "pages past 4 GiB")
     del kb, vb, ksb, vsb
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("page", [64, 128])
+def test_stream_kernel_device_context_longer_than_plan(page):
+    """64-row FP8 items (the streaming kernel) with device lengths beyond the
+    planned ones: the open-ended last partition reads the page ids past the
+    staged range from the block table."""
+    inp = W.make_dense_case(80 + page, [9000, 2500, 300], query_len=4, num_q_heads=16, num_kv_heads=1,
+                            head_dim=128, page_size=page, scale_mode="token", sliding_window=0)
+    announce(f"stream kernel, plan lengths below device lengths page={page}")
+    got, _ = run(inp, lens_for_plan=[1000, 300, 1], cu_count=16)
+    compare(got, O.attend(inp), "stream kernel, longer device context")
