@@ -39,6 +39,7 @@ WORKLOADS = {
     "dense_mtp4_fp8": "dense MTP4 verify, FP8 KV, per-token scales: B32 Hq16/Hkv1 D128 QL4 page128 L~U[16K,32K]",
     "dense_mtp4_bf16": "dense MTP4 verify, BF16 KV: B32 Hq16/Hkv1 D128 QL4 page128 L~U[16K,32K]",
     "long_d256": "long-context D256: B4 Hkv2 GQA8 QL4 page64 L=131072 window 8193, transposed V, per-tensor",
+    "long_d256_nowindow": "supplementary: the long-context D256 batch with the window off (all 131072 tokens visible)",
     "ragged": "ragged batch: B128 Hkv4 GQA4 D128 QL1 page16 log-uniform L, window 257, sinks, per-token",
     "sparse": "sparse decode: 64 rows Hq16/Hkv1 D128 page16, 2048 of 65536 slots, per-token, 4 partitions",
     "tiny": "tiny decode: B2 Hq8/Hkv1 D128 QL1 page16 L=37,100, per-tensor, one partition",
@@ -82,6 +83,8 @@ def make_inputs(workload: str):
         return W.config_tiny(), dict(max_partitions=1)
     if workload == "long_d256":
         return W.config_long_d256(), {}
+    if workload == "long_d256_nowindow":
+        return W.config_long_d256(window=0), {}
     if workload == "ragged":
         return W.config_ragged(), {}
     if workload == "dense_mtp4_bf16":
