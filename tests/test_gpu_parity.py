@@ -269,3 +269,48 @@ def test_stream_kernel_device_context_longer_than_plan(page):
     announce(f"stream kernel, plan lengths below device lengths page={page}")
     got, _ = run(inp, lens_for_plan=[1000, 300, 1], cu_count=16)
     compare(got, O.attend(inp), "stream kernel, longer device context")
+
+
+@pytest.mark.parametrize("kind", ["stream", "tile"])
+def test_graph_replay_with_changing_lengths(kind):
+    """One pa_decode + pa_reduce captured in a HIP graph and replayed while the
+    device context lengths change between replays (growing past the planned
+    lengths, and shrinking): every replay against the oracle and against an
+    eager call with the same lengths (bit-identical).  Works because the
+    plan's last partition of every row is open-ended and nothing in a call
+    allocates, uploads or clears memory once the metadata is on the device."""
+    import dataclasses
+
+    if kind == "stream":
+        cfg = dict(query_len=4, num_q_heads=16, page_size=128)
+    else:
+        cfg = dict(query_len=1, num_q_heads=8, page_size=16)
+    lens_max = [6000, 2500, 900]
+    inp = W.make_dense_case(90 + len(kind), lens_max, num_kv_heads=1, head_dim=128, scale_mode="token",
+                            sliding_window=0, fill="context", **cfg)
+    dev = to_device(inp)
+    planned = [3000, 1000, 500]
+    plan = B.Plan(B.problem_of(inp.problem), planned, cu_count=64).allocate("cuda")
+    cl = dev["context_lens"]
+    out = torch.empty_like(dev["q"])
+    args = (dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], cl, dev["k_scale"], dev["v_scale"], None)
+    cl.copy_(torch.tensor(planned, dtype=torch.int32))
+    B.attend(plan, out, *args)  # first call: uploads the plan metadata
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.attend(plan, out, *args)
+    torch.cuda.synchronize()
+    for lens in ([3000, 1000, 500], [6000, 2500, 900], [4100, 1, 0], [5000, 2000, 700]):
+        announce(f"graph replay {kind} lens={lens}")
+        cl.copy_(torch.tensor(lens, dtype=torch.int32))
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy()
+        ref = O.attend(dataclasses.replace(inp, context_lens=torch.tensor(lens, dtype=torch.int32)))
+        compare(got, ref, f"graph replay {lens}")
+        eager = torch.full_like(out, float("nan"))
+        B.attend(plan, eager, *args)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, eager.float().cpu().numpy())
