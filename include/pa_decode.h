@@ -80,6 +80,10 @@ typedef struct {
   int32_t max_partitions;   /* per (sequence, KV head); 0: cu_count, capped at 256 */
   int32_t partition_tokens; /* > 0: fixed partition length (rounded up to 128 tokens) */
   int32_t stage_limit;      /* page/slot ids staged in LDS per work item; 0: 1024 (max) */
+  int32_t refreshable;      /* 1: a fixed budget of work items and partial slots (cu_count x resident
+                               workgroups, at least one per (sequence, KV head, row group)) and one reduce
+                               entry per such unit, so that pa_plan_refresh can re-partition the plan on
+                               the device from device context lengths (e.g. between HIP graph replays) */
 } pa_plan_opts;
 
 typedef struct pa_plan_s pa_plan_t;
@@ -146,6 +150,24 @@ pa_status pa_decode(const pa_plan_t* plan, void* out, const void* q, const void*
  */
 pa_status pa_reduce(const pa_plan_t* plan, void* out, const float* sinks, void* meta_dev, void* workspace_dev,
                     void* stream);
+
+/*
+ * Re-partition a refreshable plan on the device from the device context
+ * lengths (one single-workgroup launch on `stream`, no host synchronisation,
+ * no allocation, no host-to-device copy: it can be captured in a HIP graph
+ * in front of pa_decode and pa_reduce).  Partition counts follow the host
+ * planner's rule (the CU-count budget of aiter PR #4332, "Add paged-attention
+ * Tile kernel", work plans): the smallest longest-item length M whose
+ * partitions (ceil(tiles / M) per (sequence, KV head, row group), at most
+ * max_partitions and at most one per tile) fit the plan's item and slot
+ * budget, with each unit's tiles split evenly.  The work list and reduce
+ * table in meta_dev are rewritten in full (unused items do nothing); the
+ * plan's host copy is not changed, and later pa_decode calls with this
+ * meta_dev use the refreshed list.  Must precede pa_decode on the same
+ * stream.  Errors: PA_ERR_INVALID for a NULL pointer or a plan made without
+ * `refreshable`, PA_ERR_DEVICE for a launch error.
+ */
+pa_status pa_plan_refresh(const pa_plan_t* plan, const int32_t* context_lens, void* meta_dev, void* stream);
 
 /* Thread-local message for the last non-OK status of this thread. */
 const char* pa_last_error(void);

@@ -24,7 +24,7 @@ PA_V_PLAIN, PA_V_TRANSPOSED = range(2)
 PA_SCALE_NONE, PA_SCALE_PER_TENSOR, PA_SCALE_PER_TOKEN = range(3)
 
 EXPORTS = ["pa_plan", "pa_plan_sizes", "pa_plan_info", "pa_plan_work", "pa_plan_free", "pa_decode", "pa_reduce",
-           "pa_last_error"]
+           "pa_plan_refresh", "pa_last_error"]
 
 
 class PaProblem(ctypes.Structure):
@@ -35,7 +35,8 @@ class PaProblem(ctypes.Structure):
 
 
 class PaPlanOpts(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("cu_count", "max_partitions", "partition_tokens", "stage_limit")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("cu_count", "max_partitions", "partition_tokens", "stage_limit",
+                                              "refreshable")]
 
 
 class PaPlanInfo(ctypes.Structure):
@@ -70,6 +71,8 @@ def load_library(path: str = LIB_PATH):
     L.pa_decode.argtypes = [vp] * 13
     L.pa_reduce.restype = ctypes.c_int
     L.pa_reduce.argtypes = [vp] * 6
+    L.pa_plan_refresh.restype = ctypes.c_int
+    L.pa_plan_refresh.argtypes = [vp] * 4
     L.pa_last_error.restype = ctypes.c_char_p
     L.pa_last_error.argtypes = []
     _lib = L
@@ -108,12 +111,12 @@ class Plan:
     """Owns a pa_plan_t plus the device metadata and workspace it needs."""
 
     def __init__(self, problem: PaProblem, context_lens_host, cu_count=0, max_partitions=0, partition_tokens=0,
-                 stage_limit=0):
+                 stage_limit=0, refreshable=0):
         L = load_library()
         self.problem = problem
         lens = torch.as_tensor(context_lens_host, dtype=torch.int32).contiguous().cpu()
         self._lens = lens
-        opts = PaPlanOpts(cu_count, max_partitions, partition_tokens, stage_limit)
+        opts = PaPlanOpts(cu_count, max_partitions, partition_tokens, stage_limit, refreshable)
         h = ctypes.c_void_p()
         _check(L.pa_plan(ctypes.byref(problem), lens.data_ptr() if lens.numel() else None, ctypes.byref(opts),
                          ctypes.byref(h)))
@@ -186,6 +189,15 @@ def pa_decode(plan: Plan, out, q, k_cache, v_cache, block_tables, context_lens, 
 def pa_reduce(plan: Plan, out, sinks=None, stream=None):
     _check(load_library().pa_reduce(plan.handle, _ptr(out), _ptr(sinks), _ptr(plan.meta), _ptr(plan.workspace),
                                     _stream_ptr(stream)))
+
+
+def pa_plan_refresh(plan: Plan, context_lens, stream=None):
+    """Re-partition a refreshable plan on the device from device lengths."""
+    if not context_lens.is_cuda or context_lens.dtype != torch.int32:
+        raise ValueError("context_lens must be an int32 device tensor")
+    if plan.meta is None:
+        plan.allocate(context_lens.device)
+    _check(load_library().pa_plan_refresh(plan.handle, _ptr(context_lens), _ptr(plan.meta), _stream_ptr(stream)))
 
 
 def attend(plan: Plan, out, q, k_cache, v_cache, block_tables, context_lens, k_scale=None, v_scale=None, sinks=None,

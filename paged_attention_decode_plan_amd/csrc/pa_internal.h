@@ -19,13 +19,15 @@ constexpr int kMaxPartitions = 256; // static per-(sequence, KV head) bound
 struct WorkItem {
   int32_t seq, kvh, rg;           // sequence, KV head, row group
   int32_t tile_begin, tile_end;   // tiles relative to the page-aligned span start; -1: to the end
+  // (seq -1: an unused item of a refreshable plan, which does nothing)
   int32_t slot;                   // partial slot; -1: direct output
   int32_t part, nparts;
 };
 static_assert(sizeof(WorkItem) == 32, "work item is 32 bytes");
 
 // One multi-partition (sequence, KV head, row group): its partials occupy
-// slots [first_slot, first_slot + nparts) in partition order.
+// slots [first_slot, first_slot + nparts) in partition order.  nparts < 2:
+// nothing to merge (refreshable plans keep one entry per unit).
 struct ReduceItem {
   int32_t seq, kvh, rg, first_slot, nparts, pad0, pad1, pad2;
 };
@@ -44,6 +46,8 @@ struct Plan {
   int max_parts = 0;
   int total_tiles = 0;
   float scale_log2 = 0.f;  // softmax_scale * log2(e)
+  int maxp = 0;            // partition cap per unit (refreshable plans)
+  int budget_items = 0;    // fixed item count of a refreshable plan (0: not refreshable)
   std::vector<WorkItem> items;
   std::vector<ReduceItem> reduce;
   int num_slots = 0;

@@ -128,6 +128,7 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   const int wt = w / R::WR;  // this wave's token group
 
   const WorkItem it = a.items[blockIdx.x];
+  if (it.seq < 0) return;  // an unused item of a refreshable plan
   const int s = it.seq, kvh = it.kvh, rg = it.rg;
   const int ps = a.page_size;
   const int ps_log2 = 31 - __builtin_clz(ps);
@@ -1003,6 +1004,7 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(ReduceArgs a) {
   __shared__ float wgt[RR][kMaxPartitions];
   __shared__ float rowf[RR];
   const ReduceItem e = a.entries[blockIdx.x / a.chunks_per_entry];
+  if (e.nparts < 2) return;  // a unit with one partition wrote its rows itself
   const int chunk = blockIdx.x % a.chunks_per_entry;
   const int rpg = a.rows_per_group;
   const int row0 = e.rg * kMaxRowsPerItem;
@@ -1115,6 +1117,127 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(ReduceArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Device-side re-partition of a refreshable plan (one workgroup).  The rule
+// is the host planner's: per unit (sequence, KV head, row group) of T
+// visible 128-token tiles, p = ceil(T / M) partitions (at most maxp and T;
+// one for an empty unit, which clears its rows), M the smallest length whose
+// partitions fit the item and slot budget; each unit's tiles are split
+// evenly, the first T % p partitions taking one extra tile.
+// ---------------------------------------------------------------------------
+struct RefreshArgs {
+  const int32_t* context_lens;
+  WorkItem* items;
+  ReduceItem* reduce;
+  int num_seqs, QL, window, causal, page_size, table_stride, token_table, Hkv, row_groups;
+  int maxp, n_items, n_slots;
+};
+
+constexpr int REF_T = 1024;  // threads of the refresh workgroup
+
+__device__ int refresh_tiles(const RefreshArgs& a, int s) {
+  const long cap = a.token_table ? (long)a.table_stride : (long)a.table_stride * a.page_size;
+  const long L = min(max((long)a.context_lens[s], 0L), cap);
+  long lo = 0;
+  if (!a.token_table && L > 0 && a.window > 0) {
+    const long first_pos = a.causal ? L - a.QL : L - 1;
+    lo = max(0L, first_pos - a.window + 1);
+  }
+  const long t0 = a.token_table ? 0 : (lo / a.page_size) * a.page_size;
+  return L > lo ? (int)((L - t0 + kTileTokens - 1) / kTileTokens) : 0;
+}
+
+__device__ __forceinline__ int refresh_parts(int T, int M, int maxp) {
+  return T == 0 ? 1 : min(min((T + M - 1) / M, maxp), T);
+}
+
+// block-wide sum of one long per thread
+__device__ long refresh_sum(long v, long* red) {
+  const int tid = threadIdx.x;
+  red[tid] = v;
+  __syncthreads();
+  for (int o = REF_T / 2; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  const long r = red[0];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(REF_T) void pa_refresh_kernel(RefreshArgs a) {
+  __shared__ long red[REF_T];
+  __shared__ long scan_i[REF_T], scan_s[REF_T];
+  const int tid = threadIdx.x;
+  const int U = a.Hkv * a.row_groups;
+  // longest unit
+  int tmax = 0;
+  for (int s = tid; s < a.num_seqs; s += REF_T) tmax = max(tmax, refresh_tiles(a, s));
+  red[tid] = tmax;
+  __syncthreads();
+  for (int o = REF_T / 2; o > 0; o >>= 1) {
+    if (tid < o) red[tid] = max(red[tid], red[tid + o]);
+    __syncthreads();
+  }
+  tmax = (int)red[0];
+  __syncthreads();
+  // smallest feasible M in [1, max(tmax, 1)] (M = tmax gives one partition per unit)
+  int lo = 1, hi = max(tmax, 1);
+  while (lo < hi) {
+    const int mid = lo + (hi - lo) / 2;
+    long ni = 0, ns = 0;
+    for (int s = tid; s < a.num_seqs; s += REF_T) {
+      const int p = refresh_parts(refresh_tiles(a, s), mid, a.maxp);
+      ni += p;
+      ns += p > 1 ? p : 0;
+    }
+    ni = refresh_sum(ni, red) * U;
+    ns = refresh_sum(ns, red) * U;
+    if (ni <= a.n_items && ns <= a.n_slots)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  const int M = lo;
+  // emit, REF_T sequences at a time: exclusive scans of items and slots
+  long item_base = 0, slot_base = 0;
+  for (int c0 = 0; c0 < a.num_seqs; c0 += REF_T) {
+    const int s = c0 + tid;
+    const int T = s < a.num_seqs ? refresh_tiles(a, s) : 0;
+    const int p = s < a.num_seqs ? refresh_parts(T, M, a.maxp) : 0;
+    scan_i[tid] = (long)p * U;
+    scan_s[tid] = p > 1 ? (long)p * U : 0;
+    __syncthreads();
+    for (int o = 1; o < REF_T; o <<= 1) {  // inclusive Hillis-Steele scans
+      const long vi = tid >= o ? scan_i[tid - o] : 0, vs = tid >= o ? scan_s[tid - o] : 0;
+      __syncthreads();
+      scan_i[tid] += vi;
+      scan_s[tid] += vs;
+      __syncthreads();
+    }
+    const long ib = item_base + scan_i[tid] - (long)p * U, sb = slot_base + scan_s[tid] - (p > 1 ? (long)p * U : 0);
+    if (s < a.num_seqs) {
+      for (int g = 0; g < a.Hkv; ++g)
+        for (int rg = 0; rg < a.row_groups; ++rg) {
+          const int u = g * a.row_groups + rg;
+          const long first = sb + (long)u * p;
+          a.reduce[(long)s * U + u] = ReduceItem{s, g, rg, p > 1 ? (int)first : 0, p > 1 ? p : 0, 0, 0, 0};
+          const int base = T / p, extra = T % p;
+          for (int part = 0; part < p; ++part) {
+            const int b = part * base + min(part, extra);
+            const int e = b + base + (part < extra ? 1 : 0);
+            a.items[ib + (long)u * p + part] =
+                WorkItem{s, g, rg, b, part == p - 1 ? -1 : e, p > 1 ? (int)(first + part) : -1, part, p};
+          }
+        }
+    }
+    item_base += scan_i[REF_T - 1];
+    slot_base += scan_s[REF_T - 1];
+    __syncthreads();
+  }
+  for (long i = item_base + tid; i < a.n_items; i += REF_T) a.items[i] = WorkItem{-1, 0, 0, 0, 0, -1, 0, 1};
+}
+
+// ---------------------------------------------------------------------------
 // Launch selection
 // ---------------------------------------------------------------------------
 template <int D, bool FP8, int NRT, bool SPARSE>
@@ -1221,6 +1344,36 @@ extern "C" pa_status pa_decode(const pa_plan_t* plan, void* out, const void* q, 
     return launch_nrt<256, true>(P.nrt, sparse, args, n, st);
   }
   return launch_nrt<128, false>(P.nrt, sparse, args, n, st);
+}
+
+extern "C" pa_status pa_plan_refresh(const pa_plan_t* plan, const int32_t* context_lens, void* meta_dev,
+                                     void* stream) {
+  if (!plan) return set_error(PA_ERR_INVALID, "plan is NULL");
+  const Plan& P = plan->plan;
+  if (P.budget_items <= 0) return set_error(PA_ERR_INVALID, "the plan was made without refreshable");
+  if (!meta_dev || (P.prob.num_seqs > 0 && !context_lens))
+    return set_error(PA_ERR_INVALID, "meta_dev or context_lens is NULL");
+  RefreshArgs ra;
+  ra.context_lens = context_lens;
+  ra.items = (WorkItem*)meta_dev;
+  ra.reduce = (ReduceItem*)((uint8_t*)meta_dev + P.items.size() * sizeof(WorkItem));
+  ra.num_seqs = P.prob.num_seqs;
+  ra.QL = P.prob.query_len;
+  ra.window = P.prob.sliding_window;
+  ra.causal = P.prob.causal;
+  ra.page_size = P.prob.page_size;
+  ra.table_stride = P.prob.table_stride;
+  ra.token_table = P.prob.token_table;
+  ra.Hkv = P.prob.num_kv_heads;
+  ra.row_groups = P.row_groups;
+  ra.maxp = P.maxp;
+  ra.n_items = (int)P.items.size();
+  ra.n_slots = P.num_slots;
+  hipLaunchKernelGGL(pa_refresh_kernel, dim3(1), dim3(REF_T), 0, (hipStream_t)stream, ra);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return set_error(PA_ERR_DEVICE, std::string("refresh launch failed: ") + hipGetErrorString(err));
+  P.uploaded_to = meta_dev;  // the device list is now the one to use
+  return PA_OK;
 }
 
 extern "C" pa_status pa_reduce(const pa_plan_t* plan, void* out, const float* sinks, void* meta_dev,

@@ -90,6 +90,7 @@ extern "C" pa_status pa_plan(const pa_problem* problem, const int32_t* context_l
   if (opts) o = *opts;
   if (o.cu_count < 0 || o.max_partitions < 0 || o.partition_tokens < 0 || o.stage_limit < 0)
     return set_error(PA_ERR_INVALID, "plan options must be >= 0");
+  if (o.refreshable & ~1) return set_error(PA_ERR_INVALID, "refreshable must be 0 or 1");
   const pa_problem& p = *problem;
 
   int cu = o.cu_count;
@@ -196,6 +197,8 @@ extern "C" pa_status pa_plan(const pa_problem* problem, const int32_t* context_l
         if (np > 1) {
           P.reduce.push_back(ReduceItem{s, g, rg, slot, np, 0, 0, 0});
           slot += np;
+        } else if (o.refreshable) {
+          P.reduce.push_back(ReduceItem{s, g, rg, 0, 0, 0, 0, 0});  // one entry per unit: nothing to merge
         }
         for (int part = 0; part < np; ++part) {
           // balanced split: the first (nt % np) parts get one extra tile
@@ -217,6 +220,15 @@ extern "C" pa_status pa_plan(const pa_problem* problem, const int32_t* context_l
     };
     return len(a) > len(b);
   });
+  if (o.refreshable) {
+    // A fixed budget that pa_plan_refresh re-partitions on the device: items
+    // past the used ones do nothing (seq -1), and each item owns at most
+    // one partial slot.
+    P.maxp = maxp;
+    P.budget_items = (int)std::max<long>(slots_budget, (long)P.items.size());
+    P.items.resize(P.budget_items, WorkItem{-1, 0, 0, 0, 0, -1, 0, 1});
+    P.num_slots = std::max(P.num_slots, P.budget_items);
+  }
   P.meta_host.resize(P.items.size() * sizeof(WorkItem) + P.reduce.size() * sizeof(ReduceItem));
   if (!P.items.empty()) std::memcpy(P.meta_host.data(), P.items.data(), P.items.size() * sizeof(WorkItem));
   if (!P.reduce.empty())

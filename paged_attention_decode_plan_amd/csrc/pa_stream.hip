@@ -98,6 +98,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   const int h = lane >> 5;
 
   const WorkItem it = a.items[blockIdx.x];
+  if (it.seq < 0) return;  // an unused item of a refreshable plan
   const int s = it.seq, kvh = it.kvh, rg = it.rg;
   const int ps = a.page_size;
   const int ps_log2 = 31 - __builtin_clz(ps);

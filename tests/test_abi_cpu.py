@@ -171,3 +171,23 @@ def test_plan_zero_sequences():
     prob = _prob(num_seqs=0)
     plan = B.Plan(prob, [], cu_count=8)
     assert plan.info().num_items == 0 and plan.meta_bytes == 0
+
+
+def test_refreshable_plan_layout():
+    """A refreshable plan: a fixed item budget (cu_count x resident
+    workgroups) padded with unused items (seq -1), one reduce entry per
+    (sequence, KV head, row group), at least one partial slot per item; a
+    plan made without the option refuses pa_plan_refresh."""
+    lens = [5000, 0, 1, 700]
+    prob = B.make_problem(4, 4, 16, 1, 128, 128, 64, 16, "bf16", "fp8", False, "token", 1, 0, 0, 0, 0.0)
+    plan = B.Plan(prob, lens, cu_count=32, refreshable=1)
+    info = plan.info()
+    work = plan.work().numpy()
+    assert info.num_items == 32 and work.shape[0] == 32
+    used = work[:, 0] >= 0
+    assert used.sum() >= 4 and (work[~used, 0] == -1).all()
+    assert info.num_reduce == 4  # one entry per unit (Hkv 1, one row group)
+    assert info.num_slots >= info.num_items
+    plain = B.Plan(prob, lens, cu_count=32)
+    with pytest.raises(ValueError):
+        B._check(B.load_library().pa_plan_refresh(plain.handle, None, None, None))

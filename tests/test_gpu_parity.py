@@ -314,3 +314,91 @@ def test_graph_replay_with_changing_lengths(kind):
         B.attend(plan, eager, *args)
         torch.cuda.synchronize()
         assert np.array_equal(got, eager.float().cpu().numpy())
+
+
+def _check_device_work_list(plan, inp, lens, host_max_len):
+    """Structure of a device-refreshed work list: every unit's visible tiles
+    covered once, in partition order, by an even split; unused items do
+    nothing; partial slots distinct and inside the budget; the longest item
+    no longer than the host planner's for the same lengths."""
+    p = inp.problem
+    n = plan.info().num_items
+    items = plan.meta[: n * 32].view(torch.int32).view(n, 8).cpu().numpy()
+    used = items[items[:, 0] >= 0]
+    slots = used[used[:, 5] >= 0, 5]
+    assert len(set(slots.tolist())) == len(slots) and (slots < plan.info().num_slots).all()
+    longest = 0
+    for s in range(p.num_seqs):
+        lo, hi = W.visible_span(int(lens[s]), p.query_len, p.sliding_window, p.causal)
+        t0 = (lo // p.page_size) * p.page_size
+        T = -(-(hi - t0) // 128) if hi > lo else 0
+        mine = used[used[:, 0] == s]
+        assert len(mine) >= 1
+        parts = mine[:, 7]
+        assert (parts == parts[0]).all() and len(mine) == parts[0] * p.num_kv_heads
+        mine = mine[np.argsort(mine[:, 6], kind="stable")]
+        ends = [e if e >= 0 else T for e in mine[:, 4]]
+        assert mine[0, 3] == 0 and ends[-1] == T and mine[-1, 4] == -1
+        assert all(mine[i + 1, 3] == ends[i] for i in range(len(mine) - 1))
+        lengths = [e - b for b, e in zip(mine[:, 3], ends)]
+        assert max(lengths) - min(lengths) <= 1
+        longest = max(longest, max(lengths))
+    assert longest <= host_max_len
+
+
+@pytest.mark.parametrize("kind", ["stream", "tile"])
+def test_device_refresh_in_graph(kind):
+    """Row f2: pa_plan_refresh re-partitions a refreshable plan on the device
+    from the device lengths; a graph of refresh + decode + reduce is replayed
+    as the lengths change, every replay against the oracle and an eager call,
+    and the refreshed work list is checked structurally."""
+    import dataclasses
+
+    if kind == "stream":
+        cfg = dict(query_len=4, num_q_heads=16, page_size=128)
+    else:
+        cfg = dict(query_len=1, num_q_heads=8, page_size=16)
+    lens_max = [6000, 2500, 900, 40]
+    inp = W.make_dense_case(95 + len(kind), lens_max, num_kv_heads=1, head_dim=128, scale_mode="token",
+                            sliding_window=0, has_sinks=True, fill="context", **cfg)
+    dev = to_device(inp)
+    planned = [3000, 1000, 500, 40]
+    plan = B.Plan(B.problem_of(inp.problem), planned, cu_count=64, refreshable=1).allocate("cuda")
+    cl = dev["context_lens"]
+    out = torch.empty_like(dev["q"])
+    args = (dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], cl, dev["k_scale"], dev["v_scale"],
+            dev["sinks"])
+    cl.copy_(torch.tensor(planned, dtype=torch.int32))
+    B.pa_plan_refresh(plan, cl)
+    B.attend(plan, out, *args)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.pa_plan_refresh(plan, cl)
+        B.attend(plan, out, *args)
+    torch.cuda.synchronize()
+    for lens in ([6000, 2500, 900, 40], [3000, 1, 0, 17], [5900, 2400, 100, 40], [200, 2500, 900, 0]):
+        announce(f"device refresh {kind} lens={lens}")
+        cl.copy_(torch.tensor(lens, dtype=torch.int32))
+        out.fill_(float("nan"))
+        plan.workspace.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy()
+        ref = O.attend(dataclasses.replace(inp, context_lens=torch.tensor(lens, dtype=torch.int32)))
+        compare(got, ref, f"device refresh {lens}")
+        host = B.Plan(B.problem_of(inp.problem), lens, cu_count=64)
+        hw = host.work().numpy()
+        host_len = 0
+        for row in hw:
+            s_ = int(row[0])
+            lo, hi = W.visible_span(lens[s_], inp.problem.query_len, 0, True)
+            t0 = (lo // inp.problem.page_size) * inp.problem.page_size
+            T = -(-(hi - t0) // 128) if hi > lo else 0
+            host_len = max(host_len, (row[4] if row[4] >= 0 else T) - row[3])
+        _check_device_work_list(plan, inp, lens, host_len)
+        eager = torch.full_like(out, float("nan"))
+        B.pa_plan_refresh(plan, cl)
+        B.attend(plan, eager, *args)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, eager.float().cpu().numpy())
