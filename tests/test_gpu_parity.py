@@ -402,3 +402,16 @@ def test_device_refresh_in_graph(kind):
         B.attend(plan, eager, *args)
         torch.cuda.synchronize()
         assert np.array_equal(got, eager.float().cpu().numpy())
+
+
+@pytest.mark.parametrize("kv,hq,hkv,d,page", [("fp8", 16, 1, 128, 128), ("fp8", 16, 2, 256, 64),
+                                              ("bf16", 8, 1, 128, 16)])
+def test_non_causal_multi_token(kv, hq, hkv, d, page):
+    """Multi-token rows without the causal mask (row f3): the streaming kernel
+    (64 rows), the D256 and the BF16 tile kernels, with and without a window."""
+    for ql, window in [(2, 0), (4, 0), (4, 33)]:
+        inp = W.make_dense_case(110 + ql + window + d, LENS, query_len=ql, num_q_heads=hq, num_kv_heads=hkv,
+                                head_dim=d, page_size=page, kv_dtype=kv, scale_mode="token" if kv == "fp8" else "none",
+                                sliding_window=window, causal=False)
+        announce(f"non-causal kv={kv} d={d} page={page} ql={ql} w={window}")
+        _parity(inp, cu_count=64)

@@ -251,3 +251,20 @@ def test_planted_token_digits():
     out = O.attend(inp)
     page = int(inp.block_tables[0, target // 16])
     np.testing.assert_array_equal(out[0, 0], np.array([(page + d) % 16 for d in range(16)], np.float32))
+
+
+@pytest.mark.parametrize("page", [16, 64])
+def test_oracle_vs_bruteforce_non_causal(page):
+    """Multi-token rows without the causal mask (every row at position L - 1)."""
+    for ql, w in itertools.product([2, 4], [0, 1, 17]):
+        inp = W.make_dense_case(700 + 13 * ql + w + page, LENS, query_len=ql, num_q_heads=4, num_kv_heads=2,
+                                head_dim=32, page_size=page, scale_mode="token", sliding_window=w, causal=False,
+                                poison=False, fill="context")
+        got = O.attend(inp, nthreads=2).astype(np.float64)
+        np.testing.assert_allclose(got, bruteforce.attend(inp), rtol=1e-6, atol=1e-7, err_msg=f"ql={ql} w={w}")
+        # all rows of one (sequence, head) see the same tokens: equal queries give equal outputs
+        p = inp.problem
+        q = inp.q.view(p.num_seqs, ql, p.num_q_heads, p.head_dim)
+        q[:, 1:] = q[:, :1]
+        out = O.attend(inp, nthreads=2).reshape(p.num_seqs, ql, p.num_q_heads, p.head_dim)
+        np.testing.assert_array_equal(out[:, 1:], np.broadcast_to(out[:, :1], out[:, 1:].shape))
