@@ -63,6 +63,10 @@ struct StreamSmem {
   static constexpr int SCALES = SW * 64 * 4;  // per wave: 32 k scales, 32 v scales of its step
   static constexpr int STATS = (SW * ROWS * 2 + SW + ROWS * 4) * 4;
   static constexpr int TOTAL = MERGE + IDS + SCALES + STATS;
+  // Requested at launch: more than half of a CU's 160 KB, so that the
+  // dispatcher places one workgroup per CU (the plan's budget) also for one
+  // row block, whose own footprint would let two share a CU.
+  static constexpr int LAUNCH = TOTAL > 81 * 1024 ? TOTAL : 81 * 1024;
 };
 
 // Step data of one wave, loaded two steps ahead.
@@ -563,11 +567,14 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       l_acc[rb] += ls;
       // a PV operand p * (normalised V scale) of 2^15 or more shows in the
       // lane's sum times the largest normalised V scale; a reference raised
-      // by log2 of that product brings every operand to at most 1
+      // by log2 of that product brings every operand to at most 1.  A sum
+      // that overflowed to infinity raises it by 127 (a finite reference:
+      // the restart's masked steps then find the exact maximum if it is
+      // still too low).
       const float bnd = ls * vsmax;
       const bool big = bnd > 0x1p15f;
       ovf |= big;
-      m_hi[rb] = big ? fmaxf(m_hi[rb], m_ref[rb] + __builtin_amdgcn_logf(bnd)) : m_hi[rb];
+      m_hi[rb] = big ? fmaxf(m_hi[rb], m_ref[rb] + __builtin_amdgcn_logf(fminf(bnd, 0x1p127f))) : m_hi[rb];
       if constexpr (PT) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) y[i] *= vs16[i];
@@ -589,13 +596,14 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     };
 
     // Schedule (one wave per SIMD, so the overlap has to come from within
-    // the wave): QK of row block 0 with the V conversion; QK of row block 1
-    // with the probabilities of block 0; PV of block 0 with the
-    // probabilities of block 1; PV of block 1 with the next step's scales.
-    // V is reloaded (three steps ahead) once converted, K once both row
-    // blocks' QK MFMAs have read it.
-    static_assert(RB == 2, "the schedule below is written for two row blocks");
-    half8 p0[2], p1[2];
+    // the wave).  Two row blocks: QK of row block 0 with the V conversion;
+    // QK of row block 1 with the probabilities of block 0; PV of block 0
+    // with the probabilities of block 1; PV of block 1 with the next step's
+    // scales.  One row block: QK with the V conversion, the probabilities on
+    // their own, PV with the next step's scales.  V is reloaded (three steps
+    // ahead) once converted, K once every row block's QK MFMAs have read it.
+    static_assert(RB == 1 || RB == 2, "one or two row blocks");
+    half8 p0[2];
     const f32x16 s0 = qk(0);
     vcvt();
 #pragma unroll
@@ -605,25 +613,34 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
     load_v(cur, kn, nid, std::false_type{});  // this step's V is converted
-    const f32x16 s1 = qk(1);
-    scales();
-    probs(0, s0, p0);
+    if constexpr (RB == 2) {
+      half8 p1[2];
+      const f32x16 s1 = qk(1);
+      scales();
+      probs(0, s0, p0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // MFMA (FP8, 16 passes)
-      __builtin_amdgcn_sched_group_barrier(0x002, 16, 1);  // VALU
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    load_k(cur, kn, nid, std::false_type{});  // both row blocks' QK have read this step's K
-    pv(0, p0);
-    probs(1, s1, p1);
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // MFMA (FP8, 16 passes)
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 1);  // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      load_k(cur, kn, nid, std::false_type{});  // both row blocks' QK have read this step's K
+      pv(0, p0);
+      probs(1, s1, p1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 2);  // VALU
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 2);  // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      pv(1, p1);
+    } else {
+      load_k(cur, kn, nid, std::false_type{});  // the QK MFMAs have read this step's K
+      scales();
+      probs(0, s0, p0);
+      __builtin_amdgcn_sched_barrier(0);
+      pv(0, p0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    pv(1, p1);
     prep(nxt, k + 1);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -820,7 +837,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
 
 template <int RB, bool PT, bool BIG>
 static pa_status launch_stream_t(const KernelArgs& args, int nblocks, hipStream_t stream) {
-  constexpr int bytes = StreamSmem<RB>::TOTAL;
+  constexpr int bytes = StreamSmem<RB>::LAUNCH;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   static bool configured = false;
   if (!configured) {
@@ -839,15 +856,21 @@ static pa_status launch_stream_t(const KernelArgs& args, int nblocks, hipStream_
 
 bool stream_kernel_applies(const Plan& P) {
   const pa_problem& p = P.prob;
-  return p.kv_dtype == PA_FP8_E4M3FN && p.head_dim == 128 && !p.token_table && P.rows_per_group > 32 &&
+  return p.kv_dtype == PA_FP8_E4M3FN && p.head_dim == 128 && !p.token_table && P.rows_per_group > 16 &&
          p.num_pages > 0;
 }
 
-pa_status launch_stream(const Plan& P, const KernelArgs& args, int nblocks, hipStream_t stream) {
+template <int RB>
+static pa_status launch_stream_rb(const Plan& P, const KernelArgs& args, int nblocks, hipStream_t stream) {
   const bool pt = P.prob.scale_mode == PA_SCALE_PER_TOKEN;
   if (P.prob.page_size >= 32)
-    return pt ? launch_stream_t<2, true, true>(args, nblocks, stream) : launch_stream_t<2, false, true>(args, nblocks, stream);
-  return pt ? launch_stream_t<2, true, false>(args, nblocks, stream) : launch_stream_t<2, false, false>(args, nblocks, stream);
+    return pt ? launch_stream_t<RB, true, true>(args, nblocks, stream) : launch_stream_t<RB, false, true>(args, nblocks, stream);
+  return pt ? launch_stream_t<RB, true, false>(args, nblocks, stream) : launch_stream_t<RB, false, false>(args, nblocks, stream);
+}
+
+pa_status launch_stream(const Plan& P, const KernelArgs& args, int nblocks, hipStream_t stream) {
+  return P.rows_per_group > 32 ? launch_stream_rb<2>(P, args, nblocks, stream)
+                               : launch_stream_rb<1>(P, args, nblocks, stream);
 }
 
 }  // namespace pa

@@ -129,9 +129,11 @@ def test_run_to_run_bit_exact():
 def test_planted_token_digits_exact():
     """One token's key dominates; the output must equal its integer V digits
     exactly, wherever the token sits (page / tile / partition / staged-bound /
-    window edges)."""
+    window edges).  4, 16, 32 and 64 rows: the tile kernel and both row-block
+    counts of the streaming kernel, where a token after the first step of a
+    wave exceeds its reference by 522 (base 2) and forces a restart."""
     page, L = 16, 700
-    for ql, window, target_off in [(1, 0, None), (4, 0, None), (1, 33, None)]:
+    for ql, window, target_off in [(1, 0, None), (4, 0, None), (1, 33, None), (8, 0, None), (16, 0, None)]:
         base = W.make_dense_case(45, [L], query_len=ql, num_q_heads=4, num_kv_heads=1, head_dim=128, page_size=page,
                                  scale_mode="tensor", sliding_window=window, poison=True, fill="context")
         p = base.problem
@@ -184,8 +186,9 @@ def test_uniform_attention_census():
 
 
 @pytest.mark.parametrize("page", [64, 128])
-def test_wide_scales_64_rows(page):
-    """64-row FP8 items: queries of magnitude 2^24 with per-token k scales
+@pytest.mark.parametrize("ql", [4, 2])
+def test_wide_scales_stream_rows(page, ql):
+    """FP8 items of 64 and 32 rows (the streaming kernel): queries of magnitude 2^24 with per-token k scales
     2^24 smaller (the whole-item power-of-two rescaling of the query, folded
     back into the logits), and V scales 2^30 larger (the clamped V exponent
     and its overflow restart), against the oracle.  The output is linear in
@@ -193,27 +196,30 @@ def test_wide_scales_64_rows(page):
     by 2^30: the absolute part of the tolerance keeps its meaning."""
     for name, qmul, kmul, vmul in [("q x 2^24, k scales x 2^-24", 2.0**24, 2.0**-24, 1.0),
                                    ("v scales x 2^30", 1.0, 1.0, 2.0**30)]:
-        inp = W.make_dense_case(48 + page, LENS, query_len=4, num_q_heads=16, num_kv_heads=1, head_dim=128,
+        inp = W.make_dense_case(48 + page + ql, LENS, query_len=ql, num_q_heads=16, num_kv_heads=1, head_dim=128,
                                 page_size=page, scale_mode="token")
         inp.q.mul_(qmul)
         real = inp.k_scale < 1e29  # poisoned slots keep their poison
         inp.k_scale[real] *= kmul
         real = inp.v_scale < 1e29
         inp.v_scale[real] *= vmul
-        announce(f"wide scales page={page}: {name}")
+        announce(f"wide scales page={page} rows={16 * ql}: {name}")
         got, _ = run(inp, cu_count=64)
         compare(got / vmul, O.attend(inp) / vmul, name)
 
 
-@pytest.mark.parametrize("page", [64, 128])
-def test_stream_kernel_run_to_run_bit_exact(page):
-    """64-row FP8 items (the streaming kernel, several partitions per
-    sequence, merged in partition order): against the oracle, and two calls
-    with one plan give identical bytes."""
-    inp = W.make_dense_case(60 + page, [5000, 3, 0, 1, 2600, 700], query_len=4, num_q_heads=16, num_kv_heads=1,
-                            head_dim=128, page_size=page, scale_mode="token", sliding_window=0, has_sinks=True)
+@pytest.mark.parametrize("page", [16, 64, 128])
+@pytest.mark.parametrize("ql,hq", [(4, 16), (3, 8)])
+def test_stream_kernel_run_to_run_bit_exact(page, ql, hq):
+    """FP8 items of 64 rows (the streaming kernel's two row blocks) and of 24
+    rows (one row block, 8 padding rows), several partitions per sequence
+    merged in partition order: against the oracle, and two calls with one
+    plan give identical bytes."""
+    inp = W.make_dense_case(60 + page + ql, [5000, 3, 0, 1, 2600, 700], query_len=ql, num_q_heads=hq,
+                            num_kv_heads=1, head_dim=128, page_size=page, scale_mode="token", sliding_window=0,
+                            has_sinks=True)
     dev = to_device(inp)
-    announce(f"stream kernel twice page={page}")
+    announce(f"stream kernel twice page={page} rows={ql * hq}")
     a, plan = run(inp, dev=dev, cu_count=64)
     assert plan.info().num_reduce > 0
     compare(a, O.attend(inp), "stream kernel")
@@ -260,13 +266,14 @@ def test_pages_past_4gib(ql, hq, page):
 
 
 @pytest.mark.parametrize("page", [64, 128])
-def test_stream_kernel_device_context_longer_than_plan(page):
-    """64-row FP8 items (the streaming kernel) with device lengths beyond the
-    planned ones: the open-ended last partition reads the page ids past the
-    staged range from the block table."""
-    inp = W.make_dense_case(80 + page, [9000, 2500, 300], query_len=4, num_q_heads=16, num_kv_heads=1,
+@pytest.mark.parametrize("ql", [4, 2])
+def test_stream_kernel_device_context_longer_than_plan(page, ql):
+    """FP8 items of 64 and 32 rows (the streaming kernel, two and one row
+    blocks) with device lengths beyond the planned ones: the open-ended last
+    partition reads the page ids past the staged range from the block table."""
+    inp = W.make_dense_case(80 + page + ql, [9000, 2500, 300], query_len=ql, num_q_heads=16, num_kv_heads=1,
                             head_dim=128, page_size=page, scale_mode="token", sliding_window=0)
-    announce(f"stream kernel, plan lengths below device lengths page={page}")
+    announce(f"stream kernel, plan lengths below device lengths page={page} rows={16 * ql}")
     got, _ = run(inp, lens_for_plan=[1000, 300, 1], cu_count=16)
     compare(got, O.attend(inp), "stream kernel, longer device context")
 
@@ -408,7 +415,7 @@ def test_device_refresh_in_graph(kind):
                                               ("bf16", 8, 1, 128, 16)])
 def test_non_causal_multi_token(kv, hq, hkv, d, page):
     """Multi-token rows without the causal mask (row f3): the streaming kernel
-    (64 rows), the D256 and the BF16 tile kernels, with and without a window."""
+    (32 and 64 rows), the D256 and the BF16 tile kernels, with and without a window."""
     for ql, window in [(2, 0), (4, 0), (4, 33)]:
         inp = W.make_dense_case(110 + ql + window + d, LENS, query_len=ql, num_q_heads=hq, num_kv_heads=hkv,
                                 head_dim=d, page_size=page, kv_dtype=kv, scale_mode="token" if kv == "fp8" else "none",
