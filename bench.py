@@ -38,6 +38,7 @@ PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
 WORKLOADS = {
     "dense_mtp4_fp8": "dense MTP4 verify, FP8 KV, per-token scales: B32 Hq16/Hkv1 D128 QL4 page128 L~U[16K,32K]",
     "dense_mtp4_bf16": "dense MTP4 verify, BF16 KV: B32 Hq16/Hkv1 D128 QL4 page128 L~U[16K,32K]",
+    "dense_mtp2_fp8": "supplementary: the dense MTP4 FP8 batch with QL2 (32 rows per KV head), same caches and tables",
     "long_d256": "long-context D256: B4 Hkv2 GQA8 QL4 page64 L=131072 window 8193, transposed V, per-tensor",
     "long_d256_nowindow": "supplementary: the long-context D256 batch with the window off (all 131072 tokens visible)",
     "ragged": "ragged batch: B128 Hkv4 GQA4 D128 QL1 page16 log-uniform L, window 257, sinks, per-token",
@@ -89,6 +90,8 @@ def make_inputs(workload: str):
         return W.config_ragged(), {}
     if workload == "dense_mtp4_bf16":
         return W.config_dense_mtp4("bf16"), {}
+    if workload == "dense_mtp2_fp8":
+        return W.config_dense_mtp4("fp8", query_len=2), {}
     return W.config_dense_mtp4("fp8"), {}
 
 

@@ -351,9 +351,11 @@ def dense_mtp4_lengths(rng: np.random.Generator, n: int = 32) -> np.ndarray:
     return rng.integers(16384, 32768, size=n, endpoint=True).astype(np.int32)
 
 
-def config_dense_mtp4(kv_dtype: str = KV_FP8, poison: bool = True, num_seqs: int = 32) -> Inputs:
+def config_dense_mtp4(kv_dtype: str = KV_FP8, poison: bool = True, num_seqs: int = 32, query_len: int = 4) -> Inputs:
     """C4: batch 32, Hq 16 / Hkv 1, D 128, QL 4 causal, page 128, lengths
-    uniform in [16384, 32768]; FP8 with per-token scales, or BF16 unscaled."""
+    uniform in [16384, 32768]; FP8 with per-token scales, or BF16 unscaled.
+    Another query_len gives the same caches and tables with that many
+    causal rows per sequence (QL 2: 32 rows per KV head)."""
     seed = config_seed(4)
     rng = _streams(seed ^ 0xB10C, 2)
     lens = dense_mtp4_lengths(rng[1], 32)[:num_seqs]
@@ -361,10 +363,10 @@ def config_dense_mtp4(kv_dtype: str = KV_FP8, poison: bool = True, num_seqs: int
     num_pages = int(lens_pages.sum())
     stride = 256
     bt = disjoint_tables(rng[0], lens_pages, num_pages, stride)
-    prob = Problem(num_seqs=num_seqs, query_len=4, num_q_heads=16, num_kv_heads=1, head_dim=128, page_size=128,
-                   num_pages=num_pages, table_stride=stride, kv_dtype=kv_dtype,
+    prob = Problem(num_seqs=num_seqs, query_len=query_len, num_q_heads=16, num_kv_heads=1, head_dim=128,
+                   page_size=128, num_pages=num_pages, table_stride=stride, kv_dtype=kv_dtype,
                    scale_mode=SCALE_TOKEN if kv_dtype == KV_FP8 else SCALE_NONE)
-    return build_dense(prob, lens, bt, seed, fill="context", poison=poison, name=f"dense_mtp4_{kv_dtype}")
+    return build_dense(prob, lens, bt, seed, fill="context", poison=poison, name=f"dense_mtp{query_len}_{kv_dtype}")
 
 
 def ragged_lengths(rng: np.random.Generator, n: int = 128) -> np.ndarray:

@@ -2,8 +2,9 @@
 the benchmark times (its input factory and plan options, the device's CU
 count): every output where the oracle is cheap (sparse, long-context D256,
 ragged), and a fixed sample of (row, head) outputs of every sequence for the
-dense MTP4 batches, compared element by element with the oracle within
-atol = rtol = 0.005 (aiter PR #6617, Validation)."""
+dense MTP4 batches (and the same FP8 batch with QL 2), compared element by
+element with the oracle within atol = rtol = 0.005 (aiter PR #6617,
+Validation)."""
 
 from __future__ import annotations
 
@@ -30,7 +31,7 @@ def test_full_size_every_output(workload):
     compare(got, O.attend(inp), f"{workload} full size")
 
 
-@pytest.mark.parametrize("workload", ["dense_mtp4_fp8", "dense_mtp4_bf16"])
+@pytest.mark.parametrize("workload", ["dense_mtp4_fp8", "dense_mtp4_bf16", "dense_mtp2_fp8"])
 def test_full_size_sampled(workload):
     inp, plan_kw = make_inputs(workload)
     p = inp.problem
