@@ -82,10 +82,16 @@ def test_d256(ql, hq, hkv):
         seed += 1
 
 
-def test_fp16_queries():
-    inp = W.make_dense_case(41, LENS, query_len=2, num_q_heads=16, num_kv_heads=2, head_dim=128, page_size=16,
-                            q_dtype="fp16", scale_mode="token", sliding_window=17, has_sinks=True)
-    announce("fp16 queries")
+@pytest.mark.parametrize("ql,hq,hkv,d,page,scale", [(2, 16, 2, 128, 16, "token"), (4, 16, 1, 128, 128, "token"),
+                                                    (2, 16, 1, 128, 64, "token"), (3, 8, 1, 128, 16, "tensor"),
+                                                    (4, 16, 2, 256, 64, "tensor")])
+def test_fp16_queries(ql, hq, hkv, d, page, scale):
+    """FP16 queries in every decode path: the 16-row tile kernel, the
+    streaming kernel with two row blocks (64 rows) and one (32 and 24 rows,
+    pages of 64 and 16), and the D256 tile kernel."""
+    inp = W.make_dense_case(41 + ql + d + page, LENS, query_len=ql, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                            page_size=page, q_dtype="fp16", scale_mode=scale, sliding_window=17, has_sinks=True)
+    announce(f"fp16 queries ql={ql} hq={hq} hkv={hkv} d={d} page={page} scale={scale}")
     _parity(inp, cu_count=64)
 
 
