@@ -113,7 +113,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // s_waitcnt lgkmcnt(0) with the other counters unconstrained.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
 
-// Streaming kernel for FP8 caches, head dim 128 and 33..64-row work items.
+// Streaming kernel for FP8 caches, head dim 128, page tables and 17..64-row
+// work items.
 bool stream_kernel_applies(const Plan& P);
 pa_status launch_stream(const Plan& P, const KernelArgs& args, int nblocks, hipStream_t stream);
 

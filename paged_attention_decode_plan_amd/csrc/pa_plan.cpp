@@ -66,8 +66,9 @@ pa_status validate_problem(const pa_problem* p) {
 }
 
 // Workgroups of the decode kernel that stay resident on one CU together.
-// (16-row items: 4-wave workgroups, two per CU; 32/64-row items: one 8-wave
-// workgroup per CU; head dim 256 and BF16 caches fill the LDS with one.)
+// (16-row items: 4-wave workgroups, two per CU; 17-64-row items: one
+// workgroup per CU, the 8-wave tile kernel or the 4-wave streaming kernel;
+// head dim 256 and BF16 caches fill the LDS with one.)
 static int resident_per_cu(const pa_problem& p, int nrt) {
   if (nrt >= 2 || p.head_dim > 128 || p.kv_dtype == PA_BF16 || p.token_table) return 1;
   return 2;

@@ -1,5 +1,6 @@
-// gfx950 streaming decode kernel for FP8 caches, head dim 128, and work items
-// of 33..64 query rows (multi-token (MTP) verify rows times a GQA group).
+// gfx950 streaming decode kernel for FP8 caches, head dim 128, page tables,
+// and work items of 17..64 query rows (multi-token (MTP) verify rows times a
+// GQA group): one 32-row block (RB = 1) or two (RB = 2).
 //
 // Same method as the tile kernel (online softmax per partition, partials
 // merged by the reducer in a fixed order: aiter PR #4332 "Add paged-attention
@@ -11,15 +12,15 @@
 //    tile, for all of the item's query rows;
 //  * a wave loads its K, V and per-token scales straight into registers with
 //    16-byte global loads (no LDS staging: on this part LDS-DMA streaming
-//    tops out well below what register loads reach), two steps ahead of the
-//    step it computes (two register buffers, steps taken in pairs), so the
-//    waves never synchronise inside the loop;
-//  * QK^T runs on v_mfma_f32_32x32x16_f16: K converts exactly to FP16 in
-//    registers, the query is FP16 with softmax_scale * log2(e) (and a
-//    per-tensor k scale) folded in, so the accumulator holds base-2 logits;
-//    per-token k scales multiply them in the FMA that also subtracts the
-//    reference maximum (the scaled conversions take only a power-of-two
-//    scale);
+//    tops out well below what register loads reach), three steps ahead of
+//    the step it computes (three register buffers, steps taken in groups of
+//    three), so the waves never synchronise inside the loop;
+//  * QK^T runs on v_mfma_scale_f32_32x32x64_f8f6f4 with K as stored (FP8)
+//    against two FP8 terms of the query (hi and a 16x residual, each with
+//    its own E8M0 block scale), softmax_scale * log2(e) (and a per-tensor k
+//    scale) folded in, so the accumulator holds base-2 logits; per-token k
+//    scales multiply them in the FMA that also subtracts the reference
+//    maximum;
 //  * the QK row of MFMA output register i in lane half h is token 16h + i of
 //    the step (the K rows are fed in that order), which is exactly the token
 //    order of the lane's slots in the PV operand: probabilities go from the
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   const int32_t* bt_row = a.block_tables + (long)s * a.table_stride;
 
   // ---- the query rows' raw bits (issued first: their wait does not cover the K/V loads) ----
-  const int q_r = tid >> 2, q_qq = tid & 3;  // 64 rows x 4 quarters
+  const int q_r = tid >> 2, q_qq = tid & 3;  // up to 64 rows x 4 quarters
   const bool q_valid = q_r < nrows && q_r < StreamSmem<RB>::ROWS;
   u32x4 qraw[4];
   {
@@ -194,13 +195,6 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     const long tok0 = (long)t0 + ((j + (long)tb * ppt) << ps_log2);
     return tok0 < hi_u && tok0 + ps > lo_u;
   };
-  // id of page j: staged in LDS, past the staged bound from the block table;
-  // pages without visible tokens read page 0 of the head (masked later)
-  auto page_id = [&](long j, auto DIRECT) -> long {
-    if (!page_ok(j)) return 0;
-    if (!decltype(DIRECT)::value && j < nstaged) return (long)ids[j];
-    return (long)__builtin_nontemporal_load(bt_row + id0 + j);
-  };
   // Lane-constant parts of the addresses (page >= 32: a step lies in one page)
   const int slot_k = (32 * w + kt) & (ps - 1);
   const uint32_t koff = (uint32_t)((2 * h * ps + slot_k) * 16);
@@ -215,37 +209,37 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   const uint32_t soff = (uint32_t)((kvh * ps + ((32 * w + c32) & (ps - 1))) * 4);
   const float* sbase = h ? a.v_scale : a.k_scale;
 
-  auto load_k = [&](StepData& d, int k, long id, auto DIRECT) {
-    const int ts_rel = (k - tb) * TT + 32 * w;  // step start relative to the item's first tile
+  // Page ids of a step, wave-uniform: the step's page (page >= 32), or its
+  // two pages (page 16: tokens 0-15 and 16-31 of the step).
+  struct StepPages {
+    long a, b;
+  };
+  auto load_k = [&](StepData& d, StepPages id) {
     if constexpr (BIG) {
-      const uint8_t* kp = kbase + id * a.page_stride;
+      const uint8_t* kp = kbase + id.a * a.page_stride;
       d.k[0] = load32(kp + koff, kp + koff + kcs);
       d.k[1] = load32(kp + koff + 4 * kcs, kp + koff + 5 * kcs);
-      if constexpr (PT) d.sc = *(const float*)((const uint8_t*)(sbase + id * a.Hkv * ps) + soff);
+      if constexpr (PT) d.sc = *(const float*)((const uint8_t*)(sbase + id.a * a.Hkv * ps) + soff);
     } else {
-      // page 16: the step spans two pages; addresses per lane
-      const int tk = ts_rel + kt;
-      const long idk = page_id(tk >> ps_log2, DIRECT);
-      const uint8_t* src = kbase + idk * a.page_stride + (long)(tk & (ps - 1)) * 16;
+      // page 16: token kt of the step is slot kt & 15 of its first or second page
+      const long idk = kt >= 16 ? id.b : id.a;
+      const uint8_t* src = kbase + idk * a.page_stride + (long)(kt & 15) * 16;
       d.k[0] = load32(src + (2 * h) * kcs, src + (2 * h + 1) * kcs);
       d.k[1] = load32(src + (2 * h + 4) * kcs, src + (2 * h + 5) * kcs);
       if constexpr (PT) {
-        const int tsc = ts_rel + c32;
-        const long ids_ = page_id(tsc >> ps_log2, DIRECT);
-        d.sc = sbase[(ids_ * a.Hkv + kvh) * ps + (tsc & (ps - 1))];
+        const long ids_ = c32 >= 16 ? id.b : id.a;
+        d.sc = sbase[(ids_ * a.Hkv + kvh) * ps + (c32 & 15)];
       }
     }
     if constexpr (!PT) d.sc = 0.f;
   };
-  auto load_v = [&](StepData& d, int k, long id, auto DIRECT) {
-    const int ts_rel = (k - tb) * TT + 32 * w;
+  auto load_v = [&](StepData& d, StepPages id) {
     if constexpr (BIG) {
-      const uint8_t* vp = vbase + id * a.page_stride;
+      const uint8_t* vp = vbase + id.a * a.page_stride;
 #pragma unroll
       for (int db = 0; db < 4; ++db) d.v[db] = *(const u32x4*)(vp + voff[db]);
     } else {
-      const long idv = page_id((ts_rel + 16 * h) >> ps_log2, DIRECT);  // the lane's 16 tokens: one page
-      const uint8_t* pg = vbase + idv * a.page_stride;
+      const uint8_t* pg = vbase + (h ? id.b : id.a) * a.page_stride;  // the lane's 16 tokens: one page
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const uint8_t* src = pg + (long)(32 * db + c32) * 16;  // page 16: both V layouts put a dim's 16 bytes here
@@ -256,10 +250,12 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
 
   const __attribute__((address_space(4))) int32_t* btc =
       (const __attribute__((address_space(4))) int32_t*)bt_row;
-  auto step_page_direct = [&](int k) -> long {  // page id of step k from the block table (page >= 32)
+  auto step_pages_direct = [&](int k) -> StepPages {  // step k's page ids from the block table
     const long j = (long)((k - tb) * TT + 32 * wu) >> ps_log2;
-    if (!page_ok(j)) return 0;
-    return btc[id0 + j];
+    StepPages r{0, 0};
+    if (page_ok(j)) r.a = btc[id0 + j];
+    if (!BIG && page_ok(j + 1)) r.b = btc[id0 + j + 1];
+    return r;
   };
   // Unconditional, so that the compiler's wait counts stay exact: an empty
   // item (tb >= te) reads page 0 of its head, which exists (the host routes
@@ -267,15 +263,15 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   StepData ba, bb, bc;
   {
     const int k1 = min(tb + 1, te - 1), k2 = min(tb + 2, te - 1);
-    const long p0 = BIG ? step_page_direct(tb) : 0;
-    const long p1 = BIG ? step_page_direct(k1) : 0;
-    const long p2 = BIG ? step_page_direct(k2) : 0;
-    load_k(ba, tb, p0, std::true_type{});
-    load_v(ba, tb, p0, std::true_type{});
-    load_k(bb, k1, p1, std::true_type{});
-    load_v(bb, k1, p1, std::true_type{});
-    load_k(bc, k2, p2, std::true_type{});
-    load_v(bc, k2, p2, std::true_type{});
+    const StepPages p0 = step_pages_direct(tb);
+    const StepPages p1 = step_pages_direct(k1);
+    const StepPages p2 = step_pages_direct(k2);
+    load_k(ba, p0);
+    load_v(ba, p0);
+    load_k(bb, p1);
+    load_v(bb, p1);
+    load_k(bc, p2);
+    load_v(bc, p2);
   }
 
   // ---- query operand: two FP8 terms per row with a power-of-two scale ----
@@ -398,8 +394,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   // MFMAs have consumed its V registers; each part then has a whole step to
   // arrive and lands in the registers it replaces.
   const int idv = lane < nstaged ? ids[lane] : 0;  // the first 64 staged ids, one per lane
-  auto step_page = [&](int k) -> long {  // page id of step k (page >= 32: wave-uniform)
-    const long j = (long)((k - tb) * TT + 32 * wu) >> ps_log2;
+  auto page_uniform = [&](long j) -> long {  // id of page j, wave-uniform
     // each source is read and made uniform in its own branch, so waiting for
     // the rare block-table read never waits for the K/V loads in flight
     if (!page_ok(j)) return 0;
@@ -408,6 +403,10 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     // past the staged bound: a scalar read of the block table (the table is
     // constant for the kernel's lifetime), counted apart from the K/V loads
     return btc[id0 + j];
+  };
+  auto step_page = [&](int k) -> StepPages {  // page ids of step k
+    const long j = (long)((k - tb) * TT + 32 * wu) >> ps_log2;
+    return StepPages{page_uniform(j), BIG ? 0L : page_uniform(j + 1)};
   };
 
   // Tiles [ti0, ti1) are visible to every row; their steps skip the masks
@@ -464,7 +463,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     const int tl = tsa + 16 * h;           // first of the lane's 16 tokens
     const int span_lo = lo_u, span_hi = hi_u;  // tokens whose V may be used
     const int kn = min(k + 3, te - 1);
-    const long nid = BIG ? step_page(kn) : 0;
+    const StepPages nid = step_page(kn);
 
     // V of the step; tokens outside the visible span get zero V (their bytes
     // may be anything, and 0 * NaN would reach O)
@@ -612,7 +611,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // VALU
     }
     __builtin_amdgcn_sched_barrier(0);
-    load_v(cur, kn, nid, std::false_type{});  // this step's V is converted
+    load_v(cur, nid);  // this step's V is converted
     if constexpr (RB == 2) {
       half8 p1[2];
       const f32x16 s1 = qk(1);
@@ -624,7 +623,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x002, 16, 1);  // VALU
       }
       __builtin_amdgcn_sched_barrier(0);
-      load_k(cur, kn, nid, std::false_type{});  // both row blocks' QK have read this step's K
+      load_k(cur, nid);  // both row blocks' QK have read this step's K
       pv(0, p0);
       probs(1, s1, p1);
 #pragma unroll
@@ -635,7 +634,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       pv(1, p1);
     } else {
-      load_k(cur, kn, nid, std::false_type{});  // the QK MFMAs have read this step's K
+      load_k(cur, nid);  // the QK MFMAs have read this step's K
       scales();
       probs(0, s0, p0);
       __builtin_amdgcn_sched_barrier(0);
@@ -665,17 +664,17 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     }
     if (tb >= te) return true;
     if (!first) {  // a restart: the first three steps' loads again
-      const long p0 = BIG ? step_page(tb) : 0;
-      load_k(ba, tb, p0, std::false_type{});
-      load_v(ba, tb, p0, std::false_type{});
+      const StepPages p0 = step_page(tb);
+      load_k(ba, p0);
+      load_v(ba, p0);
       const int k1 = min(tb + 1, te - 1);
-      const long p1 = BIG ? step_page(k1) : 0;
-      load_k(bb, k1, p1, std::false_type{});
-      load_v(bb, k1, p1, std::false_type{});
+      const StepPages p1 = step_page(k1);
+      load_k(bb, p1);
+      load_v(bb, p1);
       const int k2 = min(tb + 2, te - 1);
-      const long p2 = BIG ? step_page(k2) : 0;
-      load_k(bc, k2, p2, std::false_type{});
-      load_v(bc, k2, p2, std::false_type{});
+      const StepPages p2 = step_page(k2);
+      load_k(bc, p2);
+      load_v(bc, p2);
     }
     prep(ba, tb);
     // Groups of three steps: boundary groups (masks, reference updates)
