@@ -595,21 +595,19 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     };
 
     // Schedule (one wave per SIMD, so the overlap has to come from within
-    // the wave).  Two row blocks: QK of row block 0 with the V conversion;
-    // QK of row block 1 with the probabilities of block 0; PV of block 0
-    // with the probabilities of block 1; PV of block 1 with the next step's
-    // scales.  One row block: QK with the V conversion, the probabilities on
-    // their own, PV with the next step's scales.  V is reloaded (three steps
-    // ahead) once converted, K once every row block's QK MFMAs have read it.
+    // the wave), in parts fenced by scheduling barriers.  Two row blocks: QK
+    // of row block 0 with the V conversion; QK of row block 1 with the
+    // probabilities of block 0; PV of block 0 with the probabilities of
+    // block 1; PV of block 1 with the next step's scales.  One row block: QK
+    // with the V conversion, the probabilities on their own, PV with the
+    // next step's scales.  V is reloaded (three steps ahead) once converted,
+    // K once every row block's QK MFMAs have read it.  Inside a part the
+    // compiler interleaves the MFMAs with the VALU work (an interleave pinned
+    // by hand, one MFMA per 8-16 VALU, measured 2 % slower).
     static_assert(RB == 1 || RB == 2, "one or two row blocks");
     half8 p0[2];
     const f32x16 s0 = qk(0);
     vcvt();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA (FP8, 16 passes)
-      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // VALU
-    }
     __builtin_amdgcn_sched_barrier(0);
     load_v(cur, nid);  // this step's V is converted
     if constexpr (RB == 2) {
@@ -617,20 +615,10 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       const f32x16 s1 = qk(1);
       scales();
       probs(0, s0, p0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // MFMA (FP8, 16 passes)
-        __builtin_amdgcn_sched_group_barrier(0x002, 16, 1);  // VALU
-      }
       __builtin_amdgcn_sched_barrier(0);
       load_k(cur, nid);  // both row blocks' QK have read this step's K
       pv(0, p0);
       probs(1, s1, p1);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 2);  // VALU
-      }
       __builtin_amdgcn_sched_barrier(0);
       pv(1, p1);
     } else {
@@ -641,11 +629,6 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       pv(0, p0);
     }
     prep(nxt, k + 1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 3);  // VALU
-    }
     __builtin_amdgcn_sched_barrier(0);
     return !__builtin_amdgcn_ballot_w64(ovf);
   };
