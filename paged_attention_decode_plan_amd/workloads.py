@@ -456,3 +456,72 @@ def kv_bytes_visible(inp: Inputs) -> int:
             n = hi - lo
         tot += n
     return tot * p.num_kv_heads * per_tok
+
+
+def config_long_mtp4_device(device, num_seqs: int = 200, context: int = 200_000, seed: int = 0x5EED0200) -> Inputs:
+    """The pages' own MI355X decode shape (aiter PR #4332, the MI355 BS=200,
+    MTP4, C=200k measurement): batch 200, every context 200 000 tokens, QL 4
+    causal, Hq 16 / Hkv 1, D 128, page 128, FP8 e4m3fn K/V with per-token
+    scales, plain V, no window.  10.56 GB of KV per call, so the caches are
+    drawn on the device (torch's generator, seeded): K/V ~ N(0, 1) rounded
+    to FP8, per-token scales uniform in [0.005, 0.015), Q ~ N(0, 1) in BF16,
+    each sequence's pages a disjoint slice of one random permutation.  Every
+    tensor but context_lens lives on ``device``; use host_subset() to give
+    the oracle a few of the sequences."""
+    D, page, H = 128, 128, 1
+    pages_per_seq = (context + page - 1) // page
+    num_pages = num_seqs * pages_per_seq
+    prob = Problem(num_seqs=num_seqs, query_len=4, num_q_heads=16, num_kv_heads=H, head_dim=D, page_size=page,
+                   num_pages=num_pages, table_stride=pages_per_seq, kv_dtype=KV_FP8, scale_mode=SCALE_TOKEN)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def fp8_normal(shape):
+        out = torch.empty(shape, dtype=torch.uint8, device=device)
+        flat = out.view(-1)
+        step = 1 << 28  # bounded temporaries
+        for i in range(0, flat.numel(), step):
+            n = min(step, flat.numel() - i)
+            x = torch.randn(n, generator=g, device=device, dtype=torch.float32)
+            flat[i:i + n] = x.to(torch.float8_e4m3fn).view(torch.uint8)
+        return out
+
+    kc = fp8_normal((num_pages, H, D // 16, page, 16))
+    vc = fp8_normal((num_pages, H, D, page))
+    ks = 0.005 + 0.01 * torch.rand((num_pages, H, page), generator=g, device=device, dtype=torch.float32)
+    vs = 0.005 + 0.01 * torch.rand((num_pages, H, page), generator=g, device=device, dtype=torch.float32)
+    q = torch.randn((prob.rows, prob.num_q_heads, D), generator=g, device=device, dtype=torch.float32)
+    perm = torch.randperm(num_pages, generator=g, device=device).to(torch.int32)
+    return Inputs(problem=prob, q=q.to(torch.bfloat16).contiguous(), k_cache=kc, v_cache=vc,
+                  block_tables=perm.view(num_seqs, pages_per_seq).contiguous(),
+                  context_lens=torch.full((num_seqs,), context, dtype=torch.int32), k_scale=ks, v_scale=vs,
+                  sinks=None, name="long_mtp4_c200k")
+
+
+def host_subset(inp: Inputs, seqs) -> Inputs:
+    """A host copy of some sequences of a block-table workload whose tensors
+    may live on a device: their query rows, lengths and the pages their
+    tables name (renumbered in order), the rest of the problem unchanged.
+    The oracle's result for sequence seqs[i] of the subset is the original
+    sequence's."""
+    p = inp.problem
+    assert not p.token_table
+    seqs = list(seqs)
+    bt = inp.block_tables[seqs].cpu().long()  # [n, stride]
+    ids = bt.reshape(-1)
+    dev_ids = ids.to(inp.k_cache.device)
+    sub = dataclasses.replace(p, num_seqs=len(seqs), num_pages=int(ids.numel()))
+    rows = torch.cat([torch.arange(s * p.query_len, (s + 1) * p.query_len) for s in seqs])
+    per_token = inp.k_scale is not None and inp.k_scale.numel() > 1
+    return Inputs(
+        problem=sub,
+        q=inp.q[rows.to(inp.q.device)].cpu().contiguous(),
+        k_cache=inp.k_cache[dev_ids].cpu().contiguous(),
+        v_cache=inp.v_cache[dev_ids].cpu().contiguous(),
+        block_tables=torch.arange(ids.numel(), dtype=torch.int32).view(len(seqs), -1).contiguous(),
+        context_lens=inp.context_lens[seqs].cpu().contiguous(),
+        k_scale=None if inp.k_scale is None else (inp.k_scale[dev_ids] if per_token else inp.k_scale).cpu().contiguous(),
+        v_scale=None if inp.v_scale is None else (inp.v_scale[dev_ids] if per_token else inp.v_scale).cpu().contiguous(),
+        sinks=None if inp.sinks is None else inp.sinks.cpu(),
+        name=inp.name + "_subset",
+    )

@@ -37,8 +37,8 @@ def check_shapes(inp, dev):
     assert dev["v_cache"].numel() * dev["v_cache"].element_size() == p.num_pages * per_page * elem
     assert dev["block_tables"].shape == (p.num_seqs, p.table_stride)
     assert dev["context_lens"].shape == (p.num_seqs,)
-    bt = inp.block_tables.numpy()
-    lens = inp.context_lens.numpy()
+    bt = inp.block_tables.cpu().numpy()
+    lens = inp.context_lens.cpu().numpy()
     for s in range(p.num_seqs):
         n = int(min(max(lens[s], 0), p.table_stride if p.token_table else p.table_stride * p.page_size))
         used = bt[s, :n] if p.token_table else bt[s, : (n + p.page_size - 1) // p.page_size]
