@@ -132,7 +132,7 @@ def test_plan_covers_tiles_exactly_once(cu, ql, window, page):
     info = plan.info()
     assert info.max_parts <= min(cu, 256)
     units = len(lens) * 2 * info.row_groups
-    assert info.num_items <= max(units, 2 * cu)
+    assert info.num_items <= max(units, 8 * 2 * cu)  # at most 8 items per resident workgroup slot
     # longest items first
     lens_tiles = []
     for (s, g, rg, b, e, slot, part, np_) in work.tolist():
@@ -140,6 +140,24 @@ def test_plan_covers_tiles_exactly_once(cu, ql, window, page):
     # determinism
     again = B.Plan(prob, lens, cu_count=cu).work()
     assert (again.numpy() == work).all()
+
+
+def test_plan_multi_wave_for_long_batches():
+    """Long contexts on fewer units than resident slots: the planner takes
+    more items than slots when that balances the slots (the pages' MI355X
+    shape gets about five partitions per sequence), and keeps to one item
+    per slot for the dense MTP4 batch; refreshable plans keep the budget."""
+    prob = _prob(num_seqs=200, query_len=4, num_q_heads=16, num_kv_heads=1, page_size=128,
+                 num_pages=200 * 1563, table_stride=1563)
+    lens = [200000] * 200
+    plan = B.Plan(prob, lens, cu_count=256)
+    info = plan.info()
+    assert 4 * 256 <= info.num_items <= 8 * 256 and 5 <= info.max_parts <= 6
+    _coverage(plan, np.array(lens), prob, 4, 0, 128)
+    refresh = B.Plan(prob, lens, cu_count=256, refreshable=1)
+    assert refresh.info().num_items == 256
+    c4 = W.config_dense_mtp4("fp8", poison=False)
+    assert B.Plan(B.problem_of(c4.problem), c4.context_lens, cu_count=256).info().num_items == 256
 
 
 def test_plan_empty_sequences_get_clearing_items():
