@@ -233,6 +233,21 @@ def test_stream_kernel_run_to_run_bit_exact(page, ql, hq):
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("ql,hq,page", [(4, 16, 128), (2, 16, 64), (1, 8, 16)])
+def test_multi_wave_plans(ql, hq, page):
+    """Plans with more items than resident workgroups (long sequences on a
+    small CU count, so several waves of items run through each slot), in
+    the streaming kernel (64 and 32 rows) and the tile kernel (8 rows):
+    against the oracle."""
+    inp = W.make_dense_case(130 + ql + page, [12000, 11800, 12100, 12050, 11900], query_len=ql, num_q_heads=hq,
+                            num_kv_heads=1, head_dim=128, page_size=page, scale_mode="token", sliding_window=0,
+                            has_sinks=True, fill="context")
+    announce(f"multi-wave plan ql={ql} hq={hq} page={page}")
+    _, plan = _parity(inp, cu_count=3)
+    slots = 3 * (1 if ql * hq > 16 else 2)  # resident workgroups on three CUs
+    assert plan.info().num_items > slots
+
+
 @pytest.mark.parametrize("ql,hq,page", [(4, 16, 128), (1, 8, 16)])
 def test_pages_past_4gib(ql, hq, page):
     """Caches of more than 4 GiB (the pages' 200 000-token MI355 shape needs
