@@ -299,7 +299,7 @@ def test_stream_kernel_device_context_longer_than_plan(page, ql):
     compare(got, O.attend(inp), "stream kernel, longer device context")
 
 
-@pytest.mark.parametrize("kind", ["stream", "tile"])
+@pytest.mark.parametrize("kind", ["stream", "stream32", "tile"])
 def test_graph_replay_with_changing_lengths(kind):
     """One pa_decode + pa_reduce captured in a HIP graph and replayed while the
     device context lengths change between replays (growing past the planned
@@ -311,6 +311,8 @@ def test_graph_replay_with_changing_lengths(kind):
 
     if kind == "stream":
         cfg = dict(query_len=4, num_q_heads=16, page_size=128)
+    elif kind == "stream32":  # one row block
+        cfg = dict(query_len=2, num_q_heads=16, page_size=64)
     else:
         cfg = dict(query_len=1, num_q_heads=8, page_size=16)
     lens_max = [6000, 2500, 900]
@@ -374,7 +376,7 @@ def _check_device_work_list(plan, inp, lens, host_max_len):
     assert longest <= host_max_len
 
 
-@pytest.mark.parametrize("kind", ["stream", "tile"])
+@pytest.mark.parametrize("kind", ["stream", "stream32", "tile"])
 def test_device_refresh_in_graph(kind):
     """Row f2: pa_plan_refresh re-partitions a refreshable plan on the device
     from the device lengths; a graph of refresh + decode + reduce is replayed
@@ -384,6 +386,8 @@ def test_device_refresh_in_graph(kind):
 
     if kind == "stream":
         cfg = dict(query_len=4, num_q_heads=16, page_size=128)
+    elif kind == "stream32":  # one row block
+        cfg = dict(query_len=2, num_q_heads=16, page_size=64)
     else:
         cfg = dict(query_len=1, num_q_heads=8, page_size=16)
     lens_max = [6000, 2500, 900, 40]
