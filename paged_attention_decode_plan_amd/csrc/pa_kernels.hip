@@ -769,6 +769,7 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
 
   // ---- main loop: one attempt over the item's tiles ----
   bool first_attempt = true;
+  bool scan = false;  // the scan pass: an attempt that does not stop at an overflow
   auto attempt = [&](auto PTc) {
     if constexpr (!SPARSE) {
       // NST-deep ring: tiles tb .. tb+NST-2 in flight before the first compute
@@ -801,7 +802,7 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
           asm volatile("" ::: "memory");
           __builtin_amdgcn_s_barrier();
           asm volatile("" ::: "memory");
-          if (*(volatile int*)restart_flag) return false;  // an overflow: stop this attempt
+          if (!scan && *(volatile int*)restart_flag) return false;  // an overflow: stop this attempt
           if (tile + NST - 1 < te)
             issue_tile(tile + NST - 1, stage_base + ((tile - tb + NST - 1) % NST) * T::STAGE);
           compute_tile(PTc, INc, tile, stage_base + cur * T::STAGE);
@@ -819,7 +820,7 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
       }
       for (int tile = tb; tile < te; ++tile) {
         __syncthreads();
-        if (*(volatile int*)restart_flag) break;
+        if (!scan && *(volatile int*)restart_flag) break;
         const int cur = (tile - tb) & 1;
         const bool more = tile + 1 < te;
         if (more) load_sparse(tile + 1, st);
@@ -831,18 +832,27 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
       }
     }
   };
+  // Restarts.  An attempt that overflowed raises the references only to the
+  // maxima it saw before it stopped, so logits that keep climbing could stop
+  // every later attempt as well.  The first restart is therefore a scan pass
+  // that runs through the whole item: without an overflow its result stands;
+  // with one, the maxima it recorded (every score above its reference + TAU,
+  // every V-scale maximum above its band) raise each reference to at least
+  // the largest value of the item, and the last pass cannot overflow for any
+  // finite input.  At most three passes.
   auto run = [&](auto PTc) {
-    for (;; first_attempt = false) {
+    for (int pass = 0;; ++pass, first_attempt = false) {
 #pragma unroll
       for (int rt = 0; rt < NRW; ++rt) {
         l_part[rt] = 0.f;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[rt][dt] = f4{0.f, 0.f, 0.f, 0.f};
       }
+      scan = pass == 1;
       attempt(PTc);
       __syncthreads();
       const bool again = *(volatile int*)restart_flag != 0;
-      if (!again) break;
+      if (!again || pass == 2) break;
       // restart with the larger references
       __syncthreads();
       if (tid == 0) *restart_flag = 0;

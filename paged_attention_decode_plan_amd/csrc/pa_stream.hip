@@ -428,6 +428,9 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   // token.
   // Returns false when the wave has to restart with a larger reference.
   bool ovf = false;
+  // Scan pass (wave-uniform): a restart that does not stop at an overflow and
+  // records, per row, a reference bound over the whole share (see below).
+  bool scan = false;
   // V conversion scale of the next step: with per-token scales, 2^E comes
   // from the step's largest V scale (lanes 32-63 hold its 32 V scales), and
   // the scales go to LDS with the V scales divided by 2^E (and the k scales
@@ -549,7 +552,15 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
         const bool first = m_ref[rb] == -INFINITY;
         const bool over = !first && mx > m_ref[rb] + TAU_S;
         ovf |= over;
-        m_hi[rb] = over ? fmaxf(m_hi[rb], mx) : m_hi[rb];
+        if (scan) {
+          // a reference no logit of the step exceeds and under which the
+          // lane's probability sum (at most 16 * 2^(mx - ref)) times the
+          // largest normalised V scale stays at most 2^14
+          const float need = mx + fmaxf(0.f, __builtin_amdgcn_logf(vsmax) - 10.0f);
+          m_hi[rb] = fmaxf(m_hi[rb], need);
+        } else {
+          m_hi[rb] = over ? fmaxf(m_hi[rb], mx) : m_hi[rb];
+        }
         m_ref[rb] = first ? mx : m_ref[rb];
       }
       const float nm = m_ref[rb] == -INFINITY ? 0.f : -m_ref[rb];
@@ -573,7 +584,8 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       const float bnd = ls * vsmax;
       const bool big = bnd > 0x1p15f;
       ovf |= big;
-      m_hi[rb] = big ? fmaxf(m_hi[rb], m_ref[rb] + __builtin_amdgcn_logf(fminf(bnd, 0x1p127f))) : m_hi[rb];
+      if (!(gen && scan))
+        m_hi[rb] = big ? fmaxf(m_hi[rb], m_ref[rb] + __builtin_amdgcn_logf(fminf(bnd, 0x1p127f))) : m_hi[rb];
       if constexpr (PT) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) y[i] *= vs16[i];
@@ -637,7 +649,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   // load buffer each (a count that is not a multiple of three ends with one
   // or two steps that return at once).  An overflow stops it at the top of
   // the next group (a single latch keeps each O accumulator in place across
-  // iterations).
+  // iterations), except in the scan pass, which runs to the end.
   auto attempt = [&](bool first) __attribute__((always_inline)) -> bool {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -674,6 +686,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       go = step(GENc, bc, ba, k + 2) && go;
       __builtin_amdgcn_sched_barrier(0);
+      go = go || scan;
       k += 3;
     };
     if (first) {
@@ -687,30 +700,35 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       for (; k + 2 < ti1 && go;) triple(std::false_type{});
     }
     for (; k < te && go;) triple(std::true_type{});  // a restart runs every step with the masks
-    return go;
+    return !__builtin_amdgcn_ballot_w64(ovf);
   };
-  // A restart raises every reference to at least the maxima seen, so a second
-  // attempt normally completes; the bound only guards against inputs (NaN,
-  // infinities) for which no reference helps.
+  // Restarts.  The first attempt raises a row's reference only to the
+  // maxima it saw before it stopped, so logits that keep climbing could
+  // stop every later attempt too.  Instead the first restart is a scan pass
+  // over the wave's whole share: if it meets no overflow its result stands;
+  // otherwise it has recorded, per row, a reference no logit exceeds and
+  // under which no PV operand reaches 2^15, and one last pass with that
+  // reference cannot overflow for any finite input.  At most three passes.
   // The first attempt is its own copy of the loop, entered straight from the
   // early loads (no join with the restart path, whose different load history
   // would make the compiler wait for all three steps before the first).
-  auto raise_refs = [&]() __attribute__((always_inline)) {
-    wait_vmcnt<0>();  // loads issued past the stop
-    // restart this wave's share with references at least the maxima seen
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float mh = fmax_swap32(m_hi[rb]);
-      if (mh > m_ref[rb]) m_ref[rb] = mh;
-      m_hi[rb] = -INFINITY;
-    }
-    ovf = false;
-  };
   if (!attempt(true)) {
-    for (int tries = 2;; ++tries) {
-      raise_refs();
-      if (attempt(false) || tries == 8) break;
+    for (int pass = 0; pass < 2; ++pass) {
+      wait_vmcnt<0>();  // loads issued past the stop
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float mh = fmax_swap32(m_hi[rb]);
+        // after the first attempt: at least the maxima seen; after the scan:
+        // the bound over the whole share (rows without visible tokens keep
+        // their reference)
+        if (pass == 0 ? mh > m_ref[rb] : mh > -INFINITY) m_ref[rb] = mh;
+        m_hi[rb] = -INFINITY;
+      }
+      ovf = false;
+      scan = pass == 0;
+      if (attempt(false)) break;
     }
+    scan = false;
   }
 
   // ---- merge the four waves' states ----

@@ -42,7 +42,10 @@ def logical_caches(inp):
     return K, V
 
 
-def attend(inp) -> np.ndarray:
+def attend(inp, pos_shift: int = 0, window_shift: int = 0) -> np.ndarray:
+    """Dense masked softmax attention.  ``pos_shift`` / ``window_shift`` move
+    the causal bound and the window length (mutations for the sensitivity
+    test; 0 for the definition)."""
     p = inp.problem
     K, V = logical_caches(inp)
     q = inp.q.double().numpy()  # exact for bf16 / fp16
@@ -66,9 +69,9 @@ def attend(inp) -> np.ndarray:
         # explicit mask matrix [QL, L]
         i = np.arange(p.query_len)[:, None]
         pos = (L - p.query_len + i) if p.causal else np.full_like(i, L - 1)
-        mask = (t[None, :] <= pos) & (t[None, :] < L)
+        mask = (t[None, :] <= pos + pos_shift) & (t[None, :] < L)
         if p.sliding_window > 0:
-            mask &= t[None, :] > pos - p.sliding_window
+            mask &= t[None, :] > pos - (p.sliding_window + window_shift)
         for ii in range(p.query_len):
             row = s * p.query_len + ii
             for h in range(p.num_q_heads):

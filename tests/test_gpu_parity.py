@@ -447,3 +447,84 @@ def test_non_causal_multi_token(kv, hq, hkv, d, page):
                                 sliding_window=window, causal=False)
         announce(f"non-causal kv={kv} d={d} page={page} ql={ql} w={window}")
         _parity(inp, cu_count=64)
+
+
+ZERO_Q_PATHS = [
+    # name, query_len, Hq, Hkv, D, page, kv, scale
+    ("tile16", 1, 16, 1, 128, 16, "fp8", "token"),
+    ("tile8-tensor", 1, 8, 1, 128, 64, "fp8", "tensor"),
+    ("stream32", 2, 16, 1, 128, 64, "fp8", "token"),
+    ("stream64", 4, 16, 1, 128, 128, "fp8", "token"),
+    ("stream64-p16-tensor", 4, 16, 1, 128, 16, "fp8", "tensor"),
+    ("d256", 4, 16, 2, 256, 64, "fp8", "tensor"),
+    ("d256-token", 1, 8, 1, 256, 16, "fp8", "token"),
+    ("bf16", 4, 16, 1, 128, 128, "bf16", "none"),
+]
+
+
+@pytest.mark.parametrize("case", ZERO_Q_PATHS, ids=[c[0] for c in ZERO_Q_PATHS])
+def test_zero_query_rows(case):
+    """All-zero query rows (every head of every third row, and head 5 of every
+    row): the FP8 query split meets amax = 0, and the output must be the mean
+    of the visible V rows with no NaN (aiter PR #4332, follow-up commit: an
+    all-zero query row quantised to scale 0 turned the output into NaN)."""
+    name, ql, hq, hkv, d, page, kv, scale = case
+    inp = W.make_dense_case(150 + len(name), LENS, query_len=ql, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                            page_size=page, kv_dtype=kv, scale_mode=scale, sliding_window=17 if ql == 2 else 0,
+                            has_sinks=ql == 4)
+    inp.q[::3] = 0
+    inp.q[:, 5] = 0
+    announce(f"zero query rows {name}")
+    _parity(inp, cu_count=64)
+    _parity(inp, cu_count=4, max_partitions=1)
+
+
+def test_zero_query_rows_token_table():
+    inp = W.config_sparse(num_rows=6, selected=700, pool_pages=64)
+    inp.q[::2] = 0
+    inp.q[:, 3] = 0
+    announce("zero query rows, token table")
+    _parity(inp, cu_count=64, partition_tokens=256)
+
+
+@pytest.mark.parametrize("scale", ["tensor", "token"])
+@pytest.mark.parametrize("window", [0, 1, 17, 8193])
+def test_d256_breadth(scale, window):
+    """Head dim 256 across the pages' D256 validation axes (aiter PR #6617,
+    Validation): per-tensor and per-token scales, 1-4 causal rows, windows
+    0 / 1 / 17 / 8193, sinks, BF16 and FP16 queries, pages of 16 and 64,
+    plain and transposed V, on lengths from 0 to past the largest window."""
+    lens = [0, 1, 2, 17, 300, 9000]
+    seed = 3100 + window + (scale == "token")
+    for ql, page, vt in [(1, 16, True), (2, 64, False), (4, 64, True), (3, 16, False)]:
+        sinks = (ql + window) % 2 == 0
+        qd = "fp16" if ql % 2 == 1 else "bf16"
+        inp = W.make_dense_case(seed, lens, query_len=ql, num_q_heads=16, num_kv_heads=2, head_dim=256,
+                                page_size=page, q_dtype=qd, v_transposed=vt, scale_mode=scale, sliding_window=window,
+                                has_sinks=sinks)
+        announce(f"d256 scale={scale} w={window} ql={ql} page={page} vt={vt} sinks={sinks} q={qd}")
+        _parity(inp, cu_count=64)
+        seed += 1
+
+
+@pytest.mark.parametrize("kind", ["tile", "stream64", "stream32", "token_table"])
+def test_clamped_lengths(kind):
+    """Device and planned context lengths below 0 (count as 0) and past the
+    table's capacity (count as table_stride pages, or table_stride slots for
+    token tables) in every kernel, against the oracle on the same lengths."""
+    import dataclasses
+
+    if kind == "token_table":
+        inp = W.config_sparse(num_rows=4, selected=300, pool_pages=32)
+        cap = inp.problem.table_stride
+    else:
+        ql = {"tile": 1, "stream64": 4, "stream32": 2}[kind]
+        inp = W.make_dense_case(170 + ql, [2000, 40, 1000, 700], query_len=ql, num_q_heads=16, num_kv_heads=1,
+                                page_size=64, scale_mode="token", fill="context", table_slack=0,
+                                poison=False)  # the clamp makes stale table entries visible
+        cap = inp.problem.table_stride * inp.problem.page_size
+    lens = torch.tensor([cap + 5, -3, 1 << 30, -(1 << 30)], dtype=torch.int32)
+    wild = dataclasses.replace(inp, context_lens=lens)
+    announce(f"clamped lengths {kind} cap={cap}")
+    got, _ = run(wild, cu_count=64)
+    compare(got, O.attend(wild), f"clamped lengths {kind}")

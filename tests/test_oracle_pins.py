@@ -12,6 +12,7 @@
 
 from __future__ import annotations
 
+import dataclasses
 import itertools
 import math
 import os
@@ -268,3 +269,79 @@ def test_oracle_vs_bruteforce_non_causal(page):
         q[:, 1:] = q[:, :1]
         out = O.attend(inp, nthreads=2).reshape(p.num_seqs, ql, p.num_q_heads, p.head_dim)
         np.testing.assert_array_equal(out[:, 1:], np.broadcast_to(out[:, :1], out[:, 1:].shape))
+
+
+@pytest.mark.parametrize("page", [16, 64])
+def test_oracle_vs_bruteforce_fp16_queries(page):
+    """FP16 queries (decoded exactly by both sides) over the same sweep of
+    lengths, query lengths and windows, with per-token and per-tensor FP8
+    caches and sinks."""
+    for (ql, w), scale in itertools.product(itertools.product([1, 2, 4], [0, 1, 17]), ["tensor", "token"]):
+        inp = W.make_dense_case(800 + 7 * ql + w + page + (scale == "token"), LENS, query_len=ql, num_q_heads=4,
+                                num_kv_heads=2, head_dim=32, page_size=page, q_dtype="fp16", scale_mode=scale,
+                                sliding_window=w, has_sinks=True, poison=False, fill="context")
+        assert inp.q.dtype == torch.float16
+        got = O.attend(inp, nthreads=2).astype(np.float64)
+        np.testing.assert_allclose(got, bruteforce.attend(inp), rtol=1e-6, atol=1e-7, err_msg=f"ql={ql} w={w}")
+
+
+@pytest.mark.parametrize("token_table", [False, True])
+def test_clamped_lengths(token_table):
+    """Context lengths below 0 count as 0 and lengths past the table's
+    capacity (table_stride pages, or table_stride slots for token tables)
+    count as that capacity: against the brute force, and identical to the
+    oracle on the clamped lengths."""
+    if token_table:
+        inp = W.config_sparse(num_rows=4, selected=40, pool_pages=8)
+        cap = inp.problem.table_stride
+    else:
+        inp = W.make_dense_case(21, [40, 17, 5, 33], **_case(query_len=2, scale_mode="token", table_slack=0))
+        cap = inp.problem.table_stride * inp.problem.page_size
+        assert cap < 100
+    lens = torch.tensor([-7, cap + 1, -1, 1 << 30], dtype=torch.int32)
+    wild = dataclasses.replace(inp, context_lens=lens)
+    tame = dataclasses.replace(inp, context_lens=torch.tensor([0, cap, 0, cap], dtype=torch.int32))
+    got = O.attend(wild, nthreads=2)
+    np.testing.assert_allclose(got.astype(np.float64), bruteforce.attend(wild), rtol=1e-6, atol=1e-7)
+    np.testing.assert_array_equal(got, O.attend(tame, nthreads=2))
+    ql = inp.problem.query_len
+    assert (got[0:ql] == 0).all() and (got[2 * ql:3 * ql] == 0).all()
+    assert np.isfinite(got).all() and (got[ql:2 * ql] != 0).any()
+
+
+def _mutants(inp):
+    """The oracle's output with one plausible mistake planted: (name, output)."""
+    p = inp.problem
+    out = []
+    out.append(("causal bound + 1", bruteforce.attend(inp, pos_shift=1)))
+    if p.sliding_window > 0:
+        out.append(("window + 1", bruteforce.attend(inp, window_shift=1)))
+    if p.scale_mode == "token":
+        for name in ("k_scale", "v_scale"):
+            m = dataclasses.replace(inp, **{name: torch.roll(getattr(inp, name), 1, dims=2).contiguous()})
+            out.append((f"{name} one slot off", O.attend(m, nthreads=2)))
+    bt = inp.block_tables.clone()
+    bt[:, 0] = inp.block_tables[:, 1]  # every sequence's first page replaced by its second
+    out.append(("first page id", O.attend(dataclasses.replace(inp, block_tables=bt), nthreads=2)))
+    return out
+
+
+@pytest.mark.parametrize("scale,window", [("token", 0), ("token", 17), ("tensor", 257)])
+def test_tolerance_detects_planted_mistakes(scale, window):
+    """On inputs of the GPU parity matrix's kind (the same lengths, MTP rows,
+    GQA and N(0,1) data), each planted mistake -- a causal bound shifted by
+    one, a window one token longer, per-token K or V scales misplaced by one
+    slot, a wrong page id -- moves some output by at least ten times the
+    parity tolerance and puts at least 16 outputs outside it, so atol = rtol
+    = 0.005 cannot hide them (the pages report differences of 0.13 or more
+    for such mistakes in their cases, aiter PR #7079 test list; here a
+    window one token longer than 257 moves outputs by about 0.1)."""
+    inp = W.make_dense_case(900 + window, [0, 1, 2, 15, 17, 150, 300, 1000], query_len=4, num_q_heads=16,
+                            num_kv_heads=1, head_dim=128, page_size=16, scale_mode=scale, sliding_window=window,
+                            poison=False, fill="context")
+    ref = O.attend(inp, nthreads=4).astype(np.float64)
+    for name, got in _mutants(inp):
+        err = np.abs(np.asarray(got, np.float64) - ref)
+        excess = err - (0.005 + 0.005 * np.abs(ref))
+        assert err.max() >= 0.05, (name, float(err.max()))
+        assert (excess > 0).sum() >= 16, (name, int((excess > 0).sum()))
