@@ -23,9 +23,14 @@
  *
  * Ownership: the caller allocates every device buffer (query, output, caches,
  * tables, scales, sinks, meta_dev, workspace_dev).  The library allocates only
- * the host plan object; it never allocates device memory and never
- * synchronises the host.  Status codes are returned, never exceptions; the
- * thread-local pa_last_error() explains the last non-OK status.
+ * the host plan object and its pinned host copy of the metadata; it never
+ * allocates device memory and never synchronises the host.  Status codes are
+ * returned, never exceptions; the thread-local pa_last_error() explains the
+ * last non-OK status.
+ *
+ * Call order: pa_plan, pa_plan_sizes, (allocate meta_dev and workspace_dev),
+ * pa_plan_upload once, then pa_decode + pa_reduce per step (optionally
+ * preceded by pa_plan_refresh for a refreshable plan).
  */
 #ifndef PA_DECODE_H
 #define PA_DECODE_H
@@ -79,7 +84,10 @@ typedef struct {
   int32_t cu_count;         /* 0: query the current device */
   int32_t max_partitions;   /* per (sequence, KV head); 0: cu_count, capped at 256 */
   int32_t partition_tokens; /* > 0: fixed partition length (rounded up to 128 tokens) */
-  int32_t stage_limit;      /* page/slot ids staged in LDS per work item; 0: 1024 (max) */
+  int32_t stage_limit;      /* page/slot ids staged in LDS per work item; 0: 1024 (max; the rest of an
+                               item's ids are read from the block table with scalar loads).  1024 ids
+                               (4 KB) keep two 16-row workgroups within one CU's 160 KB of LDS; the
+                               pages' 4096 would not */
   int32_t refreshable;      /* 1: a fixed budget of work items and partial slots (cu_count x resident
                                workgroups, at least one per (sequence, KV head, row group)) and one reduce
                                entry per such unit, so that pa_plan_refresh can re-partition the plan on
@@ -101,17 +109,26 @@ typedef struct {
 
 /*
  * Build a plan from host context lengths (planning reads only the host copy).
- * Partitions per (sequence, KV head) minimise the longest work item under a
- * budget of (cu_count x resident workgroups per CU) items; empty sequences
- * get one zero-length item that clears their rows.  Returns PA_ERR_INVALID /
+ * The split-KV work plan of aiter PR #4332 "Add paged-attention Tile kernel"
+ * (work plans and the commit that defaults the per-sequence partition limit
+ * to the CU count): partitions per (sequence, KV head, row group of up to 64
+ * query rows) minimise the longest work item under a budget of (cu_count x
+ * resident workgroups per CU) items, at most max_partitions (default: the CU
+ * count, capped at 256) each, over the 128-token tiles of the union of what
+ * the sequence's query rows can see (window and causal MTP rows, aiter PR
+ * #6617 "Extend packed D256 PA decode pipe", summary); empty sequences get
+ * one zero-length item that clears their rows (aiter PR #7079 "Merge gfx1250
+ * PA decode partitions", Partition merges).  Returns PA_ERR_INVALID /
  * PA_ERR_UNSUPPORTED for bad problems (see pa_decode), PA_ERR_DEVICE if
- * cu_count is 0 and no device can be queried.  *out is NULL on error.
+ * cu_count is 0 and no device can be queried.  *out is NULL on error.  The
+ * plan is a host object owned by the caller (pa_plan_free).
  */
 pa_status pa_plan(const pa_problem* problem, const int32_t* context_lens_host, const pa_plan_opts* opts,
                   pa_plan_t** out);
 
-/* Device bytes the caller must provide: meta_dev (work list, reduce table)
- * and workspace_dev (FP32 partial states).  Either may be 0 bytes. */
+/* Device bytes the caller must provide: meta_dev (a 32-byte header, the work
+ * list and the reduce table; at least 32 bytes) and workspace_dev (FP32
+ * partial states; may be 0 bytes). */
 pa_status pa_plan_sizes(const pa_plan_t* plan, size_t* meta_bytes, size_t* workspace_bytes);
 
 /* Summary counts of a plan (host only). */
@@ -123,30 +140,60 @@ pa_status pa_plan_info(const pa_plan_t* plan, pa_plan_info_t* info);
  * n_items_capacity limits the copy; returns PA_ERR_INVALID if too small. */
 pa_status pa_plan_work(const pa_plan_t* plan, int32_t* out, int32_t n_items_capacity);
 
+/*
+ * Copy the plan's metadata (header, work list, reduce table: meta_bytes of
+ * pa_plan_sizes) into the caller's device buffer meta_dev with one
+ * asynchronous copy on `stream`, from a pinned host copy that the first call
+ * allocates and pa_plan_free releases.  Required once per (plan, buffer)
+ * before pa_decode / pa_reduce use the buffer, and again whenever the buffer
+ * has held another plan's list (pa_decode and pa_reduce return
+ * PA_ERR_WORKSPACE for a buffer whose last upload or refresh was another
+ * plan's).  The header carries a per-plan serial that every kernel checks:
+ * a buffer reallocated or overwritten after its upload makes the kernels do
+ * nothing (the output is left untouched) instead of following a foreign
+ * list.  Errors: PA_ERR_INVALID (NULL plan, meta_dev not 16-byte aligned),
+ * PA_ERR_WORKSPACE (NULL meta_dev), PA_ERR_DEVICE (pinned allocation or copy
+ * failed).
+ */
+pa_status pa_plan_upload(const pa_plan_t* plan, void* meta_dev, void* stream);
+
 void pa_plan_free(pa_plan_t* plan);
 
 /*
- * One launch: every work item of the plan.  Writes partial states to
- * workspace_dev for multi-partition (sequence, KV head) pairs and the final
- * rows of `out` for the others (including cleared rows of empty sequences).
- * The plan metadata is copied to meta_dev on `stream` when meta_dev differs
- * from the last upload.  `stream` is a hipStream_t (NULL: default stream).
+ * One launch over every work item of the plan: the decode of aiter PR #4332
+ * "Add paged-attention Tile kernel" (host wrapper: query, paged caches,
+ * block tables, context lengths, scales; partials pmax / psum / pout for
+ * split-KV): page-id staging, K/V page gather, QK^T with the dequant scales
+ * applied before the mask (aiter PR #6617, review), masked online softmax,
+ * PV, and the partition epilogue.  Writes partial states to workspace_dev
+ * for multi-partition (sequence, KV head) pairs and the final rows of `out`
+ * for the others (including cleared rows of empty sequences).
+ * Arguments: device pointers in the layouts of pa_problem; meta_dev filled
+ * by pa_plan_upload (or pa_plan_refresh) for this plan; workspace_dev of
+ * workspace_bytes; `stream` a hipStream_t (NULL: default stream).  Never
+ * allocates, copies or synchronises: it can be captured in a HIP graph.
  * Device context_lens are authoritative: a sequence longer than planned is
  * still fully processed (its last partition runs to the end, reading page ids
- * past the staged range from the block table directly).
+ * past the staged range from the block table directly); lengths below 0
+ * count as 0 and lengths past table_stride pages (slots) as that capacity.
  * Errors: PA_ERR_INVALID for null or misaligned (16 B) pointers,
- * PA_ERR_WORKSPACE for missing meta/workspace, PA_ERR_DEVICE for launch errors.
+ * PA_ERR_WORKSPACE for missing meta/workspace or a meta_dev that does not
+ * hold this plan's metadata, PA_ERR_DEVICE for launch errors.
  */
 pa_status pa_decode(const pa_plan_t* plan, void* out, const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* context_lens, const float* k_scale,
                     const float* v_scale, const float* sinks, void* meta_dev, void* workspace_dev, void* stream);
 
 /*
- * Merge the partial states of every multi-partition (sequence, KV head) into
- * `out` (log-sum-exp in partition order; sinks join the denominator; a row
- * with no visible token gets 0).  At most one launch; none if the plan has no
- * multi-partition pair.  Must follow pa_decode of the same plan on the same
- * stream.  A plan with its meta/workspace must not serve two in-flight calls.
+ * The partition merge (aiter PR #7079 "Merge gfx1250 PA decode partitions",
+ * Launch and reducer latency; sinks at the merge, Partition merges): merge
+ * the partial states of every multi-partition (sequence, KV head) into `out`
+ * by the log-sum-exp rule, partitions added in a fixed order (run-to-run
+ * bit-identical); sinks join the denominator; a row with no visible token
+ * gets 0.  At most one launch; none if the plan has no multi-partition pair.
+ * Must follow pa_decode of the same plan on the same stream.  A plan with
+ * its meta/workspace must not serve two in-flight calls.  Errors as
+ * pa_decode.
  */
 pa_status pa_reduce(const pa_plan_t* plan, void* out, const float* sinks, void* meta_dev, void* workspace_dev,
                     void* stream);

@@ -23,8 +23,9 @@ PA_BF16, PA_FP16, PA_FP8_E4M3FN = range(3)
 PA_V_PLAIN, PA_V_TRANSPOSED = range(2)
 PA_SCALE_NONE, PA_SCALE_PER_TENSOR, PA_SCALE_PER_TOKEN = range(3)
 
-EXPORTS = ["pa_plan", "pa_plan_sizes", "pa_plan_info", "pa_plan_work", "pa_plan_free", "pa_decode", "pa_reduce",
-           "pa_plan_refresh", "pa_last_error"]
+EXPORTS = ["pa_plan", "pa_plan_sizes", "pa_plan_info", "pa_plan_work", "pa_plan_upload", "pa_plan_free", "pa_decode",
+           "pa_reduce", "pa_plan_refresh", "pa_last_error"]
+META_HEADER_BYTES = 32  # meta_dev starts with the plan's header; the work list follows
 
 
 class PaProblem(ctypes.Structure):
@@ -65,6 +66,8 @@ def load_library(path: str = LIB_PATH):
     L.pa_plan_info.argtypes = [vp, ctypes.POINTER(PaPlanInfo)]
     L.pa_plan_work.restype = ctypes.c_int
     L.pa_plan_work.argtypes = [vp, vp, ctypes.c_int32]
+    L.pa_plan_upload.restype = ctypes.c_int
+    L.pa_plan_upload.argtypes = [vp, vp, vp]
     L.pa_plan_free.restype = None
     L.pa_plan_free.argtypes = [vp]
     L.pa_decode.restype = ctypes.c_int
@@ -138,11 +141,23 @@ class Plan:
         _check(load_library().pa_plan_work(self.handle, out.data_ptr(), n))
         return out[:n]
 
-    def allocate(self, device="cuda"):
-        """Device metadata and workspace (16-byte aligned torch allocations)."""
+    def allocate(self, device="cuda", stream=None):
+        """Device metadata and workspace (16-byte aligned torch allocations),
+        and the metadata upload (pa_plan_upload) on `stream`."""
         self.meta = torch.empty(max(self.meta_bytes, 16), dtype=torch.uint8, device=device)
         self.workspace = torch.empty(max(self.workspace_bytes // 4, 4), dtype=torch.float32, device=device)
+        self.upload(stream)
         return self
+
+    def upload(self, stream=None):
+        """Copy the plan's metadata into self.meta (needed again only if the
+        buffer has since held another plan's list)."""
+        _check(load_library().pa_plan_upload(self.handle, _ptr(self.meta), _stream_ptr(stream)))
+
+    def work_list_device(self) -> torch.Tensor:
+        """The work list as it is in self.meta (int32 [num_items, 8])."""
+        n = self.info().num_items
+        return self.meta[META_HEADER_BYTES: META_HEADER_BYTES + 32 * n].view(torch.int32).view(n, 8)
 
     def __del__(self):
         h = getattr(self, "handle", None)

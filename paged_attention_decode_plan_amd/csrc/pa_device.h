@@ -39,6 +39,8 @@ struct KernelArgs {
   const float* v_scale;
   const float* sinks;
   const WorkItem* items;
+  const MetaHeader* meta;  // header of the metadata buffer (items follow it)
+  uint32_t tag_lo, tag_hi;  // the launching plan's serial: the header must hold it
   float* workspace;
   long long page_stride;  // bytes between physical pages (Hkv * D * page * elem)
   long long head_stride;  // bytes between KV heads of a page (D * page * elem)
@@ -101,6 +103,12 @@ __device__ __forceinline__ half8 fp8x8_to_half8(u32x2 v) {
 // spreads the QK operand reads of one lane group over more bank quads; it is
 // its own inverse.
 __device__ __forceinline__ int kswz(int t) { return t ^ (((t >> 3) & 1) << 2); }
+
+// Whether the metadata buffer holds the launching plan's list (its header
+// carries the plan's serial); loaded together with the work item.
+__device__ __forceinline__ bool meta_ok(const MetaHeader& h, uint32_t lo, uint32_t hi) {
+  return h.magic == kMetaMagic && h.serial_lo == lo && h.serial_hi == hi;
+}
 
 // s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
 // vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).

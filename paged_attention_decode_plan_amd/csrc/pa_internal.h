@@ -33,7 +33,17 @@ struct ReduceItem {
 };
 static_assert(sizeof(ReduceItem) == 32, "reduce item is 32 bytes");
 
-// Layout of meta_dev: [WorkItem x num_items][ReduceItem x num_reduce]
+// First 32 bytes of meta_dev: which plan's list the buffer holds.  Every
+// kernel compares it with the plan it was launched for and does nothing on
+// a mismatch (a buffer reallocated or overwritten since its upload), so a
+// foreign list can never steer its indices.
+constexpr uint32_t kMetaMagic = 0x314D4150u;  // "PAM1"
+struct MetaHeader {
+  uint32_t magic, serial_lo, serial_hi, n_items, n_reduce, pad0, pad1, pad2;
+};
+static_assert(sizeof(MetaHeader) == 32, "metadata header is 32 bytes");
+
+// Layout of meta_dev: [MetaHeader][WorkItem x num_items][ReduceItem x num_reduce]
 struct Plan {
   pa_problem prob;
   pa_plan_opts opts;
@@ -51,11 +61,13 @@ struct Plan {
   std::vector<WorkItem> items;
   std::vector<ReduceItem> reduce;
   int num_slots = 0;
-  // the meta_dev this plan was last uploaded to (re-upload on change)
-  mutable void* uploaded_to = nullptr;
-  std::vector<uint8_t> meta_host;  // serialised metadata
+  uint64_t serial = 0;              // unique per plan in the process
+  std::vector<uint8_t> meta_host;   // serialised metadata (header, items, reduce table)
+  mutable uint8_t* meta_pinned = nullptr;  // pinned copy of meta_host, made by the first upload
 
   size_t meta_bytes() const { return meta_host.size(); }
+  static constexpr size_t items_offset() { return sizeof(MetaHeader); }
+  size_t reduce_offset() const { return sizeof(MetaHeader) + items.size() * sizeof(WorkItem); }
   // partial state per slot: m[rows_per_group], l[rows_per_group], o[rows_per_group][D]
   size_t slot_floats() const { return (size_t)rows_per_group * (2 + prob.head_dim); }
   size_t workspace_bytes() const { return (size_t)num_slots * slot_floats() * sizeof(float); }
@@ -64,6 +76,11 @@ struct Plan {
 // thread-local error message helper (defined in pa_plan.cpp)
 pa_status set_error(pa_status st, const std::string& msg);
 pa_status validate_problem(const pa_problem* p);
+
+// Which plan's metadata each device buffer holds (process-wide; set by
+// pa_plan_upload and pa_plan_refresh, checked by pa_decode and pa_reduce).
+void meta_registry_set(const void* meta_dev, uint64_t serial);
+bool meta_registry_holds(const void* meta_dev, uint64_t serial);
 
 }  // namespace pa
 

@@ -128,6 +128,8 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   const int wt = w / R::WR;  // this wave's token group
 
   const WorkItem it = a.items[blockIdx.x];
+  const MetaHeader mh = *a.meta;
+  if (!meta_ok(mh, a.tag_lo, a.tag_hi)) return;  // not this plan's list: touch nothing
   if (it.seq < 0) return;  // an unused item of a refreshable plan
   const int s = it.seq, kvh = it.kvh, rg = it.rg;
   const int ps = a.page_size;
@@ -998,6 +1000,8 @@ struct ReduceArgs {
   const float* workspace;
   const float* sinks;
   const ReduceItem* entries;
+  const MetaHeader* meta;
+  uint32_t tag_lo, tag_hi;
   int QL, Hq, G, D, rows_total, rows_per_group, q_fp16, has_sinks, chunks_per_entry;
 };
 
@@ -1014,6 +1018,8 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(ReduceArgs a) {
   __shared__ float wgt[RR][kMaxPartitions];
   __shared__ float rowf[RR];
   const ReduceItem e = a.entries[blockIdx.x / a.chunks_per_entry];
+  const MetaHeader mh = *a.meta;
+  if (!meta_ok(mh, a.tag_lo, a.tag_hi)) return;  // not this plan's list: touch nothing
   if (e.nparts < 2) return;  // a unit with one partition wrote its rows itself
   const int chunk = blockIdx.x % a.chunks_per_entry;
   const int rpg = a.rows_per_group;
@@ -1136,6 +1142,8 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(ReduceArgs a) {
 // ---------------------------------------------------------------------------
 struct RefreshArgs {
   const int32_t* context_lens;
+  MetaHeader* meta;
+  MetaHeader header;  // the plan's header, written with the new list
   WorkItem* items;
   ReduceItem* reduce;
   int num_seqs, QL, window, causal, page_size, table_stride, token_table, Hkv, row_groups;
@@ -1245,6 +1253,7 @@ __global__ __launch_bounds__(REF_T) void pa_refresh_kernel(RefreshArgs a) {
     __syncthreads();
   }
   for (long i = item_base + tid; i < a.n_items; i += REF_T) a.items[i] = WorkItem{-1, 0, 0, 0, 0, -1, 0, 1};
+  if (tid == 0) *a.meta = a.header;  // the buffer now holds this plan's list
 }
 
 // ---------------------------------------------------------------------------
@@ -1306,15 +1315,10 @@ extern "C" pa_status pa_decode(const pa_plan_t* plan, void* out, const void* q, 
   }
   if (p.has_sinks && !sinks) return set_error(PA_ERR_INVALID, "has_sinks set but sinks is NULL");
   if (!meta_dev) return set_error(PA_ERR_WORKSPACE, "meta_dev is NULL");
+  if (!meta_registry_holds(meta_dev, P.serial))
+    return set_error(PA_ERR_WORKSPACE, "meta_dev does not hold this plan's metadata: call pa_plan_upload first");
   if (P.num_slots > 0 && !workspace_dev) return set_error(PA_ERR_WORKSPACE, "workspace_dev is NULL");
   hipStream_t st = (hipStream_t)stream;
-  if (P.uploaded_to != meta_dev) {
-    if (hipMemcpyAsync(meta_dev, P.meta_host.data(), P.meta_host.size(), hipMemcpyHostToDevice, st) != hipSuccess) {
-      (void)hipGetLastError();
-      return set_error(PA_ERR_DEVICE, "metadata upload failed");
-    }
-    P.uploaded_to = meta_dev;
-  }
   const int elem = p.kv_dtype == PA_FP8_E4M3FN ? 1 : 2;
   KernelArgs args;
   args.out = out;
@@ -1326,7 +1330,10 @@ extern "C" pa_status pa_decode(const pa_plan_t* plan, void* out, const void* q, 
   args.k_scale = k_scale;
   args.v_scale = v_scale;
   args.sinks = sinks;
-  args.items = (const WorkItem*)meta_dev;
+  args.items = (const WorkItem*)((const uint8_t*)meta_dev + Plan::items_offset());
+  args.meta = (const MetaHeader*)meta_dev;
+  args.tag_lo = (uint32_t)P.serial;
+  args.tag_hi = (uint32_t)(P.serial >> 32);
   args.workspace = (float*)workspace_dev;
   args.head_stride = (long long)p.head_dim * p.page_size * elem;
   args.page_stride = args.head_stride * p.num_kv_heads;
@@ -1365,8 +1372,10 @@ extern "C" pa_status pa_plan_refresh(const pa_plan_t* plan, const int32_t* conte
     return set_error(PA_ERR_INVALID, "meta_dev or context_lens is NULL");
   RefreshArgs ra;
   ra.context_lens = context_lens;
-  ra.items = (WorkItem*)meta_dev;
-  ra.reduce = (ReduceItem*)((uint8_t*)meta_dev + P.items.size() * sizeof(WorkItem));
+  ra.meta = (MetaHeader*)meta_dev;
+  std::memcpy(&ra.header, P.meta_host.data(), sizeof(MetaHeader));
+  ra.items = (WorkItem*)((uint8_t*)meta_dev + Plan::items_offset());
+  ra.reduce = (ReduceItem*)((uint8_t*)meta_dev + P.reduce_offset());
   ra.num_seqs = P.prob.num_seqs;
   ra.QL = P.prob.query_len;
   ra.window = P.prob.sliding_window;
@@ -1382,7 +1391,7 @@ extern "C" pa_status pa_plan_refresh(const pa_plan_t* plan, const int32_t* conte
   hipLaunchKernelGGL(pa_refresh_kernel, dim3(1), dim3(REF_T), 0, (hipStream_t)stream, ra);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(PA_ERR_DEVICE, std::string("refresh launch failed: ") + hipGetErrorString(err));
-  P.uploaded_to = meta_dev;  // the device list is now the one to use
+  meta_registry_set(meta_dev, P.serial);  // the device list is now this plan's
   return PA_OK;
 }
 
@@ -1395,12 +1404,16 @@ extern "C" pa_status pa_reduce(const pa_plan_t* plan, void* out, const float* si
   if (!aligned16(out)) return set_error(PA_ERR_INVALID, "out must be 16-byte aligned");
   if (P.prob.has_sinks && !sinks) return set_error(PA_ERR_INVALID, "has_sinks set but sinks is NULL");
   if (!meta_dev || !workspace_dev) return set_error(PA_ERR_WORKSPACE, "meta_dev or workspace_dev is NULL");
-  if (P.uploaded_to != meta_dev) return set_error(PA_ERR_WORKSPACE, "meta_dev was not filled by pa_decode");
+  if (!meta_registry_holds(meta_dev, P.serial))
+    return set_error(PA_ERR_WORKSPACE, "meta_dev does not hold this plan's metadata: call pa_plan_upload first");
   ReduceArgs ra;
   ra.out = out;
   ra.workspace = (const float*)workspace_dev;
   ra.sinks = sinks;
-  ra.entries = (const ReduceItem*)((const uint8_t*)meta_dev + P.items.size() * sizeof(WorkItem));
+  ra.entries = (const ReduceItem*)((const uint8_t*)meta_dev + P.reduce_offset());
+  ra.meta = (const MetaHeader*)meta_dev;
+  ra.tag_lo = (uint32_t)P.serial;
+  ra.tag_hi = (uint32_t)(P.serial >> 32);
   ra.QL = P.prob.query_len;
   ra.Hq = P.prob.num_q_heads;
   ra.G = P.prob.num_q_heads / P.prob.num_kv_heads;

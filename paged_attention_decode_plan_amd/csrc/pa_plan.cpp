@@ -3,18 +3,22 @@
 // Split-KV planning follows the FlyDSL decode pages: partitions per
 // (sequence, KV head) are bounded by the device compute-unit count and a
 // static 256-partition limit (aiter PR #4332, the commit that defaults the
-// per-sequence plan limit to the CU count); the partition range is the tile
-// union a sliding window and multi-token (MTP) rows can see (aiter PR #6617,
-// "Size staged page IDs from the visible sliding-window tile union"); empty
+// per-sequence plan limit to the CU count); the partitioned range of a
+// sequence is the union of the tiles its query rows can see under a sliding
+// window and multi-token (MTP) rows, and the staged page ids cover only that
+// union (aiter PR #6617 "Extend packed D256 PA decode pipe", summary); empty
 // sequences clear their rows (aiter PR #7079, "Partition merges").
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <functional>
+#include <mutex>
 #include <queue>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "pa_internal.h"
@@ -26,6 +30,21 @@ static thread_local std::string g_last_error;
 pa_status set_error(pa_status st, const std::string& msg) {
   g_last_error = msg;
   return st;
+}
+
+static std::atomic<uint64_t> g_next_serial{1};
+static std::mutex g_registry_mutex;
+static std::unordered_map<const void*, uint64_t> g_registry;
+
+void meta_registry_set(const void* meta_dev, uint64_t serial) {
+  std::lock_guard<std::mutex> lock(g_registry_mutex);
+  g_registry[meta_dev] = serial;
+}
+
+bool meta_registry_holds(const void* meta_dev, uint64_t serial) {
+  std::lock_guard<std::mutex> lock(g_registry_mutex);
+  auto it = g_registry.find(meta_dev);
+  return it != g_registry.end() && it->second == serial;
 }
 
 pa_status validate_problem(const pa_problem* p) {
@@ -278,11 +297,15 @@ extern "C" pa_status pa_plan(const pa_problem* problem, const int32_t* context_l
     P.items.resize(P.budget_items, WorkItem{-1, 0, 0, 0, 0, -1, 0, 1});
     P.num_slots = std::max(P.num_slots, P.budget_items);
   }
-  P.meta_host.resize(P.items.size() * sizeof(WorkItem) + P.reduce.size() * sizeof(ReduceItem));
-  if (!P.items.empty()) std::memcpy(P.meta_host.data(), P.items.data(), P.items.size() * sizeof(WorkItem));
+  P.serial = g_next_serial.fetch_add(1);
+  P.meta_host.resize(P.reduce_offset() + P.reduce.size() * sizeof(ReduceItem));
+  const MetaHeader hdr{kMetaMagic, (uint32_t)P.serial, (uint32_t)(P.serial >> 32), (uint32_t)P.items.size(),
+                       (uint32_t)P.reduce.size(), 0, 0, 0};
+  std::memcpy(P.meta_host.data(), &hdr, sizeof hdr);
+  if (!P.items.empty())
+    std::memcpy(P.meta_host.data() + P.items_offset(), P.items.data(), P.items.size() * sizeof(WorkItem));
   if (!P.reduce.empty())
-    std::memcpy(P.meta_host.data() + P.items.size() * sizeof(WorkItem), P.reduce.data(),
-                P.reduce.size() * sizeof(ReduceItem));
+    std::memcpy(P.meta_host.data() + P.reduce_offset(), P.reduce.data(), P.reduce.size() * sizeof(ReduceItem));
   *out = handle;
   return PA_OK;
 }
@@ -316,6 +339,33 @@ extern "C" pa_status pa_plan_work(const pa_plan_t* plan, int32_t* out, int32_t n
   return PA_OK;
 }
 
-extern "C" void pa_plan_free(pa_plan_t* plan) { delete plan; }
+extern "C" pa_status pa_plan_upload(const pa_plan_t* plan, void* meta_dev, void* stream) {
+  if (!plan) return set_error(PA_ERR_INVALID, "plan is NULL");
+  if (!meta_dev) return set_error(PA_ERR_WORKSPACE, "meta_dev is NULL");
+  if (((uintptr_t)meta_dev & 15) != 0) return set_error(PA_ERR_INVALID, "meta_dev must be 16-byte aligned");
+  const Plan& P = plan->plan;
+  if (!P.meta_pinned) {
+    // a pinned source keeps the copy asynchronous (and capturable in a graph)
+    void* h = nullptr;
+    if (hipHostMalloc(&h, P.meta_host.size(), hipHostMallocDefault) != hipSuccess || !h) {
+      (void)hipGetLastError();
+      return set_error(PA_ERR_DEVICE, "pinned host buffer for the metadata could not be allocated");
+    }
+    std::memcpy(h, P.meta_host.data(), P.meta_host.size());
+    P.meta_pinned = (uint8_t*)h;
+  }
+  if (hipMemcpyAsync(meta_dev, P.meta_pinned, P.meta_host.size(), hipMemcpyHostToDevice, (hipStream_t)stream) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return set_error(PA_ERR_DEVICE, "metadata upload failed");
+  }
+  meta_registry_set(meta_dev, P.serial);
+  return PA_OK;
+}
+
+extern "C" void pa_plan_free(pa_plan_t* plan) {
+  if (plan && plan->plan.meta_pinned) (void)hipHostFree(plan->plan.meta_pinned);
+  delete plan;
+}
 
 extern "C" const char* pa_last_error(void) { return g_last_error.c_str(); }

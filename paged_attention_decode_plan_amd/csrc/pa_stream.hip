@@ -103,6 +103,8 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   const int h = lane >> 5;
 
   const WorkItem it = a.items[blockIdx.x];
+  const MetaHeader mh = *a.meta;
+  if (!meta_ok(mh, a.tag_lo, a.tag_hi)) return;  // not this plan's list: touch nothing
   if (it.seq < 0) return;  // an unused item of a refreshable plan
   const int s = it.seq, kvh = it.kvh, rg = it.rg;
   const int ps = a.page_size;

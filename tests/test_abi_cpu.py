@@ -77,6 +77,13 @@ def test_decode_error_paths_without_launch():
     args[6] = 0x7000
     args[9] = None  # meta_dev
     assert L.pa_decode(plan.handle, *args) == B.PA_ERR_WORKSPACE
+    args[9] = 0x9000  # never filled by pa_plan_upload for this plan
+    assert L.pa_decode(plan.handle, *args) == B.PA_ERR_WORKSPACE
+    assert b"pa_plan_upload" in L.pa_last_error()
+    assert L.pa_reduce(plan.handle, 0x1000, None, 0x9000, 0xA000, None) in (B.PA_OK, B.PA_ERR_WORKSPACE)
+    assert L.pa_plan_upload(None, 0x9000, None) == B.PA_ERR_INVALID
+    assert L.pa_plan_upload(plan.handle, None, None) == B.PA_ERR_WORKSPACE
+    assert L.pa_plan_upload(plan.handle, 0x9008, None) == B.PA_ERR_INVALID  # misaligned
     assert L.pa_reduce(None, None, None, None, None, None) == B.PA_ERR_INVALID
     assert L.pa_plan_sizes(None, None, None) == B.PA_ERR_INVALID
 
@@ -188,7 +195,7 @@ def test_plan_row_groups():
 def test_plan_zero_sequences():
     prob = _prob(num_seqs=0)
     plan = B.Plan(prob, [], cu_count=8)
-    assert plan.info().num_items == 0 and plan.meta_bytes == 0
+    assert plan.info().num_items == 0 and plan.meta_bytes == 32  # the header only
 
 
 def test_refreshable_plan_layout():
@@ -209,3 +216,19 @@ def test_refreshable_plan_layout():
     plain = B.Plan(prob, lens, cu_count=32)
     with pytest.raises(ValueError):
         B._check(B.load_library().pa_plan_refresh(plain.handle, None, None, None))
+
+
+def test_shared_meta_buffer_is_refused_without_upload():
+    """Two plans and one meta_dev on a host without a GPU: the upload fails
+    with PA_ERR_DEVICE and registers nothing, so both plans are refused with
+    PA_ERR_WORKSPACE before any launch (the GPU test of the same name covers
+    a successful upload followed by the other plan's)."""
+    L = B.load_library()
+    a = B.Plan(_prob(), [37, 100], cu_count=256)
+    b = B.Plan(_prob(), [100, 37], cu_count=256)
+    buf = 0x10000
+    st = L.pa_plan_upload(a.handle, buf, None)
+    assert st == B.PA_ERR_DEVICE  # no device here: nothing was copied, nothing registered
+    args = [0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000, 0x8000, None, buf, 0xA000, None]
+    for plan in (a, b):
+        assert L.pa_decode(plan.handle, *args) == B.PA_ERR_WORKSPACE

@@ -325,7 +325,7 @@ def test_graph_replay_with_changing_lengths(kind):
     out = torch.empty_like(dev["q"])
     args = (dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], cl, dev["k_scale"], dev["v_scale"], None)
     cl.copy_(torch.tensor(planned, dtype=torch.int32))
-    B.attend(plan, out, *args)  # first call: uploads the plan metadata
+    B.attend(plan, out, *args)  # an eager call before the capture
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
@@ -353,7 +353,7 @@ def _check_device_work_list(plan, inp, lens, host_max_len):
     no longer than the host planner's for the same lengths."""
     p = inp.problem
     n = plan.info().num_items
-    items = plan.meta[: n * 32].view(torch.int32).view(n, 8).cpu().numpy()
+    items = plan.work_list_device().cpu().numpy()
     used = items[items[:, 0] >= 0]
     slots = used[used[:, 5] >= 0, 5]
     assert len(set(slots.tolist())) == len(slots) and (slots < plan.info().num_slots).all()
@@ -528,3 +528,42 @@ def test_clamped_lengths(kind):
     announce(f"clamped lengths {kind} cap={cap}")
     got, _ = run(wild, cu_count=64)
     compare(got, O.attend(wild), f"clamped lengths {kind}")
+
+
+def test_shared_meta_buffer():
+    """Two plans sharing one metadata buffer: after plan B's upload, plan A is
+    refused (its list is no longer there) until it uploads again; a buffer
+    whose header no longer holds the plan's serial (reallocated or
+    overwritten) makes the kernels do nothing, so the NaN-poisoned output
+    stays untouched instead of following a foreign list."""
+    inp_a = W.make_dense_case(181, [700, 300], query_len=4, num_q_heads=16, num_kv_heads=1, page_size=64,
+                              scale_mode="token")
+    inp_b = W.make_dense_case(182, [3000, 20, 900], query_len=1, num_q_heads=8, num_kv_heads=1, page_size=16,
+                              scale_mode="tensor")
+    da, db = to_device(inp_a), to_device(inp_b)
+    pa = B.Plan(B.problem_of(inp_a.problem), inp_a.context_lens, cu_count=64)
+    pb = B.Plan(B.problem_of(inp_b.problem), inp_b.context_lens, cu_count=64)
+    buf = torch.empty(max(pa.meta_bytes, pb.meta_bytes), dtype=torch.uint8, device="cuda")
+    for p_ in (pa, pb):
+        p_.meta = buf
+        p_.workspace = torch.full((max(p_.workspace_bytes // 4, 4),), float("nan"), device="cuda")
+
+    def call(plan, inp, d):
+        out = torch.full_like(d["q"], float("nan"))
+        B.attend(plan, out, d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"], d["k_scale"],
+                 d["v_scale"], d["sinks"])
+        torch.cuda.synchronize()
+        return out.float().cpu().numpy()
+
+    announce("shared meta buffer")
+    pa.upload()
+    compare(call(pa, inp_a, da), O.attend(inp_a), "plan A")
+    pb.upload()
+    compare(call(pb, inp_b, db), O.attend(inp_b), "plan B")
+    with pytest.raises(ValueError, match="pa_plan_upload"):
+        call(pa, inp_a, da)
+    pa.upload()
+    compare(call(pa, inp_a, da), O.attend(inp_a), "plan A again")
+    buf[:32].zero_()  # the header no longer names plan A
+    got = call(pa, inp_a, da)
+    assert np.isnan(got).all(), "kernels followed a list whose header is not the plan's"
