@@ -216,6 +216,26 @@ pa_status pa_reduce(const pa_plan_t* plan, void* out, const float* sinks, void* 
  */
 pa_status pa_plan_refresh(const pa_plan_t* plan, const int32_t* context_lens, void* meta_dev, void* stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): pa_decode
+ * followed by pa_reduce, with the plan metadata and the partial states kept
+ * in a static device array of this library instead of meta_dev and
+ * workspace_dev.  Each GPU holds its own array of PA_STATIC_SCRATCH_BYTES
+ * until the process ends; a plan needing more (its meta_bytes rounded up to
+ * 256, plus workspace_bytes) is refused with PA_ERR_WORKSPACE.  No call
+ * allocates: the metadata is copied into the array (asynchronously on
+ * `stream`, from the plan's pinned copy when pa_plan_upload made one) only
+ * when the array does not already hold this plan's.  All calls on one GPU
+ * share the array and it keeps the last call's contents: calls that overlap
+ * on one GPU (other streams, other threads) race.  The other arguments and
+ * errors are those of pa_decode.
+ */
+#define PA_STATIC_SCRATCH_BYTES (32u << 20)
+pa_status pa_attend_static(const pa_plan_t* plan, void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, const float* k_scale,
+                           const float* v_scale, const float* sinks, void* stream);
+
 /* Thread-local message for the last non-OK status of this thread. */
 const char* pa_last_error(void);
 

@@ -24,7 +24,8 @@ PA_V_PLAIN, PA_V_TRANSPOSED = range(2)
 PA_SCALE_NONE, PA_SCALE_PER_TENSOR, PA_SCALE_PER_TOKEN = range(3)
 
 EXPORTS = ["pa_plan", "pa_plan_sizes", "pa_plan_info", "pa_plan_work", "pa_plan_upload", "pa_plan_free", "pa_decode",
-           "pa_reduce", "pa_plan_refresh", "pa_last_error"]
+           "pa_reduce", "pa_plan_refresh", "pa_attend_static", "pa_last_error"]
+STATIC_SCRATCH_BYTES = 32 << 20  # PA_STATIC_SCRATCH_BYTES of include/pa_decode.h
 META_HEADER_BYTES = 32  # meta_dev starts with the plan's header; the work list follows
 
 
@@ -76,6 +77,8 @@ def load_library(path: str = LIB_PATH):
     L.pa_reduce.argtypes = [vp] * 6
     L.pa_plan_refresh.restype = ctypes.c_int
     L.pa_plan_refresh.argtypes = [vp] * 4
+    L.pa_attend_static.restype = ctypes.c_int
+    L.pa_attend_static.argtypes = [vp] * 11
     L.pa_last_error.restype = ctypes.c_char_p
     L.pa_last_error.argtypes = []
     _lib = L
@@ -181,19 +184,7 @@ def _stream_ptr(stream):
 
 def pa_decode(plan: Plan, out, q, k_cache, v_cache, block_tables, context_lens, k_scale=None, v_scale=None,
               sinks=None, stream=None):
-    for name, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
-                    ("block_tables", block_tables), ("context_lens", context_lens)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a device tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise ValueError("block_tables and context_lens must be int32")
-    if out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("out must match q in shape and dtype")
-    for name, t in (("k_scale", k_scale), ("v_scale", v_scale), ("sinks", sinks)):
-        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda):
-            raise ValueError(f"{name} must be a contiguous float32 device tensor")
+    _check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale, sinks)
     if plan.meta is None:
         plan.allocate(q.device)
     _check(load_library().pa_decode(plan.handle, _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
@@ -213,6 +204,34 @@ def pa_plan_refresh(plan: Plan, context_lens, stream=None):
     if plan.meta is None:
         plan.allocate(context_lens.device)
     _check(load_library().pa_plan_refresh(plan.handle, _ptr(context_lens), _ptr(plan.meta), _stream_ptr(stream)))
+
+
+def _check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale, sinks):
+    for name, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_tables", block_tables), ("context_lens", context_lens)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale), ("sinks", sinks)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda):
+            raise ValueError(f"{name} must be a contiguous float32 device tensor")
+
+
+def pa_attend_static(plan: Plan, out, q, k_cache, v_cache, block_tables, context_lens, k_scale=None, v_scale=None,
+                     sinks=None, stream=None):
+    """pa_decode + pa_reduce with the metadata and partials in the library's
+    static device array (no device allocation; plan.meta / plan.workspace
+    are not used)."""
+    _check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale, sinks)
+    _check(load_library().pa_attend_static(plan.handle, _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                           _ptr(block_tables), _ptr(context_lens), _ptr(k_scale), _ptr(v_scale),
+                                           _ptr(sinks), _stream_ptr(stream)))
+    return out
 
 
 def attend(plan: Plan, out, q, k_cache, v_cache, block_tables, context_lens, k_scale=None, v_scale=None, sinks=None,
