@@ -13,7 +13,12 @@ Hkv 1, head dim 128, 4 causal query rows, page 128, lengths uniform in
   finds its KV in the 256 MB Infinity Cache;
 * roofline: the decode kernel's algorithmic bytes over its own average
   duration, timed the same way with the decode launches alone, against 8 TB/s;
-* cpu_baseline: the CPU oracle on a bounded sample of the same workload.
+* cpu_baseline: the CPU oracle on a bounded sample of the same workload;
+* workloads: the same measurement (cold and warm us per call, KV GB/s, the
+  decode launch's roofline fraction where the shape is HBM-bound) for every
+  other configuration: the tiny, sparse, long-context D256 (with and without
+  its window), ragged and dense BF16 batches, the MTP2 shape and the pages'
+  own MI355X shape (B200, MTP4, 200 000-token contexts).  --only skips them.
 """
 
 from __future__ import annotations
@@ -47,11 +52,21 @@ WORKLOADS = {
     "sparse": "sparse decode: 64 rows Hq16/Hkv1 D128 page16, 2048 of 65536 slots, per-token, 4 partitions",
     "tiny": "tiny decode: B2 Hq8/Hkv1 D128 QL1 page16 L=37,100, per-tensor, one partition",
 }
+# Measured after the headline line by default, into its "workloads" object.
+EXTRA_WORKLOADS = ["tiny", "sparse", "long_d256", "long_d256_nowindow", "ragged", "dense_mtp4_bf16", "dense_mtp2_fp8",
+                   "long_mtp4_c200k"]
+# Shapes whose time is HBM streaming of the KV bytes (a roofline claim); the
+# tiny and ragged batches are latency-bound and the sparse batch is a gather
+# from a pool that stays in the 256 MB Infinity Cache: for those the
+# bandwidth figure is an effective rate, not a roofline fraction.
+ROOFLINE_CLAIM = {"dense_mtp4_fp8", "dense_mtp4_bf16", "dense_mtp2_fp8", "long_d256", "long_d256_nowindow",
+                  "long_mtp4_c200k"}
 
 
 # The pages' own MI355X figure for a workload, where they give one: the
 # achieved KV bandwidth of aiter PR #4332 for B200 / MTP4 / C=200k at five
-# partitions per sequence (KV and scales counted once per call).
+# partitions per sequence (KV and scales counted once per call).  Context
+# only: another machine's run, never a baseline of this one.
 PAGES_GBPS = {"long_mtp4_c200k": 5163.9}
 
 
@@ -59,30 +74,40 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def load_traffic(workload: str, launches_kv_bytes: float):
-    """HBM bytes per decode launch from committed rocprofv3 counter runs, if
-    they were taken on the current kernel source."""
+def _profile_json(workload: str, kind: str):
+    """A committed rocprofv3 summary for the workload, if it was taken on the
+    current kernel source."""
     import glob
 
-    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}_traffic.json"))):
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}_{kind}.json"))):
         with open(path) as f:
             t = json.load(f)
         if t.get("kernel_sha") == source_sha():
-            return t.get("hbm_bytes_per_launch")
+            return t
     return None
+
+
+def load_traffic(workload: str):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs."""
+    t = _profile_json(workload, "traffic")
+    return None if t is None else t.get("hbm_bytes_per_launch")
 
 
 def load_mfma(workload: str):
-    """MFMA busy fraction of the decode kernel from a committed rocprofv3
-    counter run, if it was taken on the current kernel source."""
-    import glob
+    """MFMA busy fraction of the decode kernel from a committed counter run."""
+    t = _profile_json(workload, "mfma")
+    return None if t is None else round(t.get("mfma_busy_fraction"), 4)
 
-    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}_mfma.json"))):
-        with open(path) as f:
-            t = json.load(f)
-        if t.get("kernel_sha") == source_sha():
-            return round(t.get("mfma_busy_fraction"), 4)
-    return None
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def make_inputs(workload: str):
@@ -132,33 +157,32 @@ def cpu_baseline(inp, budget_s: float = 12.0):
         if t_used >= budget_s:
             break
     gbps = done_bytes / t_used / 1e9 if t_used > 0 else 0.0
-    return {"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"all {p.query_len * p.num_q_heads} (row, head) outputs of the {done_seqs} shortest "
                       f"sequences of the workload ({done_bytes / 1e6:.1f} MB of KV) in {t_used:.1f} s"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="dense_mtp4_fp8", choices=sorted(WORKLOADS))
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="run one device-to-device copy of MIB MiB first (counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this decode engine runs on a single MI355X; "
-              "--gpus above 1 is not supported", file=sys.stderr)
-        sys.exit(1)
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda:0")
+def kernel_of(p, info) -> str:
+    """Which decode kernel the library launches for a plan (its dispatch rule)."""
+    if p.kv_dtype == "fp8" and p.head_dim == 128 and not p.token_table and info.rows_per_group > 16:
+        return "pa_stream_kernel"
+    return "pa_decode_kernel"
+
+
+def measure(workload: str, steps: int, warmup: int, dev):
+    """Time pa_decode + pa_reduce calls of one workload with its inputs
+    resident in HBM.  Timing: one pair of HIP events on the launch stream
+    around a region of K calls, divided by K (events around every launch
+    would add their own dispatch overhead to each call).  Warm: K calls on
+    one copy of the inputs.  Cold: the calls rotate over three copies of the
+    KV caches and scales at different addresses (3x the KV bytes, past the
+    256 MB Infinity Cache), so each call reads KV that the two calls before it
+    have evicted; a workload whose KV alone is far larger than that cache
+    (drawn on the device) uses one copy.  Decode: the cold region with the
+    decode launches alone."""
     t_gen = time.perf_counter()
-    inp, plan_kw = make_inputs(args.workload)
-    log(f"inputs {args.workload} built in {time.perf_counter() - t_gen:.1f}s")
+    inp, plan_kw = make_inputs(workload)
+    log(f"inputs {workload} built in {time.perf_counter() - t_gen:.1f}s")
     p = inp.problem
     d = {k: (None if v is None else v.to(dev).contiguous()) for k, v in dict(
         q=inp.q, k=inp.k_cache, v=inp.v_cache, bt=inp.block_tables, cl=inp.context_lens, ks=inp.k_scale,
@@ -168,37 +192,12 @@ def main():
     out = torch.empty_like(d["q"])
     stream = torch.cuda.current_stream()
     kv_bytes = W.kv_bytes_visible(inp)
-
-    def step():
-        B.pa_decode(plan, out, d["q"], d["k"], d["v"], d["bt"], d["cl"], d["ks"], d["vs"], d["sk"], stream)
-        B.pa_reduce(plan, out, d["sk"], stream)
-
-    if args.copy_calibration > 0:
-        n = args.copy_calibration << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        log(f"calibration copy: {n} bytes read, {n} bytes written")
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    assert torch.isfinite(out.float()).all(), "non-finite output"
-
-    # Timing: one pair of HIP events around a region of K launches on the
-    # launch stream, divided by K (events around every launch would add their
-    # own dispatch overhead to each call).  Warm: K calls on one copy of the
-    # inputs.  Cold: the calls rotate over three copies of the KV caches and
-    # scales at different addresses (3x the KV bytes, well past the 256 MB
-    # Infinity Cache), so each call reads KV that the two calls before it
-    # have evicted.
-    K = args.steps
+    on_device = inp.k_cache.is_cuda
     copies = [(d["k"], d["v"], d["ks"], d["vs"])]
-    for _ in range(2):
-        copies.append(tuple(None if t is None else t.clone() for t in copies[0]))
+    if not on_device:
+        for _ in range(2):
+            copies.append(tuple(None if t is None else t.clone() for t in copies[0]))
+    nc = len(copies)
 
     def call(c, reduce=True):
         kc, vc, ksc, vsc = copies[c]
@@ -210,54 +209,219 @@ def main():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
-        for k in range(K):
+        for k in range(steps):
             body(k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    for k in range(max(warmup, nc)):
+        call(k % nc)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all(), f"{workload}: non-finite output"
+    t_start = time.perf_counter()
+    us_warm = region(lambda k: call(0))
+    us_cold = region(lambda k: call(k % nc))
+    dec_us = region(lambda k: call(k % nc, reduce=False))
+    timed_wall = time.perf_counter() - t_start
+    res = {
+        "description": WORKLOADS[workload],
+        "kernel": kernel_of(p, info),
+        "kv_bytes_per_call": kv_bytes,
+        "us_per_call_cold": round(us_cold, 2),
+        "us_per_call_warm": round(us_warm, 2),
+        "decode_us_cold": round(dec_us, 2),
+        "gbps_cold": round(kv_bytes / (us_cold * 1e-6) / 1e9, 1),
+        "gbps_warm": round(kv_bytes / (us_warm * 1e-6) / 1e9, 1),
+        "decode_gbps_cold": round(kv_bytes / (dec_us * 1e-6) / 1e9, 1),
+        "roofline_claim": workload in ROOFLINE_CLAIM,
+        "work_items": info.num_items,
+        "partials": info.num_slots,
+        "cu_count": info.cu_count,
+        "cold_copies": nc,
+        "wall_s_timed_regions": round(timed_wall, 3),
+    }
+    if workload in ROOFLINE_CLAIM:
+        res["decode_frac"] = round(kv_bytes / (dec_us * 1e-6) / 1e9 / PEAK_GBPS, 4)
+        res["traffic"] = load_traffic(workload)
+        res["mfma_busy_fraction"] = load_mfma(workload)
+    if workload in PAGES_GBPS:
+        res["pages_gbps_context"] = {"value": PAGES_GBPS[workload],
+                                     "note": "the pages' own MI355X figure for this shape (aiter PR #4332); "
+                                             "another machine's run, context only"}
+    del copies, d, plan, out
+    torch.cuda.empty_cache()
+    return res, inp
+
+
+def ceiling(args, dev):
+    """What the memory system gives for the decode's access pattern: the
+    read-only probes of libpa_ceiling.so over the dense MTP4 FP8 batch's own
+    pages and work list (the streaming kernel's register loads; the same
+    bytes through an LDS ring), the decode launch itself, and a plain read of
+    a contiguous 2 GiB buffer, timed alike (cold: three rotating copies of the
+    caches).  Prints one JSON line."""
+    import ctypes
+
+    from paged_attention_decode_plan_amd.build import CEILING_LIB
+
+    if not os.path.exists(CEILING_LIB):
+        raise SystemExit(f"{CEILING_LIB} not built (paged_attention_decode_plan_amd.build)")
+    C = ctypes.CDLL(CEILING_LIB)
+    vp = ctypes.c_void_p
+    C.pa_ceiling_gather.restype = ctypes.c_int
+    C.pa_ceiling_gather.argtypes = [ctypes.c_int] + [vp] * 7 + [ctypes.c_int, vp] + [ctypes.c_int] * 3 + [vp]
+    C.pa_ceiling_read.restype = ctypes.c_int
+    C.pa_ceiling_read.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_int, vp]
+    inp, plan_kw = make_inputs("dense_mtp4_fp8")
+    p = inp.problem
+    d = {k: v.to(dev).contiguous() for k, v in dict(q=inp.q, k=inp.k_cache, v=inp.v_cache, bt=inp.block_tables,
+                                                       cl=inp.context_lens, ks=inp.k_scale, vs=inp.v_scale).items()}
+    plan = B.Plan(B.problem_of(p), inp.context_lens, **plan_kw).allocate(dev)
+    items = plan.work_list_device()
+    n = items.shape[0]
+    out = torch.empty(n * 256, dtype=torch.int32, device=dev)
+    qout = torch.empty_like(d["q"])
+    copies = [(d["k"], d["v"], d["ks"], d["vs"])] + [tuple(t.clone() for t in (d["k"], d["v"], d["ks"], d["vs"]))
+                                                      for _ in range(2)]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    kv_bytes = W.kv_bytes_visible(inp)
+
+    def probe(mode, c):
+        kc, vc, ksc, vsc = copies[c]
+        st = C.pa_ceiling_gather(mode, kc.data_ptr(), vc.data_ptr(), ksc.data_ptr(), vsc.data_ptr(),
+                                 d["bt"].data_ptr(), d["cl"].data_ptr(), items.data_ptr(), n, out.data_ptr(),
+                                 p.num_kv_heads, p.page_size, p.table_stride, sp)
+        assert st == 0, f"probe mode {mode}: status {st}"
+
+    def decode(c):
+        kc, vc, ksc, vsc = copies[c]
+        B.pa_decode(plan, qout, d["q"], kc, vc, d["bt"], d["cl"], ksc, vsc, None, stream)
+
+    def region(body, K):
+        for k in range(3):
+            body(k % 3)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for k in range(K):
+            body(k % 3)
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / K
 
-    t_start = time.perf_counter()
-    us_warm = region(lambda k: call(0))
-    for k in range(3):
-        call(k)  # first touch of every copy
-    us_cold = region(lambda k: call(k % 3))
-    dec_us = region(lambda k: call(k % 3, reduce=False))
-    timed_wall = time.perf_counter() - t_start
+    K = args.steps
+    res = {"metric": "read bandwidth of the decode's KV access pattern (ceiling probes)", "workload": "dense_mtp4_fp8",
+           "kv_bytes_per_call": kv_bytes, "work_items": n, "steps": K, "kernel_sha": source_sha()}
+    rounds = {"registers": [], "lds_ring": [], "decode": []}
+    for _ in range(3):  # interleaved rounds, best of three
+        rounds["registers"].append(region(lambda c: probe(0, c), K))
+        rounds["lds_ring"].append(region(lambda c: probe(1, c), K))
+        rounds["decode"].append(region(decode, K))
+    for name, v in rounds.items():
+        us = min(v)
+        res[name] = {"us": round(us, 2), "gbps": round(kv_bytes / (us * 1e-6) / 1e9, 1),
+                     "frac": round(kv_bytes / (us * 1e-6) / 1e9 / PEAK_GBPS, 4), "rounds_us": [round(x, 2) for x in v]}
     del copies
-    achieved = kv_bytes / (dec_us * 1e-6) / 1e9
-    traffic = load_traffic(args.workload, kv_bytes)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic}
+    torch.cuda.empty_cache()
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    best = None
+    for grid in (1024, 2048, 4096, 8192):
+        rout = torch.empty(grid * 256, dtype=torch.int32, device=dev)
+        us = region(lambda c: C.pa_ceiling_read(buf.data_ptr(), nbytes, rout.data_ptr(), grid, sp), max(5, K // 4))
+        gbps = nbytes / (us * 1e-6) / 1e9
+        res.setdefault("plain_read", {})[str(grid)] = round(gbps, 1)
+        best = gbps if best is None else max(best, gbps)
+    res["plain_read_best_gbps"] = round(best, 1)
+    print(json.dumps(res), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dense_mtp4_fp8", choices=sorted(WORKLOADS))
+    ap.add_argument("--only", action="store_true", help="measure the chosen workload alone (no workloads object)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--ceiling", action="store_true",
+                    help="run the read-only bandwidth probes of the decode's access pattern instead")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run one device-to-device copy of MIB MiB first (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this decode engine runs on a single MI355X; "
+              "--gpus above 1 is not supported", file=sys.stderr)
+        sys.exit(1)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.ceiling:
+        ceiling(args, dev)
+        return
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"calibration copy: {n} bytes read, {n} bytes written")
+
+    head, inp = measure(args.workload, args.steps, args.warmup, dev)
+    p = inp.problem
     on_device = inp.k_cache.is_cuda  # too large for the host oracle's timing loop
     cpu = None if (args.no_cpu or on_device) else cpu_baseline(inp, args.cpu_budget)
-    gbps = kv_bytes / (us_cold * 1e-6) / 1e9
+    del inp
+    kv_bytes = head["kv_bytes_per_call"]
+    achieved = head["decode_gbps_cold"]
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_GBPS, 4), "traffic": load_traffic(args.workload)}
+    extra = {}
+    if not args.only:
+        for wl in EXTRA_WORKLOADS:
+            if wl == args.workload:
+                continue
+            r, _ = measure(wl, args.steps, args.warmup, dev)
+            extra[wl] = r
+            log(f"{wl}: {r['us_per_call_cold']} us cold, {r['gbps_cold']} GB/s")
     res = {
         "metric": "achieved HBM GB/s of KV bytes (and us/call), FP8 paged decode",
-        "value": round(gbps, 1),
+        "value": head["gbps_cold"],
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(us_cold / 1e3, 5),
+        "ms_per_step": round(head["us_per_call_cold"] / 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(gbps / PAGES_GBPS[args.workload], 4) if args.workload in PAGES_GBPS else None,
+        "vs_baseline": None,
         "dtype": "f16" if p.kv_dtype == "fp8" else "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "description": WORKLOADS[args.workload],
-                   "kv_bytes_per_call": kv_bytes, "work_items": info.num_items, "partials": info.num_slots,
-                   "cu_count": info.cu_count},
-        "us_per_call_cold": round(us_cold, 2),
-        "us_per_call_warm": round(us_warm, 2),
-        "decode_us_cold": round(dec_us, 2),
-        "warm_gbps": round(kv_bytes / (us_warm * 1e-6) / 1e9, 1),
-        "frac_of_peak_cold": round(gbps / PEAK_GBPS, 4),
-        "wall_s_timed_regions": round(timed_wall, 3),
+                   "kv_bytes_per_call": kv_bytes, "work_items": head["work_items"], "partials": head["partials"],
+                   "cu_count": head["cu_count"]},
+        "us_per_call_cold": head["us_per_call_cold"],
+        "us_per_call_warm": head["us_per_call_warm"],
+        "decode_us_cold": head["decode_us_cold"],
+        "warm_gbps": head["gbps_warm"],
+        "frac_of_peak_cold": round(head["gbps_cold"] / PEAK_GBPS, 4),
+        "wall_s_timed_regions": head["wall_s_timed_regions"],
         "roofline": roofline,
         "mfma_busy_fraction": load_mfma(args.workload),
         "cpu_baseline": cpu,
+        "kernel": head["kernel"],
         "kernel_sha": source_sha(),
     }
+    if args.workload in PAGES_GBPS:
+        res["pages_gbps_context"] = head["pages_gbps_context"]
+    if extra:
+        res["workloads"] = extra
     print(json.dumps(res), flush=True)
 
 

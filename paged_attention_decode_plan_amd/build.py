@@ -27,10 +27,28 @@ def source_sha() -> str:
     measured."""
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".cpp", ".h")):
+        if f in SOURCES or f.endswith(".h"):
             with open(os.path.join(CSRC, f), "rb") as fh:
                 h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
+
+
+CEILING_LIB = os.path.join(PKG, "libpa_ceiling.so")
+
+
+def build_ceiling(verbose: bool = False) -> str:
+    """The read-only bandwidth probes of bench.py --ceiling (a measurement
+    tool in a library of its own; libpa.so does not contain it)."""
+    tmp = CEILING_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, os.path.join(CSRC, "pa_ceiling.hip"), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libpa_ceiling.so")
+    os.replace(tmp, CEILING_LIB)
+    return CEILING_LIB
 
 
 def build_library(verbose: bool = False) -> str:
@@ -67,3 +85,4 @@ def build_library(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     print(build_library(verbose=True))
+    print(build_ceiling(verbose=True))
