@@ -40,6 +40,7 @@ from paged_attention_decode_plan_amd import workloads as W  # noqa: E402
 from paged_attention_decode_plan_amd.build import source_sha  # noqa: E402
 
 PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
+SETTLE_MS = 100.0  # untimed calls before the warm-up steps, so that the GPU clocks have settled
 WORKLOADS = {
     "dense_mtp4_fp8": "dense MTP4 verify, FP8 KV, per-token scales: B32 Hq16/Hkv1 D128 QL4 page128 L~U[16K,32K]",
     "dense_mtp4_bf16": "dense MTP4 verify, BF16 KV: B32 Hq16/Hkv1 D128 QL4 page128 L~U[16K,32K]",
@@ -215,6 +216,20 @@ def measure(workload: str, steps: int, warmup: int, dev):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / steps
 
+    # Clock settle: untimed calls for about SETTLE_MS of GPU time before the
+    # warm-up steps.  A GPU that was idle runs its first few hundred calls at
+    # lower clocks (20-call decode regions of the dense MTP4 batch measured
+    # back to back in a fresh process: 102, 54, 59, 61, 59, 57, 56, 55, 54,
+    # 53, 52.5, 52, 51.8, 51.4 us).
+    settle_ms = 0.0
+    while settle_ms < SETTLE_MS:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for k in range(20):
+            call(k % nc)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        settle_ms += e0.elapsed_time(e1)
     for k in range(max(warmup, nc)):
         call(k % nc)
     torch.cuda.synchronize()
@@ -239,6 +254,7 @@ def measure(workload: str, steps: int, warmup: int, dev):
         "partials": info.num_slots,
         "cu_count": info.cu_count,
         "cold_copies": nc,
+        "clock_settle_ms": round(settle_ms, 1),
         "wall_s_timed_regions": round(timed_wall, 3),
     }
     if workload in ROOFLINE_CLAIM:
@@ -412,6 +428,7 @@ def main():
         "warm_gbps": head["gbps_warm"],
         "frac_of_peak_cold": round(head["gbps_cold"] / PEAK_GBPS, 4),
         "wall_s_timed_regions": head["wall_s_timed_regions"],
+        "clock_settle_ms": head["clock_settle_ms"],
         "roofline": roofline,
         "mfma_busy_fraction": load_mfma(args.workload),
         "cpu_baseline": cpu,
