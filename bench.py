@@ -51,13 +51,15 @@ WORKLOADS = {
     "long_d256_nowindow": "supplementary: the long-context D256 batch with the window off (all 131072 tokens visible)",
     "ragged": "ragged batch: B128 Hkv4 GQA4 D128 QL1 page16 log-uniform L, window 257, sinks, per-token",
     "sparse": "sparse decode: 64 rows Hq16/Hkv1 D128 page16, 2048 of 65536 slots, per-token, 4 partitions",
+    "sparse_topk": "the sparse decode batch with two-level indices: 2048 top-k logical positions per row resolved "
+                   "through a 4096-page block table in the kernel, 4 partitions",
     "tiny": "tiny decode: B2 Hq8/Hkv1 D128 QL1 page16 L=37,100, per-tensor, one partition",
 }
 # Measured after the headline line by default, into its "workloads" object.
-EXTRA_WORKLOADS = ["tiny", "sparse", "long_d256", "long_d256_nowindow", "ragged", "dense_mtp4_bf16", "dense_mtp2_fp8",
-                   "long_mtp4_c200k"]
+EXTRA_WORKLOADS = ["tiny", "sparse", "sparse_topk", "long_d256", "long_d256_nowindow", "ragged", "dense_mtp4_bf16",
+                   "dense_mtp2_fp8", "long_mtp4_c200k"]
 # Shapes whose time is HBM streaming of the KV bytes (a roofline claim); the
-# tiny and ragged batches are latency-bound and the sparse batch is a gather
+# tiny and ragged batches are latency-bound and the sparse batches gather
 # from a pool that stays in the 256 MB Infinity Cache: for those the
 # bandwidth figure is an effective rate, not a roofline fraction.
 ROOFLINE_CLAIM = {"dense_mtp4_fp8", "dense_mtp4_bf16", "dense_mtp2_fp8", "long_d256", "long_d256_nowindow",
@@ -114,6 +116,8 @@ def cpu_model() -> str:
 def make_inputs(workload: str):
     if workload == "sparse":
         return W.config_sparse(), dict(partition_tokens=512)
+    if workload == "sparse_topk":
+        return W.config_sparse_topk(), dict(partition_tokens=512)
     if workload == "tiny":
         return W.config_tiny(), dict(max_partitions=1)
     if workload == "long_d256":
@@ -147,7 +151,8 @@ def cpu_baseline(inp, budget_s: float = 12.0):
         t0 = time.perf_counter()
         _, threads = O.attend(inp, sel=sel, return_threads=True)
         t_used += time.perf_counter() - t0
-        L = int(min(max(lens[s], 0), p.table_stride if p.token_table else p.table_stride * p.page_size))
+        cap = {0: p.table_stride * p.page_size, 1: p.table_stride, 2: p.index_stride}[p.token_table]
+        L = int(min(max(lens[s], 0), cap))
         if p.token_table:
             n = L
         else:
@@ -187,7 +192,7 @@ def measure(workload: str, steps: int, warmup: int, dev):
     p = inp.problem
     d = {k: (None if v is None else v.to(dev).contiguous()) for k, v in dict(
         q=inp.q, k=inp.k_cache, v=inp.v_cache, bt=inp.block_tables, cl=inp.context_lens, ks=inp.k_scale,
-        vs=inp.v_scale, sk=inp.sinks).items()}
+        vs=inp.v_scale, sk=inp.sinks, tk=inp.topk_indices).items()}
     plan = B.Plan(B.problem_of(p), inp.context_lens, **plan_kw).allocate(dev)
     info = plan.info()
     out = torch.empty_like(d["q"])
@@ -202,7 +207,10 @@ def measure(workload: str, steps: int, warmup: int, dev):
 
     def call(c, reduce=True):
         kc, vc, ksc, vsc = copies[c]
-        B.pa_decode(plan, out, d["q"], kc, vc, d["bt"], d["cl"], ksc, vsc, d["sk"], stream)
+        if p.token_table == 2:
+            B.pa_decode_sparse(plan, out, d["q"], kc, vc, d["bt"], d["tk"], d["cl"], ksc, vsc, d["sk"], stream)
+        else:
+            B.pa_decode(plan, out, d["q"], kc, vc, d["bt"], d["cl"], ksc, vsc, d["sk"], stream)
         if reduce:
             B.pa_reduce(plan, out, d["sk"], stream)
 

@@ -68,6 +68,12 @@ typedef enum { PA_SCALE_NONE = 0, PA_SCALE_PER_TENSOR = 1, PA_SCALE_PER_TOKEN = 
  * token_table = 1: block_tables[s][j] is a physical token slot
  *   (page * page_size + offset) of the j-th attended token and
  *   context_lens[s] counts them (sparse decode; query_len 1, no window).
+ * token_table = 2: the two-level sparse front end (pa_decode_sparse): row s
+ *   attends the logical positions topk[s][0..count_s) of its paged context,
+ *   each resolved through block_tables[s] (page = block_tables[s][P / page],
+ *   slot = P % page); positions outside [0, table_stride * page_size) are
+ *   clamped to it (never read outside the row; such a position attends the
+ *   clamped token).  query_len 1, no window.
  */
 typedef struct {
   int32_t num_seqs, query_len, num_q_heads, num_kv_heads, head_dim, page_size;
@@ -77,7 +83,8 @@ typedef struct {
   int32_t v_layout;   /* pa_v_layout */
   int32_t scale_mode; /* pa_scale_mode; FP8 needs PER_TENSOR or PER_TOKEN, BF16 needs NONE */
   int32_t causal, sliding_window, has_sinks, token_table;
-  float softmax_scale; /* <= 0: 1/sqrt(head_dim) */
+  float softmax_scale;  /* <= 0: 1/sqrt(head_dim) */
+  int32_t index_stride; /* token_table = 2: row stride of the top-k index table (pa_decode_sparse) */
 } pa_problem;
 
 typedef struct {
@@ -215,6 +222,21 @@ pa_status pa_reduce(const pa_plan_t* plan, void* out, const float* sinks, void* 
  * `refreshable`, PA_ERR_DEVICE for a launch error.
  */
 pa_status pa_plan_refresh(const pa_plan_t* plan, const int32_t* context_lens, void* meta_dev, void* stream);
+
+/*
+ * The sparse decode of aiter PR #7079 (summary and Performance setup: rows
+ * attending their top-k tokens of a paged context) with two-level indices,
+ * for plans of problems with token_table = 2: row s attends
+ * topk_indices[s][0..topk_counts[s]) (int32 logical positions, row stride
+ * index_stride), resolved through block_tables[s] (int32 page ids, row
+ * stride table_stride) to physical page slots.  Otherwise as pa_decode,
+ * followed by pa_reduce as usual.  PA_ERR_INVALID for a plan whose problem is
+ * not token_table = 2 (and pa_decode refuses those plans).
+ */
+pa_status pa_decode_sparse(const pa_plan_t* plan, void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* topk_indices, const int32_t* topk_counts,
+                           const float* k_scale, const float* v_scale, const float* sinks, void* meta_dev,
+                           void* workspace_dev, void* stream);
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph

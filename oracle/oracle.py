@@ -31,6 +31,7 @@ class OrcProblem(ctypes.Structure):
         ("q_kind", ctypes.c_int), ("kv_kind", ctypes.c_int), ("v_transposed", ctypes.c_int),
         ("scale_mode", ctypes.c_int), ("causal", ctypes.c_int), ("window", ctypes.c_int),
         ("has_sinks", ctypes.c_int), ("token_table", ctypes.c_int), ("softmax_scale", ctypes.c_double),
+        ("index_stride", ctypes.c_int), ("topk", ctypes.c_void_p),
     ]
 
 
@@ -80,12 +81,13 @@ def fp16_value(bits: int) -> float:
     return lib().orc_fp16(bits)
 
 
-def _problem(p) -> OrcProblem:
+def _problem(p, held=None) -> OrcProblem:
     return OrcProblem(
         p.num_seqs, p.query_len, p.num_q_heads, p.num_kv_heads, p.head_dim, p.page_size, p.num_pages,
         p.table_stride, 1 if p.q_dtype == "fp16" else 0, 2 if p.kv_dtype == "fp8" else 0, int(p.v_transposed),
         {"none": 0, "tensor": 1, "token": 2}[p.scale_mode], int(p.causal), int(p.sliding_window),
-        int(p.has_sinks), int(p.token_table), float(p.scale),
+        int(p.has_sinks), int(p.token_table), float(p.scale), int(getattr(p, "index_stride", 0)),
+        None if held is None else held.topk_ptr,
     )
 
 
@@ -104,6 +106,9 @@ class _Held:
         self.arrays = [c(inp.q), c(inp.k_cache), c(inp.v_cache), c(inp.block_tables), c(inp.context_lens),
                        c(inp.k_scale), c(inp.v_scale), c(inp.sinks)]
         self.ptrs = [None if a is None else a.ctypes.data for a in self.arrays]
+        topk = getattr(inp, "topk_indices", None)
+        self.topk = None if topk is None else np.ascontiguousarray(topk.cpu().numpy(), dtype=np.int32)
+        self.topk_ptr = None if self.topk is None else self.topk.ctypes.data
 
 
 def attend(inp, sel=None, nthreads: int | None = None, return_threads: bool = False):
@@ -111,8 +116,8 @@ def attend(inp, sel=None, nthreads: int | None = None, return_threads: bool = Fa
     for ``sel`` an int array of (token_row, head) pairs."""
     L = lib()
     p = inp.problem
-    prob = _problem(p)
     held = _Held(inp)
+    prob = _problem(p, held)
     if nthreads is None:
         nthreads = os.cpu_count() or 1
     if sel is None:
@@ -130,8 +135,8 @@ def partial(inp, s: int, i: int, h: int, t_begin: int, t_end: int):
     """Unnormalised (m, l, o[D]) of one row over visible tokens in [t_begin, t_end)."""
     L = lib()
     p = inp.problem
-    prob = _problem(p)
     held = _Held(inp)
+    prob = _problem(p, held)
     m = np.zeros(1, np.float64)
     l = np.zeros(1, np.float64)
     o = np.zeros(p.head_dim, np.float64)

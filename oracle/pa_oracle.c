@@ -25,7 +25,13 @@
  *
  * Token address: dense tables give page = block_tables[s][t / page_size],
  * slot = t mod page_size; token tables give a physical slot S =
- * block_tables[s][t], page = S / page_size, slot = S mod page_size.
+ * block_tables[s][t], page = S / page_size, slot = S mod page_size; top-k
+ * index tables (two-level, token_table = 2) give a logical position
+ * P = topk[s][t] of the sequence's paged context, clamped to the table's
+ * extent [0, table_stride * page_size), then page = block_tables[s][P /
+ * page_size], slot = P mod page_size (the sparse front end: top-k logical
+ * positions through the block table, aiter PR #7079, summary and Performance
+ * setup).  For token tables context_lens[s] counts the row's tokens.
  *
  * Layouts (x = 16 bytes / element size):
  *   K packed      [pages, Hkv, D/x, page, x]
@@ -60,6 +66,8 @@ typedef struct {
   int scale_mode;
   int causal, window, has_sinks, token_table;
   double softmax_scale;
+  int index_stride;    /* top-k index tables: row stride of topk */
+  const int32_t* topk; /* top-k index tables: logical positions [num_seqs][index_stride] */
 } orc_problem;
 
 /* ---- scalar format decoders (from the format definitions) ---- */
@@ -95,7 +103,9 @@ double orc_fp16(uint16_t h) {
 /* ---- addressing ---- */
 
 static int orc_clamped_len(const orc_problem* p, const int32_t* context_lens, int s) {
-  long cap = p->token_table ? (long)p->table_stride : (long)p->table_stride * p->page_size;
+  long cap = p->token_table == 2 ? (long)p->index_stride
+             : p->token_table    ? (long)p->table_stride
+                                 : (long)p->table_stride * p->page_size;
   long L = context_lens[s];
   if (L < 0) L = 0;
   if (L > cap) L = cap;
@@ -104,7 +114,14 @@ static int orc_clamped_len(const orc_problem* p, const int32_t* context_lens, in
 
 /* physical (page, slot) of logical token t of sequence s */
 static void orc_locate(const orc_problem* p, const int32_t* block_tables, int s, int t, long* page, int* slot) {
-  if (p->token_table) {
+  if (p->token_table == 2) {
+    long P = p->topk[(long)s * p->index_stride + t];
+    long extent = (long)p->table_stride * p->page_size;
+    if (P < 0) P = 0;
+    if (P > extent - 1) P = extent - 1;
+    *page = block_tables[(long)s * p->table_stride + P / p->page_size];
+    *slot = (int)(P % p->page_size);
+  } else if (p->token_table) {
     long S = block_tables[(long)s * p->table_stride + t];
     *page = S / p->page_size;
     *slot = (int)(S % p->page_size);

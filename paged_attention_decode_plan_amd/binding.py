@@ -24,7 +24,7 @@ PA_V_PLAIN, PA_V_TRANSPOSED = range(2)
 PA_SCALE_NONE, PA_SCALE_PER_TENSOR, PA_SCALE_PER_TOKEN = range(3)
 
 EXPORTS = ["pa_plan", "pa_plan_sizes", "pa_plan_info", "pa_plan_work", "pa_plan_upload", "pa_plan_free", "pa_decode",
-           "pa_reduce", "pa_plan_refresh", "pa_attend_static", "pa_last_error"]
+           "pa_reduce", "pa_plan_refresh", "pa_attend_static", "pa_decode_sparse", "pa_last_error"]
 STATIC_SCRATCH_BYTES = 32 << 20  # PA_STATIC_SCRATCH_BYTES of include/pa_decode.h
 META_HEADER_BYTES = 32  # meta_dev starts with the plan's header; the work list follows
 
@@ -33,7 +33,7 @@ class PaProblem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_seqs", "query_len", "num_q_heads", "num_kv_heads", "head_dim", "page_size", "num_pages",
         "table_stride", "q_dtype", "kv_dtype", "v_layout", "scale_mode", "causal", "sliding_window",
-        "has_sinks", "token_table")] + [("softmax_scale", ctypes.c_float)]
+        "has_sinks", "token_table")] + [("softmax_scale", ctypes.c_float), ("index_stride", ctypes.c_int32)]
 
 
 class PaPlanOpts(ctypes.Structure):
@@ -77,6 +77,8 @@ def load_library(path: str = LIB_PATH):
     L.pa_reduce.argtypes = [vp] * 6
     L.pa_plan_refresh.restype = ctypes.c_int
     L.pa_plan_refresh.argtypes = [vp] * 4
+    L.pa_decode_sparse.restype = ctypes.c_int
+    L.pa_decode_sparse.argtypes = [vp] * 14
     L.pa_attend_static.restype = ctypes.c_int
     L.pa_attend_static.argtypes = [vp] * 11
     L.pa_last_error.restype = ctypes.c_char_p
@@ -98,19 +100,21 @@ def _check(st: int):
 
 def make_problem(num_seqs, query_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages, table_stride,
                  q_dtype="bf16", kv_dtype="fp8", v_transposed=False, scale_mode="tensor", causal=True,
-                 sliding_window=0, has_sinks=False, token_table=False, softmax_scale=0.0) -> PaProblem:
+                 sliding_window=0, has_sinks=False, token_table=0, softmax_scale=0.0, index_stride=0) -> PaProblem:
     dt = {"bf16": PA_BF16, "fp16": PA_FP16, "fp8": PA_FP8_E4M3FN}
     sm = {"none": PA_SCALE_NONE, "tensor": PA_SCALE_PER_TENSOR, "token": PA_SCALE_PER_TOKEN}
     return PaProblem(num_seqs, query_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages, table_stride,
                      dt[q_dtype], dt[kv_dtype], PA_V_TRANSPOSED if v_transposed else PA_V_PLAIN, sm[scale_mode],
-                     int(causal), int(sliding_window), int(has_sinks), int(token_table), float(softmax_scale))
+                     int(causal), int(sliding_window), int(has_sinks), int(token_table), float(softmax_scale),
+                     int(index_stride))
 
 
 def problem_of(p) -> PaProblem:
     """PaProblem from any object with the problem's attribute names."""
     return make_problem(p.num_seqs, p.query_len, p.num_q_heads, p.num_kv_heads, p.head_dim, p.page_size,
                         p.num_pages, p.table_stride, p.q_dtype, p.kv_dtype, p.v_transposed, p.scale_mode, p.causal,
-                        p.sliding_window, p.has_sinks, p.token_table, p.softmax_scale)
+                        p.sliding_window, p.has_sinks, p.token_table, p.softmax_scale,
+                        getattr(p, "index_stride", 0))
 
 
 class Plan:
@@ -190,6 +194,22 @@ def pa_decode(plan: Plan, out, q, k_cache, v_cache, block_tables, context_lens, 
     _check(load_library().pa_decode(plan.handle, _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                     _ptr(block_tables), _ptr(context_lens), _ptr(k_scale), _ptr(v_scale),
                                     _ptr(sinks), _ptr(plan.meta), _ptr(plan.workspace), _stream_ptr(stream)))
+
+
+def pa_decode_sparse(plan: Plan, out, q, k_cache, v_cache, block_tables, topk_indices, topk_counts, k_scale=None,
+                     v_scale=None, sinks=None, stream=None):
+    """Two-level sparse decode: rows attend their top-k logical positions
+    (int32 [rows, index_stride], the first topk_counts[r] valid), resolved
+    through block_tables."""
+    _check_decode_args(out, q, k_cache, v_cache, block_tables, topk_counts, k_scale, v_scale, sinks)
+    if not topk_indices.is_cuda or not topk_indices.is_contiguous() or topk_indices.dtype != torch.int32:
+        raise ValueError("topk_indices must be a contiguous int32 device tensor")
+    if plan.meta is None:
+        plan.allocate(q.device)
+    _check(load_library().pa_decode_sparse(plan.handle, _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                           _ptr(block_tables), _ptr(topk_indices), _ptr(topk_counts), _ptr(k_scale),
+                                           _ptr(v_scale), _ptr(sinks), _ptr(plan.meta), _ptr(plan.workspace),
+                                           _stream_ptr(stream)))
 
 
 def pa_reduce(plan: Plan, out, sinks=None, stream=None):

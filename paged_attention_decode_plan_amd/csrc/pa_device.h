@@ -38,6 +38,7 @@ struct KernelArgs {
   const float* k_scale;
   const float* v_scale;
   const float* sinks;
+  const int32_t* topk;  // top-k logical positions (two-level sparse rows), else NULL
   const WorkItem* items;
   const MetaHeader* meta;  // header of the metadata buffer (items follow it)
   uint32_t tag_lo, tag_hi;  // the launching plan's serial: the header must hold it
@@ -45,7 +46,7 @@ struct KernelArgs {
   long long page_stride;  // bytes between physical pages (Hkv * D * page * elem)
   long long head_stride;  // bytes between KV heads of a page (D * page * elem)
   int QL, Hq, Hkv, G, page_size, table_stride, window, causal;
-  int v_transposed, scale_mode, q_fp16, has_sinks, rows_total, rows_per_group, stage_limit;
+  int v_transposed, scale_mode, q_fp16, has_sinks, rows_total, rows_per_group, stage_limit, index_stride;
   float scale_log2;  // softmax_scale * log2(e)
 };
 

@@ -134,7 +134,8 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   const int s = it.seq, kvh = it.kvh, rg = it.rg;
   const int ps = a.page_size;
   const int ps_log2 = 31 - __builtin_clz(ps);
-  const long cap = SPARSE ? (long)a.table_stride : (long)a.table_stride * ps;
+  // sparse rows: the row's slots (or, two-level, its top-k positions) count
+  const long cap = SPARSE ? (long)(a.topk ? a.index_stride : a.table_stride) : (long)a.table_stride * ps;
   const int L = (int)min(max((long)a.context_lens[s], 0L), cap);
 
   // Visible span of the sequence (union over its query rows).
@@ -183,6 +184,19 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   const long id_end = SPARSE ? (long)hi_u : ((long)hi_u + ps - 1) / ps;  // one past the last valid id
   const int nstaged = (int)max(0L, min((long)a.stage_limit, min((long)(te - tb) * ppt, id_end - id0)));
   const int32_t* bt_row = a.block_tables + (long)s * a.table_stride;
+  // Id j of the row from memory: a page id (dense), a physical token slot
+  // (sparse), or a top-k logical position resolved through the block table
+  // (two-level sparse: clamped to the table's extent, so the page id read
+  // stays in the row).
+  const int32_t* tk_row = (SPARSE && a.topk) ? a.topk + (long)s * a.index_stride : nullptr;
+  auto raw_id = [&](long j) -> long {
+    if (SPARSE && tk_row) {
+      const long P = min(max((long)tk_row[j], 0L), (long)a.table_stride * ps - 1);
+      return ((long)bt_row[P >> ps_log2] << ps_log2) + (P & (ps - 1));
+    }
+    return (long)bt_row[j];
+  };
+  const long id_rowlen = (SPARSE && tk_row) ? (long)a.index_stride : (long)a.table_stride;
   // ---- the item's first reads, issued before the query is prepared ----
   // The page ids (staged in LDS after the query split), the query rows'
   // raw bits and then the first tiles' DMA with page ids read straight from
@@ -192,7 +206,7 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
 #pragma unroll
   for (int j = 0; j < IDR; ++j) {
     const long k = min((long)(tid + NTHREADS * j), (long)max(nstaged - 1, 0));
-    idr[j] = bt_row[min(max(id0 + k, 0L), (long)a.table_stride - 1)];  // in the row whatever the item
+    idr[j] = (int32_t)raw_id(min(max(id0 + k, 0L), id_rowlen - 1));  // in the row whatever the item
   }
   constexpr int NQR = FP8 ? (D / 128) * 4 : D / 32;  // 16-byte query loads per row tile
   u32x4 qraw[NRW][NQR];
@@ -448,7 +462,7 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   // kept apart so the LDS-only path never emits a generic (flat) load, which
   // would make every DMA issue wait for all outstanding loads.
   auto staged_id = [&](long j) -> long { return (long)ids[j]; };
-  auto item_id = [&](long j) -> long { return j < nstaged ? (long)ids[j] : (long)bt_row[id0 + j]; };
+  auto item_id = [&](long j) -> long { return j < nstaged ? (long)ids[j] : raw_id(id0 + j); };
 
   auto issue_tile = [&](int tile, uint8_t* stg) {
     if (min((long)(tile - tb + 1) * ppt, id_end - id0) <= (long)nstaged)
@@ -1142,6 +1156,7 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(ReduceArgs a) {
 // ---------------------------------------------------------------------------
 struct RefreshArgs {
   const int32_t* context_lens;
+  int index_stride;
   MetaHeader* meta;
   MetaHeader header;  // the plan's header, written with the new list
   WorkItem* items;
@@ -1153,7 +1168,9 @@ struct RefreshArgs {
 constexpr int REF_T = 1024;  // threads of the refresh workgroup
 
 __device__ int refresh_tiles(const RefreshArgs& a, int s) {
-  const long cap = a.token_table ? (long)a.table_stride : (long)a.table_stride * a.page_size;
+  const long cap = a.token_table == 2 ? (long)a.index_stride
+                   : a.token_table    ? (long)a.table_stride
+                                      : (long)a.table_stride * a.page_size;
   const long L = min(max((long)a.context_lens[s], 0L), cap);
   long lo = 0;
   if (!a.token_table && L > 0 && a.window > 0) {
@@ -1296,15 +1313,16 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 using namespace pa;
 
-extern "C" pa_status pa_decode(const pa_plan_t* plan, void* out, const void* q, const void* k_cache,
-                               const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
-                               const float* k_scale, const float* v_scale, const float* sinks, void* meta_dev,
-                               void* workspace_dev, void* stream) {
-  if (!plan) return set_error(PA_ERR_INVALID, "plan is NULL");
+// pa_decode and pa_decode_sparse (topk: the top-k index table of a
+// token_table = 2 problem, else NULL; context_lens: its counts).
+static pa_status decode_impl(const pa_plan_t* plan, void* out, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* block_tables, const int32_t* topk,
+                             const int32_t* context_lens, const float* k_scale, const float* v_scale,
+                             const float* sinks, void* meta_dev, void* workspace_dev, void* stream) {
   const Plan& P = plan->plan;
   const pa_problem& p = P.prob;
   if (P.items.empty()) return PA_OK;
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || (p.token_table == 2 && !topk))
     return set_error(PA_ERR_INVALID, "a required device pointer is NULL");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return set_error(PA_ERR_INVALID, "q, out, k_cache and v_cache must be 16-byte aligned");
@@ -1330,6 +1348,8 @@ extern "C" pa_status pa_decode(const pa_plan_t* plan, void* out, const void* q, 
   args.k_scale = k_scale;
   args.v_scale = v_scale;
   args.sinks = sinks;
+  args.topk = p.token_table == 2 ? topk : nullptr;
+  args.index_stride = p.index_stride;
   args.items = (const WorkItem*)((const uint8_t*)meta_dev + Plan::items_offset());
   args.meta = (const MetaHeader*)meta_dev;
   args.tag_lo = (uint32_t)P.serial;
@@ -1363,6 +1383,28 @@ extern "C" pa_status pa_decode(const pa_plan_t* plan, void* out, const void* q, 
   return launch_nrt<128, false>(P.nrt, sparse, args, n, st);
 }
 
+extern "C" pa_status pa_decode(const pa_plan_t* plan, void* out, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                               const float* k_scale, const float* v_scale, const float* sinks, void* meta_dev,
+                               void* workspace_dev, void* stream) {
+  if (!plan) return set_error(PA_ERR_INVALID, "plan is NULL");
+  if (plan->plan.prob.token_table == 2)
+    return set_error(PA_ERR_INVALID, "a plan for top-k index tables needs pa_decode_sparse");
+  return decode_impl(plan, out, q, k_cache, v_cache, block_tables, nullptr, context_lens, k_scale, v_scale, sinks,
+                     meta_dev, workspace_dev, stream);
+}
+
+extern "C" pa_status pa_decode_sparse(const pa_plan_t* plan, void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables, const int32_t* topk_indices,
+                                      const int32_t* topk_counts, const float* k_scale, const float* v_scale,
+                                      const float* sinks, void* meta_dev, void* workspace_dev, void* stream) {
+  if (!plan) return set_error(PA_ERR_INVALID, "plan is NULL");
+  if (plan->plan.prob.token_table != 2)
+    return set_error(PA_ERR_INVALID, "pa_decode_sparse needs a plan for top-k index tables (token_table 2)");
+  return decode_impl(plan, out, q, k_cache, v_cache, block_tables, topk_indices, topk_counts, k_scale, v_scale, sinks,
+                     meta_dev, workspace_dev, stream);
+}
+
 extern "C" pa_status pa_plan_refresh(const pa_plan_t* plan, const int32_t* context_lens, void* meta_dev,
                                      void* stream) {
   if (!plan) return set_error(PA_ERR_INVALID, "plan is NULL");
@@ -1383,6 +1425,7 @@ extern "C" pa_status pa_plan_refresh(const pa_plan_t* plan, const int32_t* conte
   ra.page_size = P.prob.page_size;
   ra.table_stride = P.prob.table_stride;
   ra.token_table = P.prob.token_table;
+  ra.index_stride = P.prob.index_stride;
   ra.Hkv = P.prob.num_kv_heads;
   ra.row_groups = P.row_groups;
   ra.maxp = P.maxp;

@@ -64,7 +64,10 @@ pa_status validate_problem(const pa_problem* p) {
   if (p->v_layout != PA_V_PLAIN && p->v_layout != PA_V_TRANSPOSED) return set_error(PA_ERR_INVALID, "bad v_layout");
   if (p->scale_mode < PA_SCALE_NONE || p->scale_mode > PA_SCALE_PER_TOKEN)
     return set_error(PA_ERR_INVALID, "bad scale_mode");
-  if ((p->causal | p->has_sinks | p->token_table) & ~1) return set_error(PA_ERR_INVALID, "flags must be 0 or 1");
+  if ((p->causal | p->has_sinks) & ~1) return set_error(PA_ERR_INVALID, "flags must be 0 or 1");
+  if (p->token_table < 0 || p->token_table > 2) return set_error(PA_ERR_INVALID, "token_table must be 0, 1 or 2");
+  if (p->token_table == 2 && p->num_seqs > 0 && p->index_stride < 1)
+    return set_error(PA_ERR_INVALID, "top-k index tables need index_stride >= 1");
   double cache_elems = (double)p->num_pages * p->num_kv_heads * p->page_size * p->head_dim;
   if (cache_elems > (double)(1ull << 40)) return set_error(PA_ERR_INVALID, "cache larger than 2^40 elements");
   // Valid but not implemented here.
@@ -142,7 +145,9 @@ extern "C" pa_status pa_plan(const pa_problem* problem, const int32_t* context_l
   maxp = std::max(1, std::min(maxp, kMaxPartitions));
 
   // Tiles of each sequence's visible span (the same for all its KV heads).
-  const long cap = p.token_table ? (long)p.table_stride : (long)p.table_stride * p.page_size;
+  const long cap = p.token_table == 2 ? (long)p.index_stride
+                   : p.token_table    ? (long)p.table_stride
+                                      : (long)p.table_stride * p.page_size;
   std::vector<int> seq_tiles(p.num_seqs, 0);
   for (int s = 0; s < p.num_seqs; ++s) {
     long L = std::min<long>(std::max<long>(context_lens_host[s], 0), cap);

@@ -65,8 +65,9 @@ class Problem:
     causal: bool = True
     sliding_window: int = 0
     has_sinks: bool = False
-    token_table: bool = False
+    token_table: int = 0  # 0: page tables; 1: physical token slots; 2: top-k logical positions
     softmax_scale: float = 0.0  # <= 0 means 1/sqrt(head_dim)
+    index_stride: int = 0  # top-k index tables: row stride of topk_indices
 
     @property
     def rows(self) -> int:
@@ -93,6 +94,9 @@ class Inputs:
     v_scale: Optional[torch.Tensor]
     sinks: Optional[torch.Tensor]  # float32 [Hq]
     name: str = ""
+    # top-k index tables (token_table 2): int32 [num_seqs, index_stride]
+    # logical positions; context_lens then counts each row's selected tokens
+    topk_indices: Optional[torch.Tensor] = None
 
 
 def _streams(seed: int, n: int):
@@ -429,6 +433,44 @@ def config_sparse(num_rows: int = 64, selected: int = 2048, pool_pages: int = 40
     )
 
 
+def config_sparse_topk(num_rows: int = 64, selected: int = 2048, pool_pages: int = 4096) -> Inputs:
+    """The sparse decode batch of config_sparse with two-level indices: every
+    row's context is the same 65536-token paged sequence (block table: a
+    random permutation of the 4096-page pool), and the row attends
+    ``selected`` distinct logical positions of it, drawn uniformly and
+    sorted (the output of a top-k indexer), resolved through the block
+    table by the decode.  The caches, scales and queries are those of
+    config_sparse (same seed), and so are the physical tokens each row
+    selects: the two calls give the same result."""
+    base = config_sparse(num_rows, selected, pool_pages)
+    seed = config_seed(2)
+    rq, rkv, rsel = _streams(seed, 3)
+    page = 16
+    perm = rsel.permutation(pool_pages).astype(np.int64)
+    logical = np.empty((num_rows, selected), np.int32)
+    for r in range(num_rows):
+        sel = rsel.choice(pool_pages * page, size=selected, replace=False)
+        phys = perm[sel // page] * page + sel % page
+        order = np.argsort(phys)  # the token order config_sparse uses (ascending physical slot)
+        logical[r] = sel[order].astype(np.int32)
+    bt = np.broadcast_to(perm.astype(np.int32), (num_rows, pool_pages)).copy()
+    prob = dataclasses.replace(base.problem, table_stride=pool_pages, token_table=2, index_stride=selected)
+    return dataclasses.replace(base, problem=prob, block_tables=torch.from_numpy(bt),
+                               topk_indices=torch.from_numpy(logical), name="sparse_topk")
+
+
+def resolve_topk(inp: Inputs) -> Inputs:
+    """The same call with physical token slots (token_table 1): each top-k
+    logical position resolved through the block table on the host."""
+    p = inp.problem
+    assert p.token_table == 2
+    idx = inp.topk_indices.long().clamp(0, p.table_stride * p.page_size - 1)
+    pages = torch.gather(inp.block_tables.long(), 1, idx // p.page_size)
+    slots = (pages * p.page_size + idx % p.page_size).to(torch.int32)
+    prob = dataclasses.replace(p, token_table=1, table_stride=p.index_stride, index_stride=0)
+    return dataclasses.replace(inp, problem=prob, block_tables=slots.contiguous(), topk_indices=None)
+
+
 CONFIGS = {
     "tiny": config_tiny,
     "sparse": config_sparse,
@@ -449,7 +491,7 @@ def kv_bytes_visible(inp: Inputs) -> int:
     tot = 0
     for s in range(p.num_seqs):
         if p.token_table:
-            n = int(min(max(lens[s], 0), p.table_stride))
+            n = int(min(max(lens[s], 0), p.index_stride if p.token_table == 2 else p.table_stride))
         else:
             L = int(min(max(lens[s], 0), p.table_stride * p.page_size))
             lo, hi = visible_span(L, p.query_len, p.sliding_window, p.causal)

@@ -53,13 +53,16 @@ def attend(inp, pos_shift: int = 0, window_shift: int = 0) -> np.ndarray:
     lens = inp.context_lens.numpy()
     G = p.num_q_heads // p.num_kv_heads
     out = np.zeros((p.rows, p.num_q_heads, p.head_dim), np.float64)
-    cap = p.table_stride if p.token_table else p.table_stride * p.page_size
+    cap = (p.index_stride if p.token_table == 2 else p.table_stride) if p.token_table else p.table_stride * p.page_size
     for s in range(p.num_seqs):
         L = int(min(max(int(lens[s]), 0), cap))
         if L == 0:
             continue
         t = np.arange(L)
-        if p.token_table:
+        if p.token_table == 2:
+            pos = np.clip(inp.topk_indices.numpy()[s, :L].astype(np.int64), 0, p.table_stride * p.page_size - 1)
+            pages, offs = bt[s][pos // p.page_size].astype(np.int64), pos % p.page_size
+        elif p.token_table:
             slots = bt[s, :L].astype(np.int64)
             pages, offs = slots // p.page_size, slots % p.page_size
         else:

@@ -24,7 +24,8 @@ def to_device(inp, device="cuda"):
         return None if t is None else t.to(device).contiguous()
 
     return dict(q=d(inp.q), k_cache=d(inp.k_cache), v_cache=d(inp.v_cache), block_tables=d(inp.block_tables),
-                context_lens=d(inp.context_lens), k_scale=d(inp.k_scale), v_scale=d(inp.v_scale), sinks=d(inp.sinks))
+                context_lens=d(inp.context_lens), k_scale=d(inp.k_scale), v_scale=d(inp.v_scale), sinks=d(inp.sinks),
+                topk_indices=d(getattr(inp, "topk_indices", None)))
 
 
 def check_shapes(inp, dev):
@@ -40,9 +41,13 @@ def check_shapes(inp, dev):
     bt = inp.block_tables.cpu().numpy()
     lens = inp.context_lens.cpu().numpy()
     for s in range(p.num_seqs):
-        n = int(min(max(lens[s], 0), p.table_stride if p.token_table else p.table_stride * p.page_size))
-        used = bt[s, :n] if p.token_table else bt[s, : (n + p.page_size - 1) // p.page_size]
-        lim = p.num_pages * p.page_size if p.token_table else p.num_pages
+        if p.token_table == 2:  # the whole page table is reachable (positions are clamped into it)
+            used, lim = bt[s], p.num_pages
+            assert dev["topk_indices"].shape == (p.num_seqs, p.index_stride)
+        else:
+            n = int(min(max(lens[s], 0), p.table_stride if p.token_table else p.table_stride * p.page_size))
+            used = bt[s, :n] if p.token_table else bt[s, : (n + p.page_size - 1) // p.page_size]
+            lim = p.num_pages * p.page_size if p.token_table else p.num_pages
         assert (used >= 0).all() and (used < lim).all(), "table entry out of range"
     if p.kv_dtype == "fp8" and p.scale_mode == "token":
         assert dev["k_scale"].shape == (p.num_pages, p.num_kv_heads, p.page_size)
@@ -59,8 +64,13 @@ def run(inp, dev=None, plan=None, lens_for_plan=None, **plan_kw):
         plan = B.Plan(B.problem_of(p), lens, **plan_kw).allocate("cuda")
     plan.workspace.fill_(float("nan"))
     out = torch.full_like(dev["q"], float("nan"))
-    B.attend(plan, out, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["context_lens"],
-             dev["k_scale"], dev["v_scale"], dev["sinks"])
+    if p.token_table == 2:
+        B.pa_decode_sparse(plan, out, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                           dev["topk_indices"], dev["context_lens"], dev["k_scale"], dev["v_scale"], dev["sinks"])
+        B.pa_reduce(plan, out, dev["sinks"])
+    else:
+        B.attend(plan, out, dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["context_lens"],
+                 dev["k_scale"], dev["v_scale"], dev["sinks"])
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), plan
 

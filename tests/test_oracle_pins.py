@@ -345,3 +345,18 @@ def test_tolerance_detects_planted_mistakes(scale, window):
         excess = err - (0.005 + 0.005 * np.abs(ref))
         assert err.max() >= 0.05, (name, float(err.max()))
         assert (excess > 0).sum() >= 16, (name, int((excess > 0).sum()))
+
+
+def test_oracle_two_level_topk():
+    """Top-k logical positions through the block table (token_table 2):
+    against the brute force on a small case (positions past the table's
+    extent and below 0 clamp to it), and bit-identical to the same call with
+    the positions resolved to physical slots on the host."""
+    small = W.config_sparse_topk(num_rows=3, selected=40, pool_pages=8)
+    np.testing.assert_allclose(O.attend(small).astype(np.float64), bruteforce.attend(small), rtol=1e-6, atol=1e-7)
+    wild = dataclasses.replace(small, topk_indices=small.topk_indices.clone())
+    wild.topk_indices[0, :3] = torch.tensor([-5, 1 << 20, 8 * 16], dtype=torch.int32)
+    np.testing.assert_allclose(O.attend(wild).astype(np.float64), bruteforce.attend(wild), rtol=1e-6, atol=1e-7)
+    full = W.config_sparse_topk()
+    sel = [(r, h) for r in range(0, 64, 9) for h in (0, 7, 15)]
+    np.testing.assert_array_equal(O.attend(full, sel=sel), O.attend(W.resolve_topk(full), sel=sel))
