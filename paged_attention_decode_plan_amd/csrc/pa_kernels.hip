@@ -12,24 +12,31 @@
 // output (aiter PR #4332 follow-up commit: pinning stale entries, 0*NaN).
 //
 // gfx950 design (not the pages' FlyDSL tiling):
-//  * a workgroup of 4 waves owns one work item = (sequence, KV head, row
-//    group of up to 64 query rows, a contiguous range of 128-token tiles);
-//  * dense caches: K/V pages of a tile go straight from HBM into an LDS ring
-//    (global_load_lds_dwordx4, 16 bytes per lane, coalesced page-head blocks),
-//    2 or 3 tiles deep, so later tiles stream in while one tile computes;
-//    token-table (sparse) caches gather through registers instead;
-//  * each wave takes 32 tokens of every tile for all of the item's query rows,
-//    so every K/V byte is read from LDS and converted exactly once; the four
-//    waves keep independent online-softmax states merged once at the end;
-//  * QK^T is computed as S^T = K Q^T and PV as O^T = V^T P^T with
-//    v_mfma_f32_16x16x32_{f16,bf16}: FP8 K/V convert exactly to FP16 in
-//    registers (v_cvt_scalef32_pk_f16_fp8), BF16 queries are scaled by a
-//    per-row power of two into FP16 (exact), probabilities go from the QK
-//    accumulator to the PV operand in registers (the QK rows are read in the
-//    token order PV contracts) as RNE FP16 with 11 significant bits;
+//  * a workgroup owns one work item = (sequence, KV head, row group of up to
+//    64 query rows, a contiguous range of 128-token tiles); every wave owns
+//    one 16-row tile of the item's rows and a share of each tile's tokens
+//    (Waves / Roles below);
+//  * dense caches: K/V pages of a tile go straight from HBM into LDS stages
+//    (global_load_lds, 16 bytes per lane, coalesced page-head blocks), two to
+//    four tiles deep, so later tiles stream in while one tile computes;
+//    token-table (sparse) caches gather the same way with per-token slots;
+//  * QK^T is computed as S^T = K Q^T: FP8 caches run
+//    v_mfma_scale_f32_16x16x128_f8f6f4 with K as stored against three FP8
+//    terms of the query (hi, then two residuals, each with its own E8M0 block
+//    scale), BF16 caches run v_mfma_f32_16x16x32_bf16 with the BF16 query;
+//  * PV is computed as O^T = V^T P^T: FP8 V converts exactly to FP16 in
+//    registers (v_cvt_scalef32_pk_f16_fp8) against FP16 probabilities on
+//    v_mfma_f32_16x16x32_f16; BF16 V runs against a two-term BF16 split of
+//    the probabilities; probabilities go from the QK accumulator to the PV
+//    operand in registers (the QK rows are read in the token order PV
+//    contracts);
 //  * row max/sum across the 4 lane groups of a row use v_permlane16/32_swap;
-//  * rescaling of the accumulator is lazy: only when a row maximum grows by
-//    more than 2^8, or the per-token V-scale reference leaves its band.
+//  * probabilities are taken against a per-row reference maximum set at the
+//    row's first visible tokens: a base-2 score more than TAU above it (or a
+//    per-token V scale more than VS_BAND above its reference) makes the
+//    workgroup redo the item with larger references, after at most one scan
+//    pass that records every row's true bound, so the accumulator is only
+//    ever written by MFMAs.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -69,10 +76,10 @@ struct Tile {
   static constexpr int NDT = D / 16; // 16-wide d tiles of O
 };
 
-// Wave roles: a workgroup's 4 waves split an item's rows into WR groups of
-// NRW row tiles and each tile's 128 tokens into WT groups (WR * WT = 4), so
-// that one wave's O accumulator stays at 64 registers: D 128 keeps two row
-// tiles per wave, D 256 one.
+// Wave roles: a workgroup's NW waves split an item's row tiles into WR
+// groups (one 16-row tile per wave: NRW = 1) and each tile's 128 tokens into
+// WT groups (WR * WT = NW), so that one wave's O accumulator is one 16-row
+// tile of the head dim (D / 4 registers).
 template <int D, int NRT>
 struct Roles {
   static constexpr int NW = Waves<NRT, D>::NW;
