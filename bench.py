@@ -41,6 +41,8 @@ from paged_attention_decode_plan_amd.build import source_sha  # noqa: E402
 
 PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
 SETTLE_MS = 100.0  # untimed calls before the warm-up steps, so that the GPU clocks have settled
+MERGE = {"reducer": B.MERGE_REDUCER, "in-kernel": B.MERGE_IN_KERNEL}
+merge_mode = B.MERGE_AUTO  # --merge
 WORKLOADS = {
     "dense_mtp4_fp8": "dense MTP4 verify, FP8 KV, per-token scales: B32 Hq16/Hkv1 D128 QL4 page128 L~U[16K,32K]",
     "dense_mtp4_bf16": "dense MTP4 verify, BF16 KV: B32 Hq16/Hkv1 D128 QL4 page128 L~U[16K,32K]",
@@ -193,7 +195,7 @@ def measure(workload: str, steps: int, warmup: int, dev):
     d = {k: (None if v is None else v.to(dev).contiguous()) for k, v in dict(
         q=inp.q, k=inp.k_cache, v=inp.v_cache, bt=inp.block_tables, cl=inp.context_lens, ks=inp.k_scale,
         vs=inp.v_scale, sk=inp.sinks, tk=inp.topk_indices).items()}
-    plan = B.Plan(B.problem_of(p), inp.context_lens, **plan_kw).allocate(dev)
+    plan = B.Plan(B.problem_of(p), inp.context_lens, merge=merge_mode, **plan_kw).allocate(dev)
     info = plan.info()
     out = torch.empty_like(d["q"])
     stream = torch.cuda.current_stream()
@@ -260,6 +262,11 @@ def measure(workload: str, steps: int, warmup: int, dev):
         "roofline_claim": workload in ROOFLINE_CLAIM,
         "work_items": info.num_items,
         "partials": info.num_slots,
+        # how multi-partition units are merged: the reducer launch, the
+        # last-arriving work item, or nothing to merge (every unit wrote its
+        # rows directly)
+        "merge": ("none (direct output)" if info.max_parts < 2 else
+                  "in-kernel last arriver" if merge_mode == B.MERGE_IN_KERNEL else "reducer launch"),
         "cu_count": info.cu_count,
         "cold_copies": nc,
         "clock_settle_ms": round(settle_ms, 1),
@@ -371,6 +378,8 @@ def main():
     ap.add_argument("--only", action="store_true", help="measure the chosen workload alone (no workloads object)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--merge", choices=sorted(MERGE), default=None,
+                    help="merge of multi-partition units (default: the library's choice, the reducer)")
     ap.add_argument("--ceiling", action="store_true",
                     help="run the read-only bandwidth probes of the decode's access pattern instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -384,6 +393,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    global merge_mode
+    if args.merge:
+        merge_mode = MERGE[args.merge]
     if args.ceiling:
         ceiling(args, dev)
         return
@@ -429,6 +441,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "description": WORKLOADS[args.workload],
                    "kv_bytes_per_call": kv_bytes, "work_items": head["work_items"], "partials": head["partials"],
+                   "merge": head["merge"],
                    "cu_count": head["cu_count"]},
         "us_per_call_cold": head["us_per_call_cold"],
         "us_per_call_warm": head["us_per_call_warm"],

@@ -99,6 +99,14 @@ typedef struct {
                                workgroups, at least one per (sequence, KV head, row group)) and one reduce
                                entry per such unit, so that pa_plan_refresh can re-partition the plan on
                                the device from device context lengths (e.g. between HIP graph replays) */
+  int32_t merge;            /* how multi-partition units are merged: 0 the library's choice (the reducer:
+                               on gfx950 the agent-scope L2 write-back each arriving item needs makes the
+                               in-kernel merge slower on every multi-partition shape measured), 1 the
+                               reducer launch (pa_reduce), 2 in the decode launch (aiter PR #7079,
+                               "Partition merges": the last-arriving work item of a unit merges its
+                               partials, counted on per-unit arrival counters in meta_dev that every call
+                               leaves at zero; pa_reduce then does nothing; calls that overlap on one
+                               meta_dev race on the counters).  Both give bit-identical outputs */
 } pa_plan_opts;
 
 typedef struct pa_plan_s pa_plan_t;

@@ -38,7 +38,9 @@ class PaProblem(ctypes.Structure):
 
 class PaPlanOpts(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("cu_count", "max_partitions", "partition_tokens", "stage_limit",
-                                              "refreshable")]
+                                              "refreshable", "merge")]
+
+MERGE_AUTO, MERGE_REDUCER, MERGE_IN_KERNEL = 0, 1, 2
 
 
 class PaPlanInfo(ctypes.Structure):
@@ -121,12 +123,12 @@ class Plan:
     """Owns a pa_plan_t plus the device metadata and workspace it needs."""
 
     def __init__(self, problem: PaProblem, context_lens_host, cu_count=0, max_partitions=0, partition_tokens=0,
-                 stage_limit=0, refreshable=0):
+                 stage_limit=0, refreshable=0, merge=MERGE_AUTO):
         L = load_library()
         self.problem = problem
         lens = torch.as_tensor(context_lens_host, dtype=torch.int32).contiguous().cpu()
         self._lens = lens
-        opts = PaPlanOpts(cu_count, max_partitions, partition_tokens, stage_limit, refreshable)
+        opts = PaPlanOpts(cu_count, max_partitions, partition_tokens, stage_limit, refreshable, merge)
         h = ctypes.c_void_p()
         _check(L.pa_plan(ctypes.byref(problem), lens.data_ptr() if lens.numel() else None, ctypes.byref(opts),
                          ctypes.byref(h)))

@@ -43,6 +43,7 @@ struct KernelArgs {
   const MetaHeader* meta;  // header of the metadata buffer (items follow it)
   uint32_t tag_lo, tag_hi;  // the launching plan's serial: the header must hold it
   float* workspace;
+  int* merge_ctr;  // arrival counters of the in-kernel merge, else NULL (the reducer merges)
   long long page_stride;  // bytes between physical pages (Hkv * D * page * elem)
   long long head_stride;  // bytes between KV heads of a page (D * page * elem)
   int QL, Hq, Hkv, G, page_size, table_stride, window, causal;

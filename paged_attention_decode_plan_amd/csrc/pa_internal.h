@@ -44,6 +44,8 @@ struct MetaHeader {
 static_assert(sizeof(MetaHeader) == 32, "metadata header is 32 bytes");
 
 // Layout of meta_dev: [MetaHeader][WorkItem x num_items][ReduceItem x num_reduce]
+// and, for the in-kernel merge, 128-byte aligned arrival counters: one
+// 128-byte line per partial slot (a unit's counter sits at its first slot).
 struct Plan {
   pa_problem prob;
   pa_plan_opts opts;
@@ -61,6 +63,7 @@ struct Plan {
   std::vector<WorkItem> items;
   std::vector<ReduceItem> reduce;
   int num_slots = 0;
+  bool in_kernel_merge = false;     // last-arriver merge in the decode launch (no reducer launch)
   uint64_t serial = 0;              // unique per plan in the process
   std::vector<uint8_t> meta_host;   // serialised metadata (header, items, reduce table)
   mutable uint8_t* meta_pinned = nullptr;  // pinned copy of meta_host, made by the first upload
@@ -68,6 +71,8 @@ struct Plan {
   size_t meta_bytes() const { return meta_host.size(); }
   static constexpr size_t items_offset() { return sizeof(MetaHeader); }
   size_t reduce_offset() const { return sizeof(MetaHeader) + items.size() * sizeof(WorkItem); }
+  size_t counters_offset() const { return (reduce_offset() + reduce.size() * sizeof(ReduceItem) + 127) & ~(size_t)127; }
+  static constexpr size_t kCounterBytes = 128;  // one line per counter
   // partial state per slot: m[rows_per_group], l[rows_per_group], o[rows_per_group][D]
   size_t slot_floats() const { return (size_t)rows_per_group * (2 + prob.head_dim); }
   size_t workspace_bytes() const { return (size_t)num_slots * slot_floats() * sizeof(float); }

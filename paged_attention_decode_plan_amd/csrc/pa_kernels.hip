@@ -46,6 +46,7 @@
 
 #include "pa_device.h"
 #include "pa_internal.h"
+#include "pa_merge.h"
 
 namespace pa {
 
@@ -125,6 +126,7 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   uint8_t* stage_base = smem;
   int32_t* ids = (int32_t*)(smem + S::MAIN);
   float* stats = (float*)(smem + S::MAIN + S::IDS);
+  static_assert(merge_lds_bytes<D>() <= S::MAIN, "the in-kernel merge reuses the stage LDS");
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -989,6 +991,12 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
       const int r = e / (D / 4), d4 = (e % (D / 4)) * 4;
       *(f4*)(po + (size_t)r * D + d4) = *(const f4*)(obuf + r * OROW + d4);
     }
+    if (a.merge_ctr) {
+      __syncthreads();  // the O buffer read: its LDS is the merge's
+      const MergeArgs ma{a.out, a.workspace, a.sinks, a.QL, a.Hq, a.G, a.rows_total, a.rows_per_group, a.q_fp16,
+                         a.has_sinks};
+      arrive_and_merge<D>(ma, a.merge_ctr, it, stage_base);
+    }
   } else {
     for (int e = tid; e < nrows * (D / 4); e += NTHREADS) {
       const int r = e / (D / 4), d4 = (e % (D / 4)) * 4;
@@ -1026,131 +1034,18 @@ struct ReduceArgs {
   int QL, Hq, G, D, rows_total, rows_per_group, q_fp16, has_sinks, chunks_per_entry;
 };
 
-// Rows per reducer workgroup: one (row, 4-dim) output per thread of 256.
-template <int D>
-constexpr int red_rows() { return 1024 / D; }
-
 template <int D>
 __global__ __launch_bounds__(256) void pa_reduce_kernel(ReduceArgs a) {
-  constexpr int RR = red_rows<D>();
-  constexpr int Q4 = D / 4;
-  constexpr int RCH = 16;  // partitions' loads in flight per round trip
-  static_assert(RR * Q4 == 256 && RR % 4 == 0, "one output per thread");
-  __shared__ float wgt[RR][kMaxPartitions];
+  constexpr int RR = merge_rows<D>();
+  __shared__ float wgt[RR * kMaxPartitions];
   __shared__ float rowf[RR];
   const ReduceItem e = a.entries[blockIdx.x / a.chunks_per_entry];
   const MetaHeader mh = *a.meta;
   if (!meta_ok(mh, a.tag_lo, a.tag_hi)) return;  // not this plan's list: touch nothing
   if (e.nparts < 2) return;  // a unit with one partition wrote its rows itself
-  const int chunk = blockIdx.x % a.chunks_per_entry;
-  const int rpg = a.rows_per_group;
-  const int row0 = e.rg * kMaxRowsPerItem;
-  const int nrows = min(rpg, a.rows_total - row0);
-  const int r0 = chunk * RR;
-  const size_t slot_f = (size_t)rpg * (2 + D);
-  const int tid = threadIdx.x;
-  const int np = e.nparts;
-  const float* base = a.workspace + (size_t)e.first_slot * slot_f;
-  // The thread's output (row rr, 4 dims d4).  Its partial O for the first RCH
-  // partitions is loaded before the weights are known, so that the merge
-  // costs one round trip to memory for up to RCH partitions.
-  const int rr = tid / Q4, d4 = (tid % Q4) * 4;
-  const int r = r0 + rr;
-  const float* po = base + 2 * rpg + (size_t)min(r, nrows - 1) * D + d4;
-  f4 v0[RCH];
-#pragma unroll
-  for (int j = 0; j < RCH; ++j) v0[j] = *(const f4*)(po + (size_t)min(j, np - 1) * slot_f);
-  // per-row weights: wave w takes rows w, w + 4, ..., lanes over partitions
-  // (p = lane + 64k); the rows' (max, sum) loads are issued together
-  {
-    constexpr int XR = RR / 4;
-    const int wv = tid >> 6, lane = tid & 63;
-    float mv[XR][4], lv[XR][4], skv[XR];
-#pragma unroll
-    for (int x = 0; x < XR; ++x) {
-      const int rx = min(r0 + wv + 4 * x, nrows - 1);
-      skv[x] = a.has_sinks ? a.sinks[e.kvh * a.G + (row0 + rx) % a.G] : 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float* sp = base + (size_t)min(lane + 64 * k, np - 1) * slot_f;
-        mv[x][k] = sp[rx];
-        lv[x][k] = sp[rpg + rx];
-      }
-    }
-#pragma unroll
-    for (int x = 0; x < XR; ++x) {
-      const int rw = wv + 4 * x;
-      if (r0 + rw >= nrows) continue;  // wave-uniform
-      float M = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (lane + 64 * k < np && lv[x][k] > 0.f) M = fmaxf(M, mv[x][k]);
-      M = wave_max(M);
-      float den = 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int p = lane + 64 * k;
-        if (p < np) {
-          const float wp = lv[x][k] > 0.f ? __builtin_amdgcn_exp2f(mv[x][k] - M) : 0.f;
-          wgt[rw][p] = wp;
-          den += wp * lv[x][k];
-        }
-      }
-      den = wave_sum(den);  // fixed-order sum of the denominator terms
-      if (lane == 0) {
-        float f = 0.f;
-        if (den > 0.f) {
-          if (a.has_sinks) {
-            const float sk = skv[x] * LOG2E;
-            const float M2 = fmaxf(M, sk);
-            const float sc = __builtin_amdgcn_exp2f(M - M2);
-            f = sc / (den * sc + __builtin_amdgcn_exp2f(sk - M2));
-          } else {
-            f = 1.0f / den;
-          }
-        }
-        rowf[rw] = f;
-      }
-    }
-  }
-  __syncthreads();
-  if (r >= nrows) return;
-  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-  const float f = rowf[rr];
-  if (f > 0.f) {
-    // partitions in order, RCH loads in flight at a time (the first RCH are
-    // already in v0); partitions without visible tokens are skipped by a
-    // select, not a branch
-    for (int p0 = 0; p0 < np; p0 += RCH) {
-      f4 v[RCH];
-      if (p0 == 0) {
-#pragma unroll
-        for (int j = 0; j < RCH; ++j) v[j] = v0[j];
-      } else {
-#pragma unroll
-        for (int j = 0; j < RCH; ++j) v[j] = *(const f4*)(po + (size_t)min(p0 + j, np - 1) * slot_f);
-      }
-#pragma unroll
-      for (int j = 0; j < RCH; ++j) {
-        const float wp = p0 + j < np ? wgt[rr][p0 + j] : 0.f;
-        if (wp != 0.f) acc += wp * v[j];
-      }
-    }
-  }
-  const f4 v = acc * f;
-  const int gr = row0 + r, i = gr / a.G, hl = gr % a.G;
-  const int h = e.kvh * a.G + hl;
-  const long ooff = (((long)e.seq * a.QL + i) * a.Hq + h) * D + d4;
-  uint16_t hv[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    if (a.q_fp16)
-      hv[k] = __builtin_bit_cast(uint16_t, (_Float16)v[k]);
-    else
-      hv[k] = __builtin_bit_cast(uint16_t, (__bf16)v[k]);
-  }
-  *(u32x2*)((uint16_t*)a.out + ooff) =
-      u32x2{(uint32_t)hv[0] | ((uint32_t)hv[1] << 16), (uint32_t)hv[2] | ((uint32_t)hv[3] << 16)};
+  const MergeArgs ma{a.out, a.workspace, a.sinks, a.QL, a.Hq, a.G, a.rows_total, a.rows_per_group, a.q_fp16,
+                     a.has_sinks};
+  merge_chunk<D>(ma, e, blockIdx.x % a.chunks_per_entry, wgt, rowf);
 }
 
 // ---------------------------------------------------------------------------
@@ -1362,6 +1257,7 @@ static pa_status decode_impl(const pa_plan_t* plan, void* out, const void* q, co
   args.tag_lo = (uint32_t)P.serial;
   args.tag_hi = (uint32_t)(P.serial >> 32);
   args.workspace = (float*)workspace_dev;
+  args.merge_ctr = P.in_kernel_merge ? (int*)((uint8_t*)meta_dev + P.counters_offset()) : nullptr;
   args.head_stride = (long long)p.head_dim * p.page_size * elem;
   args.page_stride = args.head_stride * p.num_kv_heads;
   args.QL = p.query_len;
@@ -1449,7 +1345,7 @@ extern "C" pa_status pa_reduce(const pa_plan_t* plan, void* out, const float* si
                                void* workspace_dev, void* stream) {
   if (!plan) return set_error(PA_ERR_INVALID, "plan is NULL");
   const Plan& P = plan->plan;
-  if (P.reduce.empty()) return PA_OK;
+  if (P.reduce.empty() || P.in_kernel_merge) return PA_OK;  // nothing to merge, or merged by pa_decode
   if (!out) return set_error(PA_ERR_INVALID, "out is NULL");
   if (!aligned16(out)) return set_error(PA_ERR_INVALID, "out must be 16-byte aligned");
   if (P.prob.has_sinks && !sinks) return set_error(PA_ERR_INVALID, "has_sinks set but sinks is NULL");
@@ -1472,7 +1368,7 @@ extern "C" pa_status pa_reduce(const pa_plan_t* plan, void* out, const float* si
   ra.rows_per_group = P.rows_per_group;
   ra.q_fp16 = P.prob.q_dtype == PA_FP16;
   ra.has_sinks = P.prob.has_sinks;
-  const int rr = P.prob.head_dim == 256 ? red_rows<256>() : red_rows<128>();
+  const int rr = P.prob.head_dim == 256 ? merge_rows<256>() : merge_rows<128>();
   ra.chunks_per_entry = (P.rows_per_group + rr - 1) / rr;
   const unsigned grid = (unsigned)(P.reduce.size() * ra.chunks_per_entry);
   if (P.prob.head_dim == 256)

@@ -112,6 +112,7 @@ extern "C" pa_status pa_plan(const pa_problem* problem, const int32_t* context_l
   if (problem->num_seqs > 0 && !context_lens_host) return set_error(PA_ERR_INVALID, "context_lens_host is NULL");
   pa_plan_opts o{};
   if (opts) o = *opts;
+  if (o.merge < 0 || o.merge > 2) return set_error(PA_ERR_INVALID, "merge must be 0, 1 or 2");
   if (o.cu_count < 0 || o.max_partitions < 0 || o.partition_tokens < 0 || o.stage_limit < 0)
     return set_error(PA_ERR_INVALID, "plan options must be >= 0");
   if (o.refreshable & ~1) return set_error(PA_ERR_INVALID, "refreshable must be 0 or 1");
@@ -303,7 +304,11 @@ extern "C" pa_status pa_plan(const pa_problem* problem, const int32_t* context_l
     P.num_slots = std::max(P.num_slots, P.budget_items);
   }
   P.serial = g_next_serial.fetch_add(1);
-  P.meta_host.resize(P.reduce_offset() + P.reduce.size() * sizeof(ReduceItem));
+  // 2 (in-kernel merge) where asked; the library's choice is the reducer
+  P.in_kernel_merge = o.merge == 2 && P.num_slots > 0;
+  P.meta_host.assign(P.in_kernel_merge ? P.counters_offset() + (size_t)P.num_slots * Plan::kCounterBytes
+                                       : P.reduce_offset() + P.reduce.size() * sizeof(ReduceItem),
+                     0);  // counters start at zero
   const MetaHeader hdr{kMetaMagic, (uint32_t)P.serial, (uint32_t)(P.serial >> 32), (uint32_t)P.items.size(),
                        (uint32_t)P.reduce.size(), 0, 0, 0};
   std::memcpy(P.meta_host.data(), &hdr, sizeof hdr);

@@ -41,6 +41,7 @@
 
 #include "pa_device.h"
 #include "pa_internal.h"
+#include "pa_merge.h"
 
 namespace pa {
 
@@ -91,6 +92,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   using S = StreamSmem<RB>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   float* obuf = (float*)smem;
+  static_assert(merge_lds_bytes<D>() <= S::MERGE, "the in-kernel merge reuses the O buffers");
   int32_t* ids = (int32_t*)(smem + S::MERGE);
   float* sbuf = (float*)(smem + S::MERGE + S::IDS);
   float* stats = (float*)(smem + S::MERGE + S::IDS + S::SCALES);
@@ -820,6 +822,12 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     for (int e = tid; e < nrows * (D / 4); e += 256) {
       const int r = e / (D / 4), d4 = (e % (D / 4)) * 4;
       *(f4*)(po + (size_t)r * D + d4) = osum(r, d4);
+    }
+    if (a.merge_ctr) {
+      __syncthreads();  // the O buffers read: their LDS is the merge's
+      const MergeArgs ma{a.out, a.workspace, a.sinks, a.QL, a.Hq, a.G, a.rows_total, a.rows_per_group, a.q_fp16,
+                         a.has_sinks};
+      arrive_and_merge<D>(ma, a.merge_ctr, it, (uint8_t*)obuf);
     }
   } else {
     for (int e = tid; e < nrows * (D / 4); e += 256) {

@@ -232,3 +232,27 @@ def test_shared_meta_buffer_is_refused_without_upload():
     args = [0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000, 0x8000, None, buf, 0xA000, None]
     for plan in (a, b):
         assert L.pa_decode(plan.handle, *args) == B.PA_ERR_WORKSPACE
+
+
+def test_in_kernel_merge_plan_layout():
+    """The in-kernel merge: the same work list and partial slots as the
+    reducer plan, plus one zeroed 128-byte arrival counter per slot after
+    the reduce table (128-byte aligned); pa_reduce then has nothing to
+    launch; merge values outside 0..2 are refused."""
+    lens = [5000, 0, 1, 700]
+    prob = B.make_problem(4, 4, 16, 1, 128, 128, 64, 16, "bf16", "fp8", False, "token", 1, 0, 0, 0, 0.0)
+    red = B.Plan(prob, lens, cu_count=32, merge=B.MERGE_REDUCER)
+    ikm = B.Plan(prob, lens, cu_count=32, merge=B.MERGE_IN_KERNEL)
+    auto = B.Plan(prob, lens, cu_count=32)
+    assert (red.work().numpy() == ikm.work().numpy()).all()
+    ri, ii = red.info(), ikm.info()
+    assert ri.num_slots == ii.num_slots > 0 and ri.num_reduce == ii.num_reduce
+    base = 32 + 32 * ri.num_items + 32 * ri.num_reduce
+    assert red.meta_bytes == base == auto.meta_bytes
+    assert ikm.meta_bytes == ((base + 127) // 128) * 128 + 128 * ii.num_slots
+    # pa_reduce of an in-kernel-merge plan returns before any argument check or launch
+    L = B.load_library()
+    assert L.pa_reduce(ikm.handle, None, None, None, None, None) == B.PA_OK
+    for bad in (-1, 3):
+        with pytest.raises(ValueError):
+            B.Plan(prob, lens, cu_count=32, merge=bad)
