@@ -285,6 +285,81 @@ def measure(workload: str, steps: int, warmup: int, dev):
     return res, inp
 
 
+# The sparse front end's indexer (pa_mqa_logits, then pa_topk), measured
+# into the same "workloads" object; bound by the FP8 matrix cores.
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, AMD's published figure
+INDEXER_WORKLOADS = {
+    "indexer_decode": "indexer of the sparse decode batch: 64 rows x 65536 FP8 index keys, 64 heads of dim 128, "
+                      "full windows, then the top 2048 of every row",
+    "mqa_logits_4095x36863": "supplementary: FP8 MQA logits alone at the pages' MI355X timing shape, 4095 rows x "
+                             "36863 keys, 64 heads of dim 128, full windows",
+}
+# The pages' MI355X (gfx950) time for FlyDSL fp8_mqa_logits at that shape
+# (aiter PR "LDS-staged fp8_mqa_logits for gfx942", gfx950 section): context
+# only; the pages do not state its windows.
+PAGES_US = {"mqa_logits_4095x36863": 1635.0}
+
+
+def measure_indexer(workload: str, steps: int, warmup: int, dev):
+    """Time pa_mqa_logits (and, for indexer_decode, pa_topk) with inputs
+    resident in HBM: one pair of HIP events on the launch stream around K
+    calls, after the clock settle and warm-up calls."""
+    if workload == "indexer_decode":
+        x, k = W.config_indexer_decode(), 2048
+    else:
+        x, k = W.make_indexer_case(W.config_seed(8), 4095, 36863, heads=64, windows="full", name=workload), 0
+    d = {n: getattr(x, n).to(dev).contiguous() for n in ("q", "kv", "kv_scale", "weights", "ks", "ke")}
+    logits = torch.empty((x.rows, x.num_kv), dtype=torch.float32, device=dev)
+    idx = torch.empty((x.rows, max(k, 1)), dtype=torch.int32, device=dev)
+    cnt = torch.empty((x.rows,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def lg():
+        B.pa_mqa_logits(logits, d["q"], d["kv"], d["kv_scale"], d["weights"], d["ks"], d["ke"], True, stream)
+
+    def tk():
+        B.pa_topk(idx, cnt, logits, d["ks"], d["ke"], None, stream)
+
+    def region(body, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            body()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    settle_ms = 0.0
+    while settle_ms < SETTLE_MS:
+        settle_ms += region(lg, 5) * 5 / 1e3
+    for _ in range(warmup):
+        lg()
+        if k:
+            tk()
+    lo = x.ks.numpy().clip(0, x.num_kv)
+    hi = np.maximum(x.ke.numpy(), lo).clip(0, x.num_kv)
+    pairs = int((hi - lo).sum())  # (row, key) scores computed
+    heads = x.q.shape[1]
+    flops = 2.0 * pairs * heads * 128
+    us_lg = region(lg, steps)
+    res = {"description": INDEXER_WORKLOADS[workload], "kernel": "mqa_logits_kernel",
+           "rows": x.rows, "keys": x.num_kv, "heads": heads, "flops_per_call": flops,
+           "logits_us": round(us_lg, 2), "logits_tflops": round(flops / us_lg / 1e6, 1),
+           "logits_bytes_written": x.rows * x.num_kv * 4,
+           "roofline": {"bound": "mfma", "achieved": round(flops / us_lg / 1e6, 1), "peak": PEAK_FP8_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(flops / us_lg / 1e6 / PEAK_FP8_TFLOPS, 4)},
+           "clock_settle_ms": round(settle_ms, 1)}
+    if k:
+        us_tk = region(tk, steps)
+        us_both = region(lambda: (lg(), tk()), steps)
+        res.update({"topk": k, "topk_us": round(us_tk, 2), "indexer_us": round(us_both, 2),
+                    "topk_gbps_logits_read": round(x.rows * x.num_kv * 4 / us_tk / 1e3, 1)})
+    if workload in PAGES_US:
+        res["pages_us_context"] = {"value": PAGES_US[workload], "note": "FlyDSL on MI355X, windows not stated"}
+    return res
+
+
 def ceiling(args, dev):
     """What the memory system gives for the decode's access pattern: the
     read-only probes of libpa_ceiling.so over the dense MTP4 FP8 batch's own
@@ -378,6 +453,8 @@ def main():
     ap.add_argument("--only", action="store_true", help="measure the chosen workload alone (no workloads object)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--indexer", choices=sorted(INDEXER_WORKLOADS), default=None,
+                    help="measure one indexer workload alone and print its JSON")
     ap.add_argument("--merge", choices=sorted(MERGE), default=None,
                     help="merge of multi-partition units (default: the library's choice, the reducer)")
     ap.add_argument("--ceiling", action="store_true",
@@ -398,6 +475,11 @@ def main():
         merge_mode = MERGE[args.merge]
     if args.ceiling:
         ceiling(args, dev)
+        return
+    if args.indexer:
+        r = measure_indexer(args.indexer, args.steps, args.warmup, dev)
+        r.update({"workload": args.indexer, "kernel_sha": source_sha()})
+        print(json.dumps(r), flush=True)
         return
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
@@ -426,6 +508,11 @@ def main():
             r, _ = measure(wl, args.steps, args.warmup, dev)
             extra[wl] = r
             log(f"{wl}: {r['us_per_call_cold']} us cold, {r['gbps_cold']} GB/s")
+        for wl in INDEXER_WORKLOADS:
+            r = measure_indexer(wl, max(3, args.steps // 5) if wl != "indexer_decode" else args.steps,
+                                min(args.warmup, 3), dev)
+            extra[wl] = r
+            log(f"{wl}: logits {r['logits_us']} us, {r['logits_tflops']} TFLOP/s")
     res = {
         "metric": "achieved HBM GB/s of KV bytes (and us/call), FP8 paged decode",
         "value": head["gbps_cold"],

@@ -53,9 +53,11 @@ def window(ks: int, ke: int, n: int) -> tuple[int, int]:
 
 
 def mqa_logits(q_codes, kv_codes, kv_scale, weights, ks, ke, rows=None):
-    """float64 logits [R, N] (or only the given rows) and the matching sum of
-    absolute terms sum_h |w| relu(s q.k) (the scale of the rounding error of
-    any float32 evaluation), both -inf / 0 outside the windows.
+    """float64 logits [R, N] (or only the given rows) and their rounding
+    scale sum_h |w| s sum_d |q k| (the sum of absolute products: the scale of
+    the error of any float32 evaluation of the dot products, whatever their
+    cancellation, and of the ReLU decision near 0), both -inf / 0 outside
+    the windows.
 
     q_codes uint8 [R, H, D], kv_codes uint8 [N, D], kv_scale float [N],
     weights float [R, H], ks / ke int [R]."""
@@ -77,7 +79,8 @@ def mqa_logits(q_codes, kv_codes, kv_scale, weights, ks, ke, rows=None):
         dots = T[q_codes[r]] @ K[lo:hi].T          # [H, n]: exact
         act = np.maximum(dots * s[lo:hi][None, :], 0.0)  # relu of the scaled score
         out[i, lo:hi] = (w[r][:, None] * act).sum(axis=0)
-        mag[i, lo:hi] = (np.abs(w[r])[:, None] * act).sum(axis=0)
+        absdots = np.abs(T[q_codes[r]]) @ np.abs(K[lo:hi]).T
+        mag[i, lo:hi] = (np.abs(w[r])[:, None] * absdots * s[lo:hi][None, :]).sum(axis=0)
     return out, mag
 
 

@@ -24,7 +24,8 @@ PA_V_PLAIN, PA_V_TRANSPOSED = range(2)
 PA_SCALE_NONE, PA_SCALE_PER_TENSOR, PA_SCALE_PER_TOKEN = range(3)
 
 EXPORTS = ["pa_plan", "pa_plan_sizes", "pa_plan_info", "pa_plan_work", "pa_plan_upload", "pa_plan_free", "pa_decode",
-           "pa_reduce", "pa_plan_refresh", "pa_attend_static", "pa_decode_sparse", "pa_last_error"]
+           "pa_reduce", "pa_plan_refresh", "pa_attend_static", "pa_decode_sparse", "pa_mqa_logits", "pa_topk",
+           "pa_last_error"]
 STATIC_SCRATCH_BYTES = 32 << 20  # PA_STATIC_SCRATCH_BYTES of include/pa_decode.h
 META_HEADER_BYTES = 32  # meta_dev starts with the plan's header; the work list follows
 
@@ -81,6 +82,10 @@ def load_library(path: str = LIB_PATH):
     L.pa_plan_refresh.argtypes = [vp] * 4
     L.pa_decode_sparse.restype = ctypes.c_int
     L.pa_decode_sparse.argtypes = [vp] * 14
+    L.pa_mqa_logits.restype = ctypes.c_int
+    L.pa_mqa_logits.argtypes = [vp] * 7 + [ctypes.c_int32] * 4 + [ctypes.c_int64, ctypes.c_int32, vp]
+    L.pa_topk.restype = ctypes.c_int
+    L.pa_topk.argtypes = [vp] * 5 + [ctypes.c_int32] * 2 + [ctypes.c_int64, ctypes.c_int32, vp]
     L.pa_attend_static.restype = ctypes.c_int
     L.pa_attend_static.argtypes = [vp] * 11
     L.pa_last_error.restype = ctypes.c_char_p
@@ -262,3 +267,51 @@ def attend(plan: Plan, out, q, k_cache, v_cache, block_tables, context_lens, k_s
     pa_decode(plan, out, q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale, sinks, stream)
     pa_reduce(plan, out, sinks, stream)
     return out
+
+
+def _dev_i32(t, name):
+    if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.int32:
+        raise ValueError(f"{name} must be a contiguous int32 device tensor")
+
+
+def pa_mqa_logits(logits, q, kv, kv_scale, weights, ks, ke, clean=True, stream=None):
+    """FP8 MQA logits (pa_indexer.h): logits float32 [rows, >= num_kv] (row
+    stride = its second dim), q uint8 FP8 codes [rows, heads, 128], kv uint8
+    [num_kv, 128], kv_scale float32 [num_kv], weights float32 [rows, heads],
+    ks / ke int32 [rows]."""
+    rows, heads, dim = q.shape
+    num_kv = kv.shape[0]
+    for t, name, dt in ((q, "q", torch.uint8), (kv, "kv", torch.uint8), (kv_scale, "kv_scale", torch.float32),
+                        (weights, "weights", torch.float32), (logits, "logits", torch.float32)):
+        if not t.is_cuda or t.dtype != dt:
+            raise ValueError(f"{name} must be a {dt} device tensor")
+        if t is not logits and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _dev_i32(ks, "ks")
+    _dev_i32(ke, "ke")
+    if kv.shape[1] != dim or weights.shape != (rows, heads) or kv_scale.shape != (num_kv,):
+        raise ValueError("q, kv, kv_scale and weights shapes disagree")
+    if ks.shape != (rows,) or ke.shape != (rows,):
+        raise ValueError("ks and ke must be [rows]")
+    if logits.dim() != 2 or logits.shape[0] != rows or logits.shape[1] < num_kv or logits.stride(1) != 1:
+        raise ValueError("logits must be [rows, >= num_kv] with unit column stride")
+    _check(load_library().pa_mqa_logits(_ptr(logits), _ptr(q), _ptr(kv), _ptr(kv_scale), _ptr(weights), _ptr(ks),
+                                        _ptr(ke), rows, num_kv, heads, dim, logits.stride(0), int(bool(clean)),
+                                        _stream_ptr(stream)))
+
+
+def pa_topk(indices, counts, logits, ks, ke, num_kv=None, stream=None):
+    """Top-k of each row's window (pa_indexer.h): indices int32 [rows, k],
+    counts int32 [rows], logits float32 [rows, >= num_kv]."""
+    rows, k = indices.shape
+    num_kv = logits.shape[1] if num_kv is None else num_kv
+    _dev_i32(indices, "indices")
+    _dev_i32(counts, "counts")
+    _dev_i32(ks, "ks")
+    _dev_i32(ke, "ke")
+    if not logits.is_cuda or logits.dtype != torch.float32 or logits.stride(1) != 1 or logits.shape[0] != rows:
+        raise ValueError("logits must be a float32 device tensor [rows, >= num_kv] with unit column stride")
+    if counts.shape != (rows,) or ks.shape != (rows,) or ke.shape != (rows,) or num_kv > logits.shape[1]:
+        raise ValueError("counts, ks and ke must be [rows]; num_kv at most logits.shape[1]")
+    _check(load_library().pa_topk(_ptr(indices), _ptr(counts), _ptr(logits), _ptr(ks), _ptr(ke), rows, num_kv,
+                                  logits.stride(0), k, _stream_ptr(stream)))

@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpa.so")
-SOURCES = ["pa_plan.cpp", "pa_kernels.hip", "pa_stream.hip", "pa_static.hip"]
+SOURCES = ["pa_plan.cpp", "pa_kernels.hip", "pa_stream.hip", "pa_static.hip", "pa_indexer.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 are generated.

@@ -471,6 +471,69 @@ def resolve_topk(inp: Inputs) -> Inputs:
     return dataclasses.replace(inp, problem=prob, block_tables=slots.contiguous(), topk_indices=None)
 
 
+@dataclasses.dataclass
+class IndexerInputs:
+    """Inputs of the indexer (FP8 MQA logits, then top-k): FP8 e4m3fn codes
+    of the query rows [rows, heads, 128] and of the KV tokens' index keys
+    [num_kv, 128], the keys' FP32 scales [num_kv], FP32 head weights
+    [rows, heads], and each row's window [ks, ke)."""
+    q: torch.Tensor
+    kv: torch.Tensor
+    kv_scale: torch.Tensor
+    weights: torch.Tensor
+    ks: torch.Tensor
+    ke: torch.Tensor
+    name: str = ""
+
+    @property
+    def rows(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def num_kv(self) -> int:
+        return self.kv.shape[0]
+
+
+def make_indexer_case(seed: int, rows: int, num_kv: int, heads: int = 64, windows: str = "full",
+                      name: str = "indexer") -> IndexerInputs:
+    """Seeded indexer inputs: queries and keys drawn N(0, 1) and quantised to
+    FP8 (keys with a per-token scale amax / 448, queries at a fixed scale of
+    32 so that they use the FP8 range), head weights N(0, 1 / heads).
+    windows: "full" (every row sees [0, num_kv)), "causal" (row r of a
+    prefill chunk ending at num_kv sees [0, num_kv - rows + r + 1)), or
+    "mixed" (a random window per row, including empty, clamped and
+    out-of-range bounds)."""
+    rq, rk, rw, rs = _streams(seed, 4)
+    D = 128
+    q = torch.from_numpy(rq.standard_normal((rows, heads, D), dtype=np.float32))
+    k = torch.from_numpy(rk.standard_normal((num_kv, D), dtype=np.float32))
+    ks = k.abs().amax(dim=1) / FP8_MAX
+    ks = torch.where(ks == 0, torch.ones_like(ks), ks)
+    w = torch.from_numpy((rw.standard_normal((rows, heads), dtype=np.float32) / np.sqrt(heads)).astype(np.float32))
+    if windows == "full":
+        lo = np.zeros(rows, np.int64)
+        hi = np.full(rows, num_kv, np.int64)
+    elif windows == "causal":
+        lo = np.zeros(rows, np.int64)
+        hi = num_kv - rows + np.arange(rows) + 1
+    else:
+        lo = rs.integers(-50, num_kv, size=rows)
+        hi = lo + rs.integers(-10, num_kv + 50, size=rows)
+        lo[:3], hi[:3] = [0, 5, num_kv - 1], [num_kv, 5, num_kv + 100]
+    return IndexerInputs(q=to_fp8_bytes(q * 32.0).contiguous(), kv=to_fp8_bytes(k / ks[:, None]).contiguous(),
+                         kv_scale=ks.contiguous(), weights=w.contiguous(),
+                         ks=torch.from_numpy(lo.astype(np.int32)), ke=torch.from_numpy(hi.astype(np.int32)),
+                         name=name)
+
+
+def config_indexer_decode() -> IndexerInputs:
+    """The indexer of the sparse decode batch (config_sparse_topk): 64 decode
+    rows, each scoring every one of its sequence's 65536 tokens with 64 FP8
+    index heads of dim 128 (the heads of the pages' indexer model shapes),
+    before the top-2048 selection."""
+    return make_indexer_case(config_seed(7), 64, 65536, heads=64, windows="full", name="indexer_decode")
+
+
 CONFIGS = {
     "tiny": config_tiny,
     "sparse": config_sparse,
