@@ -1,6 +1,7 @@
-// gfx950 streaming decode kernel for FP8 caches, head dim 128, page tables,
-// and work items of 17..64 query rows (multi-token (MTP) verify rows times a
-// GQA group): one 32-row block (RB = 1) or two (RB = 2).
+// gfx950 streaming decode kernel for FP8 caches, page tables, and work items
+// of 17..64 query rows (multi-token (MTP) verify rows times a GQA group):
+// head dim 128 with one 32-row block (RB = 1) or two (RB = 2), head dim 256
+// with one.
 //
 // Same method as the tile kernel (online softmax per partition, partials
 // merged by the reducer in a fixed order: aiter PR #4332 "Add paged-attention
@@ -55,10 +56,10 @@ constexpr float TAU_S = 15.0f;
 // largest finite value stays below 2^15).
 constexpr int VEXP_MIN = -15, VEXP_MAX = 6;
 
-template <int RB>
+template <int D, int RB>
 struct StreamSmem {
   static constexpr int ROWS = 32 * RB;
-  static constexpr int OROW = 128 + 4;  // padded O row, floats
+  static constexpr int OROW = D + 4;  // padded O row, floats
   static constexpr int OBUF = ROWS * OROW * 4;
   static constexpr int MERGE = SW * OBUF;  // one O buffer per wave
   static constexpr int IDS = kStageCap * 4;
@@ -71,11 +72,12 @@ struct StreamSmem {
   static constexpr int LAUNCH = TOTAL > 81 * 1024 ? TOTAL : 81 * 1024;
 };
 
-// Step data of one wave, loaded two steps ahead.
+// Step data of one wave, loaded NB - 1 steps ahead.
+template <int D>
 struct StepData {
-  i32x8 k[2];  // K chunks 2h, 2h+1 (dims 0..63) and 2h+4, 2h+5 (dims 64..127) of token kt
-  u32x4 v[4];  // V dim 32db + c32, tokens 16h .. 16h+15 of the step
-  float sc;    // lanes 0-31: k scale of token c32; lanes 32-63: v scale of token c32
+  i32x8 k[D / 64];  // k-step ks: K chunks 4ks + 2h, 4ks + 2h + 1 (dims 64ks + 32h .. +31) of token kt
+  u32x4 v[D / 32];  // V dim 32db + c32, tokens 16h .. 16h+15 of the step
+  float sc;         // lanes 0-31: k scale of token c32; lanes 32-63: v scale of token c32
 };
 
 
@@ -85,11 +87,18 @@ __device__ __forceinline__ i32x8 load32(const uint8_t* p0, const uint8_t* p1) {
 }
 
 // BIG: page size >= 32 (the 32 tokens of a step share one page).
-template <int RB, bool PT, bool BIG>
+template <int D, int RB, bool PT, bool BIG>
 __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
-  constexpr int D = 128;
   constexpr int TT = kTileTokens;
-  using S = StreamSmem<RB>;
+  using S = StreamSmem<D, RB>;
+  constexpr int NKS = D / 64;  // QK k-steps (64 dims each)
+  constexpr int NDB = D / 32;  // 32-dim blocks of V and O
+  // Load buffers per wave: three at head dim 128; two at 256, whose steps
+  // are twice the bytes (the same bytes in flight) and whose O accumulator
+  // is twice the registers.
+  constexpr int NB = D == 128 ? 3 : 2;
+  static_assert(D == 128 || (D == 256 && RB == 1), "head dim 256 takes one 32-row block");
+  using SD = StepData<D>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   float* obuf = (float*)smem;
   static_assert(merge_lds_bytes<D>() <= S::MERGE, "the in-kernel merge reuses the O buffers");
@@ -163,8 +172,9 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   const int32_t* bt_row = a.block_tables + (long)s * a.table_stride;
 
   // ---- the query rows' raw bits (issued first: their wait does not cover the K/V loads) ----
-  const int q_r = tid >> 2, q_qq = tid & 3;  // up to 64 rows x 4 quarters
-  const bool q_valid = q_r < nrows && q_r < StreamSmem<RB>::ROWS;
+  constexpr int QP = D / 32;                    // threads per row, 32 dims each
+  const int q_r = tid / QP, q_qq = tid % QP;    // 256 / QP rows (64 or 32)
+  const bool q_valid = q_r < nrows && q_r < S::ROWS;
   u32x4 qraw[4];
   {
     const int gr = row0 + (q_valid ? q_r : 0);
@@ -204,9 +214,9 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   const uint32_t koff = (uint32_t)((2 * h * ps + slot_k) * 16);
   const uint32_t kcs = (uint32_t)ps * 16;  // K chunk stride
   const int slot_v = (32 * w + 16 * h) & (ps - 1);
-  uint32_t voff[4];
+  uint32_t voff[NDB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
+  for (int db = 0; db < NDB; ++db) {
     const int dd = 32 * db + c32;
     voff[db] = a.v_transposed ? (uint32_t)(((slot_v >> 4) * D + dd) * 16) : (uint32_t)(dd * ps + slot_v);
   }
@@ -218,18 +228,18 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   struct StepPages {
     long a, b;
   };
-  auto load_k = [&](StepData& d, StepPages id) {
+  auto load_k = [&](SD& d, StepPages id) {
     if constexpr (BIG) {
       const uint8_t* kp = kbase + id.a * a.page_stride;
-      d.k[0] = load32(kp + koff, kp + koff + kcs);
-      d.k[1] = load32(kp + koff + 4 * kcs, kp + koff + 5 * kcs);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) d.k[ks] = load32(kp + koff + 4 * ks * kcs, kp + koff + (4 * ks + 1) * kcs);
       if constexpr (PT) d.sc = *(const float*)((const uint8_t*)(sbase + id.a * a.Hkv * ps) + soff);
     } else {
       // page 16: token kt of the step is slot kt & 15 of its first or second page
       const long idk = kt >= 16 ? id.b : id.a;
       const uint8_t* src = kbase + idk * a.page_stride + (long)(kt & 15) * 16;
-      d.k[0] = load32(src + (2 * h) * kcs, src + (2 * h + 1) * kcs);
-      d.k[1] = load32(src + (2 * h + 4) * kcs, src + (2 * h + 5) * kcs);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) d.k[ks] = load32(src + (2 * h + 4 * ks) * kcs, src + (2 * h + 4 * ks + 1) * kcs);
       if constexpr (PT) {
         const long ids_ = c32 >= 16 ? id.b : id.a;
         d.sc = sbase[(ids_ * a.Hkv + kvh) * ps + (c32 & 15)];
@@ -237,15 +247,15 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     }
     if constexpr (!PT) d.sc = 0.f;
   };
-  auto load_v = [&](StepData& d, StepPages id) {
+  auto load_v = [&](SD& d, StepPages id) {
     if constexpr (BIG) {
       const uint8_t* vp = vbase + id.a * a.page_stride;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) d.v[db] = *(const u32x4*)(vp + voff[db]);
+      for (int db = 0; db < NDB; ++db) d.v[db] = *(const u32x4*)(vp + voff[db]);
     } else {
       const uint8_t* pg = vbase + (h ? id.b : id.a) * a.page_stride;  // the lane's 16 tokens: one page
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < NDB; ++db) {
         const uint8_t* src = pg + (long)(32 * db + c32) * 16;  // page 16: both V layouts put a dim's 16 bytes here
         d.v[db] = *(const u32x4*)src;
       }
@@ -264,18 +274,20 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   // Unconditional, so that the compiler's wait counts stay exact: an empty
   // item (tb >= te) reads page 0 of its head, which exists (the host routes
   // caches without pages elsewhere), and never uses the data.
-  StepData ba, bb, bc;
+  SD ba, bb, bc;  // bc: three buffers only
   {
     const int k1 = min(tb + 1, te - 1), k2 = min(tb + 2, te - 1);
     const StepPages p0 = step_pages_direct(tb);
     const StepPages p1 = step_pages_direct(k1);
-    const StepPages p2 = step_pages_direct(k2);
     load_k(ba, p0);
     load_v(ba, p0);
     load_k(bb, p1);
     load_v(bb, p1);
-    load_k(bc, p2);
-    load_v(bc, p2);
+    if constexpr (NB == 3) {
+      const StepPages p2 = step_pages_direct(k2);
+      load_k(bc, p2);
+      load_v(bc, p2);
+    }
   }
 
   // ---- query operand: two FP8 terms per row with a power-of-two scale ----
@@ -290,8 +302,8 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   // of k-step ks holds dims 64ks + 32h .. +31, the same dims as its K
   // operand; every wave then keeps all of the item's fragments in
   // accumulator registers.
-  uint8_t* qlds = smem;  // [RB][2 ks][2 terms][64 lanes][32 B]; the merge buffers reuse it after the loop
-  int* qexp = (int*)(smem + RB * 2 * 2 * 64 * 32);  // [ROWS] E8M0 of the hi term
+  uint8_t* qlds = smem;  // [RB][NKS ks][2 terms][64 lanes][32 B]; the merge buffers reuse it after the loop
+  int* qexp = (int*)(smem + RB * NKS * 2 * 64 * 32);  // [ROWS] E8M0 of the hi term
   {
     const float cbase = a.scale_log2 * (PT ? 1.0f : a.k_scale[0]);
     const int r = q_r, qq = q_qq;
@@ -309,8 +321,9 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     float amax = 0.f;
 #pragma unroll
     for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(qv[j]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1));  // the row's four quarters are adjacent lanes
+    amax = fmaxf(amax, __shfl_xor(amax, 1));  // the row's QP parts are adjacent lanes
     amax = fmaxf(amax, __shfl_xor(amax, 2));
+    if constexpr (QP == 8) amax = fmaxf(amax, __shfl_xor(amax, 4));
     const float cq = amax * cbase;
     int e = 0;
     float mul = 0.f;
@@ -322,7 +335,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     }
     if (qq == 0 && r < S::ROWS) qexp[r] = 127 + e;
     const int rb = r >> 5, ks = qq >> 1, hh = qq & 1;
-    uint8_t* dst = qlds + ((size_t)((rb * 2 + ks) * 2) * 64 + 32 * hh + (r & 31)) * 32;
+    uint8_t* dst = qlds + ((size_t)((rb * NKS + ks) * 2) * 64 + 32 * hh + (r & 31)) * 32;
     if (r < S::ROWS) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -354,15 +367,15 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   }
   __syncthreads();
   int qsc[RB];
-  i32x8 qf[RB][2][2];
+  i32x8 qf[RB][NKS][2];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     qsc[rb] = qexp[32 * rb + c32];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const uint8_t* src = qlds + ((size_t)((rb * 2 + ks) * 2 + t) * 64 + lane) * 32;
+        const uint8_t* src = qlds + ((size_t)((rb * NKS + ks) * 2 + t) * 64 + lane) * 32;
         const u32x4 lo = *(const u32x4*)src, hi = *(const u32x4*)(src + 16);
         qf[rb][ks][t] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         asm volatile("" : "+a"(qf[rb][ks][t]));  // kept in accumulator registers for the whole loop
@@ -381,7 +394,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   // sum_t p_t * v_scale(t) * v_t for per-token scales and sum_t p_t v_t for a
   // per-tensor scale (applied at the end).
   float m_ref[RB], m_hi[RB], l_acc[RB];
-  f32x16 o[RB][4];
+  f32x16 o[RB][NDB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     m_ref[rb] = valid[rb] ? -INFINITY : 0.f;
@@ -445,7 +458,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   float vconv = 1.0f, vsmax = 1.0f;
   // V scales of tokens outside the visible span (their bytes may be
   // anything) count as 0, in the maximum and in LDS.
-  auto prep = [&](const StepData& nb, int kk) {
+  auto prep = [&](const SD& nb, int kk) {
     if constexpr (PT) {
       const int t = t0 + kk * TT + 32 * w + c32;
       const float vsc = (kk < te && t >= lo_u && t < hi_u) ? nb.sc : 0.f;
@@ -463,20 +476,20 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     }
   };
 
-  auto step = [&](auto GENc, StepData& cur, const StepData& nxt, int k) __attribute__((always_inline)) -> bool {
+  auto step = [&](auto GENc, SD& cur, const SD& nxt, int k) __attribute__((always_inline)) -> bool {
     constexpr bool gen = decltype(GENc)::value;
-    if (k >= te) return true;  // padding of the last group of three: nothing to do
+    if (k >= te) return true;  // padding of the last group of NB: nothing to do
     const int tsa = t0 + k * TT + 32 * w;  // first token of the step
     const int tl = tsa + 16 * h;           // first of the lane's 16 tokens
     const int span_lo = lo_u, span_hi = hi_u;  // tokens whose V may be used
-    const int kn = min(k + 3, te - 1);
+    const int kn = min(k + NB, te - 1);
     const StepPages nid = step_page(kn);
 
     // V of the step; tokens outside the visible span get zero V (their bytes
     // may be anything, and 0 * NaN would reach O)
-    u32x4 vv[4];
+    u32x4 vv[NDB];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) vv[db] = cur.v[db];
+    for (int db = 0; db < NDB; ++db) vv[db] = cur.v[db];
     if constexpr (gen) {
       const int va = min(max(span_lo - tl, 0), 16), vb = min(max(span_hi - tl, 0), 16);
 #pragma unroll
@@ -488,7 +501,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
           if (t >= va && t < vb) m |= 0xFFu << (8 * b);
         }
 #pragma unroll
-        for (int db = 0; db < 4; ++db) vv[db][q] &= m;
+        for (int db = 0; db < NDB; ++db) vv[db][q] &= m;
       }
     }
 
@@ -499,16 +512,16 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < NKS; ++ks)
           acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.k[ks], qf[rb][ks][t], acc, 0, 0, 0, 127, 0,
                                                                 qsc[rb] - 4 * t);
       return acc;
     };
     // V in FP16 (times 2^E): k-block kb of dim 32db + c32 = tokens 16h + 8kb .. +7
-    half8 vb[4][2];
+    half8 vb[NDB][2];
     auto vcvt = [&]() {
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const uint32_t d0 = vv[db][2 * kb], d1 = vv[db][2 * kb + 1];
@@ -604,7 +617,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     };
     auto pv = [&](int rb, const half8 (&pb)[2]) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
           o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[db][kb], pb[kb], o[rb][db], 0, 0, 0);
@@ -649,9 +662,9 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     return !__builtin_amdgcn_ballot_w64(ovf);
   };
 
-  // One pass of this wave over the item, three steps per iteration with one
-  // load buffer each (a count that is not a multiple of three ends with one
-  // or two steps that return at once).  An overflow stops it at the top of
+  // One pass of this wave over the item, NB steps per iteration with one
+  // load buffer each (a count that is not a multiple of NB ends with steps
+  // that return at once).  An overflow stops it at the top of
   // the next group (a single latch keeps each O accumulator in place across
   // iterations), except in the scan pass, which runs to the end.
   auto attempt = [&](bool first) __attribute__((always_inline)) -> bool {
@@ -659,10 +672,10 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     for (int rb = 0; rb < RB; ++rb) {
       l_acc[rb] = 0.f;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[rb][db] = f32x16{};
+      for (int db = 0; db < NDB; ++db) o[rb][db] = f32x16{};
     }
     if (tb >= te) return true;
-    if (!first) {  // a restart: the first three steps' loads again
+    if (!first) {  // a restart: the first NB steps' loads again
       const StepPages p0 = step_page(tb);
       load_k(ba, p0);
       load_v(ba, p0);
@@ -670,38 +683,44 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
       const StepPages p1 = step_page(k1);
       load_k(bb, p1);
       load_v(bb, p1);
-      const int k2 = min(tb + 2, te - 1);
-      const StepPages p2 = step_page(k2);
-      load_k(bc, p2);
-      load_v(bc, p2);
+      if constexpr (NB == 3) {
+        const int k2 = min(tb + 2, te - 1);
+        const StepPages p2 = step_page(k2);
+        load_k(bc, p2);
+        load_v(bc, p2);
+      }
     }
     prep(ba, tb);
-    // Groups of three steps: boundary groups (masks, reference updates)
-    // until the interior tiles are reached with every row's reference set,
-    // interior groups, then boundary groups again.  Each loop is entered with
-    // nothing in flight beyond its three buffers' loads, which keeps the
-    // compiler's wait counts exact inside it.
+    // Groups of NB steps: boundary groups (masks, reference updates) until
+    // the interior tiles are reached with every row's reference set, interior
+    // groups, then boundary groups again.  Each loop is entered with nothing
+    // in flight beyond its NB buffers' loads, which keeps the compiler's wait
+    // counts exact inside it.
     bool go = true;  // wave-uniform
     int k = tb;
     auto triple = [&](auto GENc) __attribute__((always_inline)) {
       go = step(GENc, ba, bb, k);
       __builtin_amdgcn_sched_barrier(0);  // the steps do not interleave (registers)
-      go = step(GENc, bb, bc, k + 1) && go;
-      __builtin_amdgcn_sched_barrier(0);
-      go = step(GENc, bc, ba, k + 2) && go;
+      if constexpr (NB == 3) {
+        go = step(GENc, bb, bc, k + 1) && go;
+        __builtin_amdgcn_sched_barrier(0);
+        go = step(GENc, bc, ba, k + 2) && go;
+      } else {
+        go = step(GENc, bb, ba, k + 1) && go;
+      }
       __builtin_amdgcn_sched_barrier(0);
       go = go || scan;
-      k += 3;
+      k += NB;
     };
     if (first) {
       for (; k < te && go;) {
         bool need_ref = false;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) need_ref |= m_ref[rb] == -INFINITY;
-        if (k >= ti0 && k + 2 < ti1 && !__builtin_amdgcn_ballot_w64(need_ref)) break;
+        if (k >= ti0 && k + NB - 1 < ti1 && !__builtin_amdgcn_ballot_w64(need_ref)) break;
         triple(std::true_type{});
       }
-      for (; k + 2 < ti1 && go;) triple(std::false_type{});
+      for (; k + NB - 1 < ti1 && go;) triple(std::false_type{});
     }
     for (; k < te && go;) triple(std::true_type{});  // a restart runs every step with the masks
     return !__builtin_amdgcn_ballot_w64(ovf);
@@ -760,7 +779,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     for (int rb = 0; rb < RB; ++rb) {
       const int r = 32 * rb + c32;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           *(f4*)(ob + r * S::OROW + 32 * db + 8 * q + 4 * h) =
@@ -845,20 +864,20 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   }
 }
 
-template <int RB, bool PT, bool BIG>
+template <int D, int RB, bool PT, bool BIG>
 static pa_status launch_stream_t(const KernelArgs& args, int nblocks, hipStream_t stream) {
-  constexpr int bytes = StreamSmem<RB>::LAUNCH;
+  constexpr int bytes = StreamSmem<D, RB>::LAUNCH;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   static bool configured = false;
   if (!configured) {
-    if (hipFuncSetAttribute((const void*)pa_stream_kernel<RB, PT, BIG>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    if (hipFuncSetAttribute((const void*)pa_stream_kernel<D, RB, PT, BIG>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             bytes) != hipSuccess) {
       (void)hipGetLastError();
       return set_error(PA_ERR_DEVICE, "hipFuncSetAttribute failed");
     }
     configured = true;
   }
-  hipLaunchKernelGGL((pa_stream_kernel<RB, PT, BIG>), dim3(nblocks), dim3(256), bytes, stream, args);
+  hipLaunchKernelGGL((pa_stream_kernel<D, RB, PT, BIG>), dim3(nblocks), dim3(256), bytes, stream, args);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(PA_ERR_DEVICE, std::string("decode launch failed: ") + hipGetErrorString(err));
   return PA_OK;
@@ -866,21 +885,24 @@ static pa_status launch_stream_t(const KernelArgs& args, int nblocks, hipStream_
 
 bool stream_kernel_applies(const Plan& P) {
   const pa_problem& p = P.prob;
-  return p.kv_dtype == PA_FP8_E4M3FN && p.head_dim == 128 && !p.token_table && P.rows_per_group > 16 &&
-         p.num_pages > 0;
+  return p.kv_dtype == PA_FP8_E4M3FN && !p.token_table && P.rows_per_group > 16 && p.num_pages > 0 &&
+         (p.head_dim == 128 || (p.head_dim == 256 && P.rows_per_group <= 32));
 }
 
-template <int RB>
+template <int D, int RB>
 static pa_status launch_stream_rb(const Plan& P, const KernelArgs& args, int nblocks, hipStream_t stream) {
   const bool pt = P.prob.scale_mode == PA_SCALE_PER_TOKEN;
   if (P.prob.page_size >= 32)
-    return pt ? launch_stream_t<RB, true, true>(args, nblocks, stream) : launch_stream_t<RB, false, true>(args, nblocks, stream);
-  return pt ? launch_stream_t<RB, true, false>(args, nblocks, stream) : launch_stream_t<RB, false, false>(args, nblocks, stream);
+    return pt ? launch_stream_t<D, RB, true, true>(args, nblocks, stream)
+              : launch_stream_t<D, RB, false, true>(args, nblocks, stream);
+  return pt ? launch_stream_t<D, RB, true, false>(args, nblocks, stream)
+            : launch_stream_t<D, RB, false, false>(args, nblocks, stream);
 }
 
 pa_status launch_stream(const Plan& P, const KernelArgs& args, int nblocks, hipStream_t stream) {
-  return P.rows_per_group > 32 ? launch_stream_rb<2>(P, args, nblocks, stream)
-                               : launch_stream_rb<1>(P, args, nblocks, stream);
+  if (P.prob.head_dim == 256) return launch_stream_rb<256, 1>(P, args, nblocks, stream);
+  return P.rows_per_group > 32 ? launch_stream_rb<128, 2>(P, args, nblocks, stream)
+                               : launch_stream_rb<128, 1>(P, args, nblocks, stream);
 }
 
 }  // namespace pa

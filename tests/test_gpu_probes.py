@@ -131,11 +131,14 @@ def test_planted_digits_fp8(rows, page, vt, scale):
     assert n >= 8
 
 
-@pytest.mark.parametrize("ql,window", [(1, 0), (4, 0), (2, 33)])
+@pytest.mark.parametrize("ql,window,page", [(1, 0, 64), (4, 0, 64), (2, 33, 64), (4, 33, 64), (3, 0, 16), (4, 0, 16)])
 @pytest.mark.parametrize("vt", [False, True])
-def test_planted_digits_d256(ql, window, vt):
-    announce(f"planted digits d256 ql={ql} w={window} vt={vt}")
-    _dense_probe(ql, 16, 2, 256, 64, vt, "token" if ql == 4 else "tensor", window=window, seed=340 + ql + window)
+def test_planted_digits_d256(ql, window, page, vt):
+    """Head dim 256: 8 and 16 rows per KV head in the tile kernel, 24 and 32
+    in the streaming kernel."""
+    announce(f"planted digits d256 ql={ql} w={window} page={page} vt={vt}")
+    _dense_probe(ql, 16, 2, 256, page, vt, "token" if ql >= 3 else "tensor", window=window,
+                 seed=340 + ql + window + page)
 
 
 @pytest.mark.parametrize("page,vt,ql", [(16, False, 1), (128, True, 4), (64, False, 2)])

@@ -96,6 +96,8 @@ CASES = [
     ("stream64-token-p16", 4, 16, 1, 128, 16, "fp8", "token", "token"),
     ("stream64-stairs", 4, 16, 1, 128, 128, "fp8", "tensor", "stairs"),
     ("d256-stairs", 4, 16, 2, 256, 64, "fp8", "tensor", "stairs"),
+    ("d256-stream-token", 4, 16, 2, 256, 64, "fp8", "token", "token"),
+    ("d256-stream-token-p16", 3, 16, 2, 256, 16, "fp8", "token", "token"),
     ("d256-token", 1, 8, 1, 256, 16, "fp8", "token", "token"),
     ("bf16-keys", 1, 8, 1, 128, 16, "bf16", "none", "bf16"),
     ("bf16-keys-64rows", 4, 16, 1, 128, 128, "bf16", "none", "bf16"),
@@ -115,13 +117,14 @@ def test_climbing_logits(case):
         compare(got, ref, f"{name} {kw}")
 
 
-@pytest.mark.parametrize("ql,page", [(4, 128), (2, 64), (1, 16)])
-def test_climbing_v_scales(ql, page):
+@pytest.mark.parametrize("ql,page,d", [(4, 128, 128), (2, 64, 128), (1, 16, 128), (4, 64, 256), (4, 16, 256)])
+def test_climbing_v_scales(ql, page, d):
     """Per-token V scales climbing to 2^100 (the V-scale band of the tile
     kernel and the clamped V exponent of the streaming kernel restart again
     and again); each (row, head) output is compared after dividing both
     sides by the largest magnitude of the oracle's output for it."""
-    inp = W.make_dense_case(560 + ql + page, LENS, query_len=ql, num_q_heads=16, num_kv_heads=1, head_dim=128,
+    hkv = 1 if d == 128 else 2  # head dim 256: 32 rows per KV head (the streaming kernel's one row block)
+    inp = W.make_dense_case(560 + ql + page + d, LENS, query_len=ql, num_q_heads=16, num_kv_heads=hkv, head_dim=d,
                             page_size=page, scale_mode="token", fill="context", name="vramp")
     _ramp_vscales(inp)
     ref = O.attend(inp)
@@ -129,6 +132,6 @@ def test_climbing_v_scales(ql, page):
     big[big == 0] = 1.0
     ref = ref / big
     for kw in (dict(cu_count=4, max_partitions=1), dict(cu_count=64)):
-        announce(f"climbing V scales rows={16 * ql} page={page} {kw}")
+        announce(f"climbing V scales d={d} rows={16 * ql // hkv} page={page} {kw}")
         got, _ = run(inp, **kw)
-        compare(got / big, ref, f"V-scale ramp rows={16 * ql} {kw}")
+        compare(got / big, ref, f"V-scale ramp d={d} rows={16 * ql // hkv} {kw}")
