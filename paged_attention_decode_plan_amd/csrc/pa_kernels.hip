@@ -217,7 +217,7 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
     const long k = min((long)(tid + NTHREADS * j), (long)max(nstaged - 1, 0));
     idr[j] = (int32_t)raw_id(min(max(id0 + k, 0L), id_rowlen - 1));  // in the row whatever the item
   }
-  constexpr int NQR = FP8 ? (D / 128) * 4 : D / 32;  // 16-byte query loads per row tile
+  constexpr int NQR = FP8 ? ((D + 127) / 128) * 4 : D / 32;  // 16-byte query loads per row tile
   u32x4 qraw[NRW][NQR];
 #pragma unroll
   for (int rt = 0; rt < NRW; ++rt) {
@@ -227,7 +227,8 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
     const uint16_t* qrow = (const uint16_t*)a.q + (((long)s * a.QL + i) * a.Hq + (long)kvh * a.G + hl) * D;
 #pragma unroll
     for (int x = 0; x < NQR; ++x)
-      qraw[rt][x] = FP8 ? *(const u32x4*)(qrow + 128 * (x / 4) + 32 * g + 8 * (x % 4))
+      qraw[rt][x] = FP8 ? (32 * g < D ? *(const u32x4*)(qrow + 128 * (x / 4) + 32 * g + 8 * (x % 4))
+                                      : u32x4{0, 0, 0, 0})  // head dim 64: lane groups 2, 3 hold no dims
                         : *(const u32x4*)(qrow + 32 * x + 8 * g);
   }
   const bool per_token = FP8 && a.scale_mode == PA_SCALE_PER_TOKEN;
@@ -350,7 +351,7 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   // holds d = 128kk + 32g .. +31 (K chunks 8kk+2g and 8kk+2g+1).
   // BF16 caches: BF16 MFMA with q as given; d of step m, lane group g, slot p
   // is 32m + 8g + p.
-  constexpr int NQ = FP8 ? D / 128 : NM;  // QK k-steps
+  constexpr int NQ = FP8 ? (D + 127) / 128 : NM;  // QK k-steps (head dim 64: one, half of it zero)
   using QFrag = typename std::conditional<FP8, i32x8, bf16x8>::type;
   QFrag qf[NRW][NQ][FP8 ? 3 : 1];
   float crow[NRW];  // log2-domain score scale of the row (incl. the query scale)
@@ -592,8 +593,11 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
       if constexpr (FP8) {
 #pragma unroll
         for (int kk = 0; kk < NQ; ++kk) {
-          const u32x4 k0 = *(const u32x4*)(krow + (8 * kk + 2 * g) * TT * 16);
-          const u32x4 k1 = *(const u32x4*)(krow + (8 * kk + 2 * g + 1) * TT * 16);
+          // head dim 64: lane groups 2, 3 would read past the K tile; their
+          // operand dims are zero (as are the query's)
+          const bool kin = D >= 128 || 32 * g < D;
+          const u32x4 k0 = kin ? *(const u32x4*)(krow + (8 * kk + 2 * g) * TT * 16) : u32x4{0, 0, 0, 0};
+          const u32x4 k1 = kin ? *(const u32x4*)(krow + (8 * kk + 2 * g + 1) * TT * 16) : u32x4{0, 0, 0, 0};
           const i32x8 kf = i32x8{(int)k0[0], (int)k0[1], (int)k0[2], (int)k0[3],
                                  (int)k1[0], (int)k1[1], (int)k1[2], (int)k1[3]};
 #pragma unroll
@@ -1280,9 +1284,11 @@ static pa_status decode_impl(const pa_plan_t* plan, void* out, const void* q, co
   const bool sparse = p.token_table != 0;
   if (stream_kernel_applies(P)) return launch_stream(P, args, n, st);
   if (p.kv_dtype == PA_FP8_E4M3FN) {
+    if (p.head_dim == 64) return launch_nrt<64, true>(P.nrt, sparse, args, n, st);
     if (p.head_dim == 128) return launch_nrt<128, true>(P.nrt, sparse, args, n, st);
     return launch_nrt<256, true>(P.nrt, sparse, args, n, st);
   }
+  if (p.head_dim == 64) return launch_nrt<64, false>(P.nrt, sparse, args, n, st);
   return launch_nrt<128, false>(P.nrt, sparse, args, n, st);
 }
 
@@ -1368,11 +1374,13 @@ extern "C" pa_status pa_reduce(const pa_plan_t* plan, void* out, const float* si
   ra.rows_per_group = P.rows_per_group;
   ra.q_fp16 = P.prob.q_dtype == PA_FP16;
   ra.has_sinks = P.prob.has_sinks;
-  const int rr = P.prob.head_dim == 256 ? merge_rows<256>() : merge_rows<128>();
+  const int rr = P.prob.head_dim == 256 ? merge_rows<256>() : P.prob.head_dim == 64 ? merge_rows<64>() : merge_rows<128>();
   ra.chunks_per_entry = (P.rows_per_group + rr - 1) / rr;
   const unsigned grid = (unsigned)(P.reduce.size() * ra.chunks_per_entry);
   if (P.prob.head_dim == 256)
     hipLaunchKernelGGL(pa_reduce_kernel<256>, dim3(grid), dim3(256), 0, (hipStream_t)stream, ra);
+  else if (P.prob.head_dim == 64)
+    hipLaunchKernelGGL(pa_reduce_kernel<64>, dim3(grid), dim3(256), 0, (hipStream_t)stream, ra);
   else
     hipLaunchKernelGGL(pa_reduce_kernel<128>, dim3(grid), dim3(256), 0, (hipStream_t)stream, ra);
   hipError_t err = hipGetLastError();

@@ -71,16 +71,16 @@ pa_status validate_problem(const pa_problem* p) {
   double cache_elems = (double)p->num_pages * p->num_kv_heads * p->page_size * p->head_dim;
   if (cache_elems > (double)(1ull << 40)) return set_error(PA_ERR_INVALID, "cache larger than 2^40 elements");
   // Valid but not implemented here.
-  if (p->head_dim != 128 && p->head_dim != 256)
-    return set_error(PA_ERR_UNSUPPORTED, "head_dim must be 128 or 256");
-  if (p->page_size != 16 && p->page_size != 64 && p->page_size != 128)
-    return set_error(PA_ERR_UNSUPPORTED, "page_size must be 16, 64 or 128");
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
+    return set_error(PA_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256");
+  if (p->page_size != 16 && p->page_size != 32 && p->page_size != 64 && p->page_size != 128)
+    return set_error(PA_ERR_UNSUPPORTED, "page_size must be 16, 32, 64 or 128");
   if (p->kv_dtype == PA_FP8_E4M3FN && p->scale_mode == PA_SCALE_NONE)
     return set_error(PA_ERR_UNSUPPORTED, "FP8 caches need a per-tensor or per-token scale");
   if (p->kv_dtype == PA_BF16 && p->scale_mode != PA_SCALE_NONE)
     return set_error(PA_ERR_UNSUPPORTED, "BF16 caches take no dequant scale");
-  if (p->kv_dtype == PA_BF16 && p->head_dim != 128)
-    return set_error(PA_ERR_UNSUPPORTED, "BF16 caches support head_dim 128 only");
+  if (p->kv_dtype == PA_BF16 && p->head_dim == 256)
+    return set_error(PA_ERR_UNSUPPORTED, "BF16 caches support head_dim 64 and 128");
   if (p->kv_dtype == PA_BF16 && p->q_dtype != PA_BF16)
     return set_error(PA_ERR_UNSUPPORTED, "BF16 caches need BF16 queries");
   if (p->token_table && (p->sliding_window > 0 || p->query_len != 1))

@@ -45,7 +45,7 @@ def _prob(**kw):
     (dict(num_q_heads=6, num_kv_heads=4), ValueError),
     (dict(sliding_window=-1), ValueError),
     (dict(head_dim=96), NotImplementedError),
-    (dict(page_size=32), NotImplementedError),
+    (dict(page_size=48), NotImplementedError),
     (dict(scale_mode="none"), NotImplementedError),
     (dict(kv_dtype="bf16"), NotImplementedError),  # BF16 with a scale
     (dict(kv_dtype="bf16", scale_mode="none", head_dim=256), NotImplementedError),

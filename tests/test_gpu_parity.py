@@ -41,7 +41,7 @@ def test_tiny(vt, maxp):
         assert plan.info().num_slots == 0
 
 
-@pytest.mark.parametrize("page", [16, 64, 128])
+@pytest.mark.parametrize("page", [16, 32, 64, 128])
 @pytest.mark.parametrize("vt", [False, True])
 @pytest.mark.parametrize("scale", ["tensor", "token"])
 def test_matrix_fp8(page, vt, scale):
@@ -58,7 +58,7 @@ def test_matrix_fp8(page, vt, scale):
         seed += 1
 
 
-@pytest.mark.parametrize("page", [16, 64, 128])
+@pytest.mark.parametrize("page", [16, 32, 64, 128])
 def test_matrix_bf16(page):
     seed = 2000 + page
     for ql, window, sinks, vt, (hq, hkv) in itertools.product([1, 4], [0, 17], [False, True], [False, True],
@@ -67,6 +67,26 @@ def test_matrix_bf16(page):
                                 page_size=page, kv_dtype="bf16", v_transposed=vt, sliding_window=window,
                                 has_sinks=sinks)
         announce(f"bf16 page={page} vt={vt} ql={ql} w={window} sinks={sinks} hq={hq}")
+        _parity(inp, cu_count=64)
+        seed += 1
+
+
+@pytest.mark.parametrize("kv,scale", [("fp8", "tensor"), ("fp8", "token"), ("bf16", "none")])
+@pytest.mark.parametrize("page", [16, 32, 64, 128])
+def test_d64(kv, scale, page):
+    """Head dim 64 in every scale mode (FP8 caches with per-tensor and
+    per-token scales, BF16 caches): 8 to 64 rows per KV head, windows,
+    sinks, plain and transposed V, BF16 and FP16 queries."""
+    seed = 4000 + page + 7 * (scale == "token") + 13 * (kv == "bf16")
+    cases = [(1, 8, 1, 0, False, False, "bf16"), (2, 16, 2, 17, True, True, "fp16"), (4, 16, 2, 0, False, True, "bf16"),
+             (4, 16, 1, 257, True, False, "bf16"), (3, 8, 1, 1, False, False, "fp16")]
+    for ql, hq, hkv, window, sinks, vt, qd in cases:
+        if kv == "bf16":
+            qd = "bf16"  # BF16 caches take BF16 queries
+        inp = W.make_dense_case(seed, LENS, query_len=ql, num_q_heads=hq, num_kv_heads=hkv, head_dim=64,
+                                page_size=page, kv_dtype=kv, q_dtype=qd, v_transposed=vt, scale_mode=scale,
+                                sliding_window=window, has_sinks=sinks)
+        announce(f"d64 {kv} {scale} page={page} ql={ql} hq={hq} hkv={hkv} w={window} sinks={sinks} vt={vt} q={qd}")
         _parity(inp, cu_count=64)
         seed += 1
 

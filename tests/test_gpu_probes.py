@@ -123,7 +123,7 @@ ROWS = {16: (1, 16), 32: (2, 16), 64: (4, 16)}
 
 
 @pytest.mark.parametrize("rows", [16, 32, 64])
-@pytest.mark.parametrize("page,vt,scale", list(itertools.product([16, 64, 128], [False, True], ["tensor", "token"])))
+@pytest.mark.parametrize("page,vt,scale", list(itertools.product([16, 32, 64, 128], [False, True], ["tensor", "token"])))
 def test_planted_digits_fp8(rows, page, vt, scale):
     ql, hq = ROWS[rows]
     announce(f"planted digits fp8 rows={rows} page={page} vt={vt} scale={scale}")
@@ -139,6 +139,13 @@ def test_planted_digits_d256(ql, window, page, vt):
     announce(f"planted digits d256 ql={ql} w={window} page={page} vt={vt}")
     _dense_probe(ql, 16, 2, 256, page, vt, "token" if ql >= 3 else "tensor", window=window,
                  seed=340 + ql + window + page)
+
+
+@pytest.mark.parametrize("kv,scale", [("fp8", "tensor"), ("fp8", "token"), ("bf16", "none")])
+@pytest.mark.parametrize("ql,page,vt", [(1, 16, False), (4, 64, True), (2, 32, False)])
+def test_planted_digits_d64(kv, scale, ql, page, vt):
+    announce(f"planted digits d64 {kv} {scale} ql={ql} page={page} vt={vt}")
+    _dense_probe(ql, 16, 1, 64, page, vt, scale, kv=kv, seed=380 + ql + page + (scale == "token"))
 
 
 @pytest.mark.parametrize("page,vt,ql", [(16, False, 1), (128, True, 4), (64, False, 2)])

@@ -100,6 +100,8 @@ CASES = [
     ("d256-stream-token-p16", 3, 16, 2, 256, 16, "fp8", "token", "token"),
     ("d256-token", 1, 8, 1, 256, 16, "fp8", "token", "token"),
     ("bf16-keys", 1, 8, 1, 128, 16, "bf16", "none", "bf16"),
+    ("d64-token", 4, 16, 1, 64, 64, "fp8", "token", "token"),
+    ("d64-bf16-keys", 2, 16, 1, 64, 16, "bf16", "none", "bf16"),
     ("bf16-keys-64rows", 4, 16, 1, 128, 128, "bf16", "none", "bf16"),
 ]
 
