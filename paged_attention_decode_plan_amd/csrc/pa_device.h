@@ -46,7 +46,11 @@ struct KernelArgs {
   int* merge_ctr;  // arrival counters of the in-kernel merge, else NULL (the reducer merges)
   long long page_stride;  // bytes between physical pages (Hkv * D * page * elem)
   long long head_stride;  // bytes between KV heads of a page (D * page * elem)
-  int QL, Hq, Hkv, G, page_size, table_stride, window, causal;
+  // page_size: the page size the kernels index tokens by.  Pages above 128
+  // tokens are taken as 2^page_sub sub-pages of 128 (dense caches): a
+  // sub-page id is (block-table entry << page_sub) | sub-page, and strides
+  // inside a page use the physical size phys_page.
+  int QL, Hq, Hkv, G, page_size, page_sub, phys_page, table_stride, window, causal;
   int v_transposed, scale_mode, q_fp16, has_sinks, rows_total, rows_per_group, stage_limit, index_stride;
   float scale_log2;  // softmax_scale * log2(e)
 };

@@ -141,10 +141,12 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   if (!meta_ok(mh, a.tag_lo, a.tag_hi)) return;  // not this plan's list: touch nothing
   if (it.seq < 0) return;  // an unused item of a refreshable plan
   const int s = it.seq, kvh = it.kvh, rg = it.rg;
-  const int ps = a.page_size;
+  const int ps = a.page_size;    // tokens per (sub-)page the item is indexed by
+  const int pps = a.phys_page;   // physical page size: strides inside a page
+  const int psub = a.page_sub;   // sub-pages per page = 2^psub (0 up to 128 tokens)
   const int ps_log2 = 31 - __builtin_clz(ps);
   // sparse rows: the row's slots (or, two-level, its top-k positions) count
-  const long cap = SPARSE ? (long)(a.topk ? a.index_stride : a.table_stride) : (long)a.table_stride * ps;
+  const long cap = SPARSE ? (long)(a.topk ? a.index_stride : a.table_stride) : (long)a.table_stride * pps;
   const int L = (int)min(max((long)a.context_lens[s], 0L), cap);
 
   // Visible span of the sequence (union over its query rows).
@@ -198,14 +200,16 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   // (two-level sparse: clamped to the table's extent, so the page id read
   // stays in the row).
   const int32_t* tk_row = (SPARSE && a.topk) ? a.topk + (long)s * a.index_stride : nullptr;
+  // (sub-)page id j of a dense row: its page's entry and the sub-page
+  auto sub_id = [&](long j) -> long { return ((long)bt_row[j >> psub] << psub) | (j & ((1L << psub) - 1)); };
   auto raw_id = [&](long j) -> long {
     if (SPARSE && tk_row) {
       const long P = min(max((long)tk_row[j], 0L), (long)a.table_stride * ps - 1);
       return ((long)bt_row[P >> ps_log2] << ps_log2) + (P & (ps - 1));
     }
-    return (long)bt_row[j];
+    return SPARSE ? (long)bt_row[j] : sub_id(j);
   };
-  const long id_rowlen = (SPARSE && tk_row) ? (long)a.index_stride : (long)a.table_stride;
+  const long id_rowlen = (SPARSE && tk_row) ? (long)a.index_stride : (long)a.table_stride << (SPARSE ? 0 : psub);
   // ---- the item's first reads, issued before the query is prepared ----
   // The page ids (staged in LDS after the query split), the query rows'
   // raw bits and then the first tiles' DMA with page ids read straight from
@@ -248,14 +252,23 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   constexpr int VRS = NTHREADS / T::VUPR;  // V rows covered per k step
   const int k_tok = kswz(tid % TT);
   const int k_pg = k_tok / ps;
-  const long k_off = ((long)(tid / TT) * ps + k_tok % ps) * 16;
-  const long k_step = (long)KCH * ps * 16;
+  const long k_off = ((long)(tid / TT) * pps + k_tok % ps) * 16;
+  const long k_step = (long)KCH * pps * 16;
   const int v_row = tid / T::VUPR;
   const int v_tok = ((tid % T::VUPR) ^ (v_row & (T::VUPR - 1))) * T::X;  // first token of the unit
   const int v_pg = v_tok / ps;
   const int v_sx = (v_tok % ps) / T::X;
-  const long v_off = a.v_transposed ? ((long)v_sx * D + v_row) * 16 : (long)v_row * ps * T::E + v_sx * 16;
-  const long v_step = a.v_transposed ? (long)VRS * 16 : (long)VRS * ps * T::E;
+  const long v_off = a.v_transposed ? ((long)v_sx * D + v_row) * 16 : (long)v_row * pps * T::E + v_sx * 16;
+  const long v_step = a.v_transposed ? (long)VRS * 16 : (long)VRS * pps * T::E;
+  // Byte offsets of a (sub-)page id inside its cache / scale array: the
+  // page's block plus the sub-page's place in it (K: token offset in every
+  // chunk; plain V: column offset in every row; transposed V: its 16-token
+  // blocks; scales: token offset).
+  const long vsub_bytes = a.v_transposed ? (long)(ps / T::X) * D * 16 : (long)ps * T::E;
+  const long msk = (1L << psub) - 1;
+  auto kpage = [&](long id) { return (id >> psub) * a.page_stride + (id & msk) * ps * 16; };
+  auto vpage = [&](long id) { return (id >> psub) * a.page_stride + (id & msk) * vsub_bytes; };
+  auto spage = [&](long id) { return ((id >> psub) * a.Hkv + kvh) * pps + (id & msk) * ps; };
   const int s_tok = (lane & 31) * 4;  // scales: wave 0, lanes 0-31 K, 32-63 V
   const int s_pg = s_tok / ps;
   const float* s_src0 = (lane >> 5) ? a.v_scale : a.k_scale;
@@ -278,7 +291,7 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   // kept inside the row) so that all of them go out together.
   auto tile_entries = [&](int tile, long (&e)[3]) {
     const long jt = (long)(tile - tb) * ppt;
-    auto entry = [&](long j) -> long { return (long)bt_row[min(max(id0 + j, 0L), (long)a.table_stride - 1)]; };
+    auto entry = [&](long j) -> long { return sub_id(min(max(id0 + j, 0L), ((long)a.table_stride << psub) - 1)); };
     e[0] = entry(jt + k_pg);
     e[1] = entry(jt + v_pg);
     e[2] = entry(jt + s_pg);
@@ -294,20 +307,20 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
     id[2] = (FP8 && per_token && w == 0 && page_ok(s_pg)) ? e[2] : -1;
   };
   auto issue_tile_at = [&](uint8_t* stg, const long (&id)[3]) {
-    const uint8_t* ksrc = kbase + k_off + (id[0] >= 0 ? id[0] * a.page_stride : 0);
+    const uint8_t* ksrc = kbase + k_off + (id[0] >= 0 ? kpage(id[0]) : 0);
     uint8_t* kdst = stg + (tid - lane) * 16;
 #pragma unroll
     for (int k = 0; k < T::KPT; ++k)
       __builtin_amdgcn_global_load_lds((const void*)(ksrc + k * k_step), (lds_void*)(kdst + k * NTHREADS * 16), 16,
                                        0, 0);
-    const uint8_t* vsrc = vbase + v_off + (id[1] >= 0 ? id[1] * a.page_stride : 0);
+    const uint8_t* vsrc = vbase + v_off + (id[1] >= 0 ? vpage(id[1]) : 0);
     uint8_t* vdst = stg + T::KBYTES + (tid - lane) * 16;
 #pragma unroll
     for (int k = 0; k < T::VPT; ++k)
       __builtin_amdgcn_global_load_lds((const void*)(vsrc + k * v_step), (lds_void*)(vdst + k * NTHREADS * 16), 16,
                                        0, 0);
     if (FP8 && per_token && w == 0) {
-      const float* src = s_src0 + (id[2] >= 0 ? (id[2] * a.Hkv + kvh) * ps + s_tok % ps : 0);
+      const float* src = s_src0 + (id[2] >= 0 ? spage(id[2]) + s_tok % ps : 0);
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(stg + T::KBYTES + T::VBYTES), 16, 0, 0);
     }
   };
@@ -1067,7 +1080,7 @@ struct RefreshArgs {
   MetaHeader header;  // the plan's header, written with the new list
   WorkItem* items;
   ReduceItem* reduce;
-  int num_seqs, QL, window, causal, page_size, table_stride, token_table, Hkv, row_groups;
+  int num_seqs, QL, window, causal, page_size, phys_page, table_stride, token_table, Hkv, row_groups;
   int maxp, n_items, n_slots;
 };
 
@@ -1076,7 +1089,7 @@ constexpr int REF_T = 1024;  // threads of the refresh workgroup
 __device__ int refresh_tiles(const RefreshArgs& a, int s) {
   const long cap = a.token_table == 2 ? (long)a.index_stride
                    : a.token_table    ? (long)a.table_stride
-                                      : (long)a.table_stride * a.page_size;
+                                      : (long)a.table_stride * a.phys_page;
   const long L = min(max((long)a.context_lens[s], 0L), cap);
   long lo = 0;
   if (!a.token_table && L > 0 && a.window > 0) {
@@ -1268,7 +1281,11 @@ static pa_status decode_impl(const pa_plan_t* plan, void* out, const void* q, co
   args.Hq = p.num_q_heads;
   args.Hkv = p.num_kv_heads;
   args.G = p.num_q_heads / p.num_kv_heads;
-  args.page_size = p.page_size;
+  // dense caches index tokens by sub-pages of at most 128 (the tile), token
+  // tables by the physical page
+  args.page_size = (p.token_table || p.page_size <= kTileTokens) ? p.page_size : kTileTokens;
+  args.page_sub = 31 - __builtin_clz((unsigned)(p.page_size / args.page_size));
+  args.phys_page = p.page_size;
   args.table_stride = p.table_stride;
   args.window = p.sliding_window;
   args.causal = p.causal;
@@ -1331,7 +1348,8 @@ extern "C" pa_status pa_plan_refresh(const pa_plan_t* plan, const int32_t* conte
   ra.QL = P.prob.query_len;
   ra.window = P.prob.sliding_window;
   ra.causal = P.prob.causal;
-  ra.page_size = P.prob.page_size;
+  ra.page_size = std::min(P.prob.page_size, kTileTokens);  // the kernels' tile origin (sub-pages above 128)
+  ra.phys_page = P.prob.page_size;
   ra.table_stride = P.prob.table_stride;
   ra.token_table = P.prob.token_table;
   ra.index_stride = P.prob.index_stride;

@@ -73,8 +73,10 @@ pa_status validate_problem(const pa_problem* p) {
   // Valid but not implemented here.
   if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
     return set_error(PA_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256");
-  if (p->page_size != 16 && p->page_size != 32 && p->page_size != 64 && p->page_size != 128)
-    return set_error(PA_ERR_UNSUPPORTED, "page_size must be 16, 32, 64 or 128");
+  if (p->page_size < 16 || p->page_size > 1024 || (p->page_size & (p->page_size - 1)))
+    return set_error(PA_ERR_UNSUPPORTED, "page_size must be a power of two from 16 to 1024");
+  if (p->token_table && p->page_size > kTileTokens)
+    return set_error(PA_ERR_UNSUPPORTED, "token tables support pages of at most 128 tokens");
   if (p->kv_dtype == PA_FP8_E4M3FN && p->scale_mode == PA_SCALE_NONE)
     return set_error(PA_ERR_UNSUPPORTED, "FP8 caches need a per-tensor or per-token scale");
   if (p->kv_dtype == PA_BF16 && p->scale_mode != PA_SCALE_NONE)
@@ -157,7 +159,10 @@ extern "C" pa_status pa_plan(const pa_problem* problem, const int32_t* context_l
       long first_pos = p.causal ? L - p.query_len : L - 1;
       lo = std::max<long>(0, first_pos - p.sliding_window + 1);
     }
-    long t0 = p.token_table ? 0 : (lo / p.page_size) * p.page_size;
+    // tiles start at the (sub-)page boundary the kernels index by: pages
+    // above 128 tokens are taken as sub-pages of 128
+    const long vps = std::min(p.page_size, kTileTokens);
+    long t0 = p.token_table ? 0 : (lo / vps) * vps;
     seq_tiles[s] = hi > lo ? (int)ceil_div(hi - t0, kTileTokens) : 0;
   }
 

@@ -118,9 +118,11 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   if (!meta_ok(mh, a.tag_lo, a.tag_hi)) return;  // not this plan's list: touch nothing
   if (it.seq < 0) return;  // an unused item of a refreshable plan
   const int s = it.seq, kvh = it.kvh, rg = it.rg;
-  const int ps = a.page_size;
+  const int ps = a.page_size;   // tokens per (sub-)page: pages above 128 are sub-pages of 128
+  const int pps = a.phys_page;  // physical page size: strides inside a page
+  const int psub = a.page_sub;  // sub-pages per page = 2^psub
   const int ps_log2 = 31 - __builtin_clz(ps);
-  const long cap = (long)a.table_stride * ps;
+  const long cap = (long)a.table_stride * pps;
   const int L = (int)min(max((long)a.context_lens[s], 0L), cap);
 
   // Visible span of the sequence (union over its query rows).
@@ -192,7 +194,8 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const long k = min((long)(tid + 256 * j), (long)max(nstaged - 1, 0));
-    idr[j] = bt_row[min(max(id0 + k, 0L), (long)a.table_stride - 1)];  // in the row whatever the item
+    const long jj = min(max(id0 + k, 0L), ((long)a.table_stride << psub) - 1);  // in the row whatever the item
+    idr[j] = (bt_row[jj >> psub] << psub) | (int)(jj & ((1 << psub) - 1));
   }
 
   // ---- the first three steps' loads ----
@@ -211,16 +214,23 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   };
   // Lane-constant parts of the addresses (page >= 32: a step lies in one page)
   const int slot_k = (32 * w + kt) & (ps - 1);
-  const uint32_t koff = (uint32_t)((2 * h * ps + slot_k) * 16);
-  const uint32_t kcs = (uint32_t)ps * 16;  // K chunk stride
+  const uint32_t koff = (uint32_t)((2 * h * pps + slot_k) * 16);
+  const uint32_t kcs = (uint32_t)pps * 16;  // K chunk stride
   const int slot_v = (32 * w + 16 * h) & (ps - 1);
   uint32_t voff[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     const int dd = 32 * db + c32;
-    voff[db] = a.v_transposed ? (uint32_t)(((slot_v >> 4) * D + dd) * 16) : (uint32_t)(dd * ps + slot_v);
+    voff[db] = a.v_transposed ? (uint32_t)(((slot_v >> 4) * D + dd) * 16) : (uint32_t)(dd * pps + slot_v);
   }
-  const uint32_t soff = (uint32_t)((kvh * ps + ((32 * w + c32) & (ps - 1))) * 4);
+  const uint32_t soff = (uint32_t)((kvh * pps + ((32 * w + c32) & (ps - 1))) * 4);
+  // A (sub-)page id's place in the caches and scales: its page's block plus
+  // the sub-page's offset (K: tokens in every chunk; plain V: columns of
+  // every row; transposed V: its 16-token blocks; scales: tokens).
+  const long msk = (1L << psub) - 1;
+  const long vsub_bytes = a.v_transposed ? (long)(ps >> 4) * D * 16 : (long)ps;
+  auto kpage = [&](long id) { return (id >> psub) * a.page_stride + (id & msk) * ps * 16; };
+  auto vpage = [&](long id) { return (id >> psub) * a.page_stride + (id & msk) * vsub_bytes; };
   const float* sbase = h ? a.v_scale : a.k_scale;
 
   // Page ids of a step, wave-uniform: the step's page (page >= 32), or its
@@ -230,10 +240,11 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   };
   auto load_k = [&](SD& d, StepPages id) {
     if constexpr (BIG) {
-      const uint8_t* kp = kbase + id.a * a.page_stride;
+      const uint8_t* kp = kbase + kpage(id.a);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) d.k[ks] = load32(kp + koff + 4 * ks * kcs, kp + koff + (4 * ks + 1) * kcs);
-      if constexpr (PT) d.sc = *(const float*)((const uint8_t*)(sbase + id.a * a.Hkv * ps) + soff);
+      if constexpr (PT)
+        d.sc = *(const float*)((const uint8_t*)(sbase + (id.a >> psub) * a.Hkv * pps + (id.a & msk) * ps) + soff);
     } else {
       // page 16: token kt of the step is slot kt & 15 of its first or second page
       const long idk = kt >= 16 ? id.b : id.a;
@@ -249,7 +260,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   };
   auto load_v = [&](SD& d, StepPages id) {
     if constexpr (BIG) {
-      const uint8_t* vp = vbase + id.a * a.page_stride;
+      const uint8_t* vp = vbase + vpage(id.a);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) d.v[db] = *(const u32x4*)(vp + voff[db]);
     } else {
@@ -267,8 +278,8 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   auto step_pages_direct = [&](int k) -> StepPages {  // step k's page ids from the block table
     const long j = (long)((k - tb) * TT + 32 * wu) >> ps_log2;
     StepPages r{0, 0};
-    if (page_ok(j)) r.a = btc[id0 + j];
-    if (!BIG && page_ok(j + 1)) r.b = btc[id0 + j + 1];
+    if (page_ok(j)) r.a = ((long)btc[(id0 + j) >> psub] << psub) | ((id0 + j) & msk);
+    if (!BIG && page_ok(j + 1)) r.b = btc[id0 + j + 1];  // page 16: no sub-pages
     return r;
   };
   // Unconditional, so that the compiler's wait counts stay exact: an empty
@@ -419,7 +430,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     if (j < nstaged) return __builtin_amdgcn_readfirstlane(ids[j]);
     // past the staged bound: a scalar read of the block table (the table is
     // constant for the kernel's lifetime), counted apart from the K/V loads
-    return btc[id0 + j];
+    return ((long)btc[(id0 + j) >> psub] << psub) | ((id0 + j) & msk);
   };
   auto step_page = [&](int k) -> StepPages {  // page ids of step k
     const long j = (long)((k - tb) * TT + 32 * wu) >> ps_log2;

@@ -46,6 +46,8 @@ def _prob(**kw):
     (dict(sliding_window=-1), ValueError),
     (dict(head_dim=96), NotImplementedError),
     (dict(page_size=48), NotImplementedError),
+    (dict(page_size=2048), NotImplementedError),
+    (dict(token_table=True, page_size=256), NotImplementedError),
     (dict(scale_mode="none"), NotImplementedError),
     (dict(kv_dtype="bf16"), NotImplementedError),  # BF16 with a scale
     (dict(kv_dtype="bf16", scale_mode="none", head_dim=256), NotImplementedError),

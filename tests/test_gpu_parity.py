@@ -91,6 +91,35 @@ def test_d64(kv, scale, page):
         seed += 1
 
 
+LARGE_PAGE_CASES = [
+    # name, query_len, Hq, Hkv, D, kv dtype, scale mode, window, sinks, transposed V
+    ("tile16-fp8", 1, 16, 4, 128, "fp8", "token", 257, True, False),
+    ("stream64-fp8", 4, 16, 1, 128, "fp8", "token", 0, False, False),
+    ("stream32-fp8", 2, 16, 1, 128, "fp8", "tensor", 300, True, True),
+    ("d256-stream", 4, 16, 2, 256, "fp8", "tensor", 8193, False, True),
+    ("d256-tile", 2, 16, 2, 256, "fp8", "token", 0, True, False),
+    ("d64-tile", 4, 16, 1, 64, "fp8", "token", 17, False, True),
+    ("bf16-64rows", 4, 16, 1, 128, "bf16", "none", 0, False, False),
+]
+
+
+@pytest.mark.parametrize("page", [256, 512, 1024])
+@pytest.mark.parametrize("case", LARGE_PAGE_CASES, ids=[c[0] for c in LARGE_PAGE_CASES])
+def test_large_pages(page, case):
+    """Pages above 128 tokens (taken as 128-token sub-pages: the page's
+    block-table entry plus the sub-page's offset in K, V and the scales) in
+    every decode path, both V layouts and both scale modes, with lengths
+    that end inside, at and past sub-page and page edges."""
+    name, ql, hq, hkv, d, kv, scale, window, sinks, vt = case
+    lens = [0, 1, 127, 128, 129, page - 1, page, page + 1, 3 * page + 77, 9000]
+    inp = W.make_dense_case(5000 + page + len(name), lens, query_len=ql, num_q_heads=hq, num_kv_heads=hkv,
+                            head_dim=d, page_size=page, kv_dtype=kv, v_transposed=vt, scale_mode=scale,
+                            sliding_window=window, has_sinks=sinks)
+    announce(f"large pages {name} page={page}")
+    _parity(inp, cu_count=64)
+    _parity(inp, cu_count=4, max_partitions=1, stage_limit=3)
+
+
 @pytest.mark.parametrize("ql,hq,hkv", [(1, 8, 1), (4, 16, 2), (4, 16, 1)])
 def test_d256(ql, hq, hkv):
     seed = 3000 + ql * 10 + hq

@@ -141,6 +141,16 @@ def test_planted_digits_d256(ql, window, page, vt):
                  seed=340 + ql + window + page)
 
 
+@pytest.mark.parametrize("rows", [16, 32, 64])
+@pytest.mark.parametrize("page,vt", [(256, False), (256, True), (512, False), (1024, True)])
+def test_planted_digits_large_pages(rows, page, vt):
+    """Pages above 128 tokens: the digits of the target encode its physical
+    page and slot, so a wrong sub-page offset in K, V or the scales shows."""
+    ql, hq = ROWS[rows]
+    announce(f"planted digits large pages rows={rows} page={page} vt={vt}")
+    _dense_probe(ql, hq, 1, 128, page, vt, "token", L=2 * page + 300, seed=390 + rows + page + vt)
+
+
 @pytest.mark.parametrize("kv,scale", [("fp8", "tensor"), ("fp8", "token"), ("bf16", "none")])
 @pytest.mark.parametrize("ql,page,vt", [(1, 16, False), (4, 64, True), (2, 32, False)])
 def test_planted_digits_d64(kv, scale, ql, page, vt):
