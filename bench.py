@@ -313,13 +313,14 @@ def measure_indexer(workload: str, steps: int, warmup: int, dev):
     logits = torch.empty((x.rows, x.num_kv), dtype=torch.float32, device=dev)
     idx = torch.empty((x.rows, max(k, 1)), dtype=torch.int32, device=dev)
     cnt = torch.empty((x.rows,), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(B.topk_workspace_bytes(x.rows, x.num_kv, max(k, 1)), 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def lg():
         B.pa_mqa_logits(logits, d["q"], d["kv"], d["kv_scale"], d["weights"], d["ks"], d["ke"], True, stream)
 
     def tk():
-        B.pa_topk(idx, cnt, logits, d["ks"], d["ke"], None, stream)
+        B.pa_topk(idx, cnt, logits, d["ks"], d["ke"], None, stream, workspace=ws)
 
     def region(body, n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

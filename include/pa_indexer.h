@@ -20,6 +20,7 @@
 #ifndef PA_INDEXER_H_
 #define PA_INDEXER_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include "pa_decode.h"
@@ -66,9 +67,20 @@ pa_status pa_mqa_logits(float* logits, const uint8_t* q, const uint8_t* kv, cons
  * indices and counts are what pa_decode_sparse takes as topk_indices (with
  * index_stride = k) and topk_counts when ks[r] is the first index key of
  * row r's sequence.  k >= 1.
+ *
+ * With few rows the windows are first cut into segments whose own top k
+ * are kept as candidates (every key of the row's top k is in its segment's
+ * top k), then each row selects from its candidates: workspace (16-byte
+ * aligned, caller-owned, contents irrelevant) holds them, of at least the
+ * bytes pa_topk_workspace_size returns for (rows, num_kv, k) (0: no
+ * workspace needed, NULL allowed); too small: PA_ERR_WORKSPACE.
  */
 pa_status pa_topk(int32_t* indices, int32_t* counts, const float* logits, const int32_t* ks, const int32_t* ke,
-                  int32_t rows, int32_t num_kv, int64_t logits_stride, int32_t k, void* stream);
+                  int32_t rows, int32_t num_kv, int64_t logits_stride, int32_t k, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/* Workspace bytes pa_topk needs for (rows, num_kv, k). */
+pa_status pa_topk_workspace_size(int32_t rows, int32_t num_kv, int32_t k, size_t* bytes);
 
 #ifdef __cplusplus
 }

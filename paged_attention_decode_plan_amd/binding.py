@@ -25,7 +25,7 @@ PA_SCALE_NONE, PA_SCALE_PER_TENSOR, PA_SCALE_PER_TOKEN = range(3)
 
 EXPORTS = ["pa_plan", "pa_plan_sizes", "pa_plan_info", "pa_plan_work", "pa_plan_upload", "pa_plan_free", "pa_decode",
            "pa_reduce", "pa_plan_refresh", "pa_attend_static", "pa_decode_sparse", "pa_mqa_logits", "pa_topk",
-           "pa_last_error"]
+           "pa_topk_workspace_size", "pa_last_error"]
 STATIC_SCRATCH_BYTES = 32 << 20  # PA_STATIC_SCRATCH_BYTES of include/pa_decode.h
 META_HEADER_BYTES = 32  # meta_dev starts with the plan's header; the work list follows
 
@@ -85,7 +85,9 @@ def load_library(path: str = LIB_PATH):
     L.pa_mqa_logits.restype = ctypes.c_int
     L.pa_mqa_logits.argtypes = [vp] * 7 + [ctypes.c_int32] * 4 + [ctypes.c_int64, ctypes.c_int32, vp]
     L.pa_topk.restype = ctypes.c_int
-    L.pa_topk.argtypes = [vp] * 5 + [ctypes.c_int32] * 2 + [ctypes.c_int64, ctypes.c_int32, vp]
+    L.pa_topk.argtypes = [vp] * 5 + [ctypes.c_int32] * 2 + [ctypes.c_int64, ctypes.c_int32, vp, ctypes.c_size_t, vp]
+    L.pa_topk_workspace_size.restype = ctypes.c_int
+    L.pa_topk_workspace_size.argtypes = [ctypes.c_int32] * 3 + [ctypes.POINTER(ctypes.c_size_t)]
     L.pa_attend_static.restype = ctypes.c_int
     L.pa_attend_static.argtypes = [vp] * 11
     L.pa_last_error.restype = ctypes.c_char_p
@@ -300,11 +302,23 @@ def pa_mqa_logits(logits, q, kv, kv_scale, weights, ks, ke, clean=True, stream=N
                                         _stream_ptr(stream)))
 
 
-def pa_topk(indices, counts, logits, ks, ke, num_kv=None, stream=None):
+def topk_workspace_bytes(rows: int, num_kv: int, k: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().pa_topk_workspace_size(rows, num_kv, k, ctypes.byref(n)))
+    return n.value
+
+
+def pa_topk(indices, counts, logits, ks, ke, num_kv=None, stream=None, workspace=None):
     """Top-k of each row's window (pa_indexer.h): indices int32 [rows, k],
-    counts int32 [rows], logits float32 [rows, >= num_kv]."""
+    counts int32 [rows], logits float32 [rows, >= num_kv]; workspace: a
+    device tensor of at least topk_workspace_bytes (allocated here if
+    None)."""
     rows, k = indices.shape
     num_kv = logits.shape[1] if num_kv is None else num_kv
+    need = topk_workspace_bytes(rows, num_kv, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=indices.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _dev_i32(indices, "indices")
     _dev_i32(counts, "counts")
     _dev_i32(ks, "ks")
@@ -314,4 +328,4 @@ def pa_topk(indices, counts, logits, ks, ke, num_kv=None, stream=None):
     if counts.shape != (rows,) or ks.shape != (rows,) or ke.shape != (rows,) or num_kv > logits.shape[1]:
         raise ValueError("counts, ks and ke must be [rows]; num_kv at most logits.shape[1]")
     _check(load_library().pa_topk(_ptr(indices), _ptr(counts), _ptr(logits), _ptr(ks), _ptr(ke), rows, num_kv,
-                                  logits.stride(0), k, _stream_ptr(stream)))
+                                  logits.stride(0), k, _ptr(workspace), wbytes, _stream_ptr(stream)))

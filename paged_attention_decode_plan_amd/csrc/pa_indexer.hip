@@ -28,6 +28,7 @@
 // keys inside it (lower positions first) until k are taken, ascending.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <string>
 
@@ -165,6 +166,10 @@ struct TopkArgs {
   const int32_t* ke;
   long long stride;
   int rows, num_kv, k;
+  int segs;          // segments per row of the first stage (1: a single stage)
+  uint32_t* ckey;    // candidates [rows][segs][k]: keys, positions, counts
+  int32_t* cpos;
+  int32_t* ccount;
 };
 
 // Order-preserving key: larger float <-> larger unsigned key; -0.0 is made
@@ -184,45 +189,116 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane) {
   return x;
 }
 
-// The thread's keys of the batch at c0 (element c0 + tid + TK_T j in slot
-// j: each load instruction of a wave reads 64 consecutive keys).  Every
-// load is unconditional (an index past the window reads the last key, and
-// the caller's bound marks the slot invalid), so all of them are in flight
-// together.
-__device__ __forceinline__ void load_keys(uint32_t (&key)[TK_E], const float* row, int c0, int n, int tid) {
-  float v[TK_E];
-#pragma unroll
-  for (int j = 0; j < TK_E; ++j) v[j] = row[min(c0 + tid + TK_T * j, n - 1)];
-#pragma unroll
-  for (int j = 0; j < TK_E; ++j) key[j] = fkey(v[j]);
-}
+// Top-k modes: the whole window of a row to its final positions; one
+// segment of a row's window to k candidates (first stage); a row's
+// candidates to its final positions (second stage).
+enum TopkMode { TK_ROW = 0, TK_SEG = 1, TK_CAND = 2 };
 
+// One workgroup selects the k largest keys of n elements in position order
+// (ties: the lower position).  Element i: key(i) and validity come from the
+// mode's source; selected elements are written in ascending position order.
+template <int MODE>
 __global__ __launch_bounds__(TK_T) void topk_kernel(TopkArgs a) {
   __shared__ uint32_t hist[TK_SUB * TK_HROW];
   __shared__ uint32_t tot[256];
   __shared__ uint32_t scan[2][TK_NE + TK_W];  // per (j, w) counts, then their exclusive scan
   __shared__ uint32_t sel[3];
+  __shared__ int32_t seg_cnt[16];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int r = blockIdx.x;
-  const int N = a.num_kv, K = a.k;
+  const int K = a.k, N = a.num_kv;
+  const int r = MODE == TK_SEG ? blockIdx.x / a.segs : blockIdx.x;
+  const int seg = MODE == TK_SEG ? blockIdx.x % a.segs : 0;
   const int lo = min(max(a.ks[r], 0), N);
   const int hi = min(max(a.ke[r], lo), N);
-  const int n = hi - lo;
-  const float* row = a.logits + (long)r * a.stride + lo;
-  int32_t* out = a.indices + (long)r * K;
-  if (n <= K) {  // the whole window
-    for (int i = tid; i < K; i += TK_T) out[i] = i < n ? i : -1;
-    if (tid == 0) a.counts[r] = n;
+  const int nw = hi - lo;  // window length
+  // the elements this workgroup selects from
+  int base = 0, n = nw;
+  if (MODE == TK_SEG) {
+    const int sl = (nw + a.segs - 1) / a.segs;
+    base = min(seg * sl, nw);
+    n = min(nw - base, sl);
+  } else if (MODE == TK_CAND) {
+    n = a.segs * K;
+    if (tid < a.segs) seg_cnt[tid] = a.ccount[r * a.segs + tid];
+    __syncthreads();
+  }
+  const float* row = a.logits + (long)r * a.stride + lo + base;
+  const uint32_t* crow_k = a.ckey + (long)r * a.segs * K;
+  const int32_t* crow_p = a.cpos + (long)r * a.segs * K;
+  // outputs: final positions of the row, or this segment's candidates
+  int32_t* out = MODE == TK_SEG ? a.cpos + ((long)r * a.segs + seg) * K : a.indices + (long)r * K;
+  uint32_t* outk = a.ckey + ((long)r * a.segs + seg) * K;  // first stage only
+  // validity of element i (candidates: inside its segment's count); the
+  // quotient by k runs through a float reciprocal with an exact correction
+  // (i < 2^24), not an integer division per element
+  const float inv_k = 1.0f / (float)K;
+  auto valid_at = [&](int i) {
+    if (MODE == TK_CAND) {
+      if (i >= n) return false;
+      int q = (int)((float)i * inv_k);
+      q -= q * K > i ? 1 : 0;
+      q += (q + 1) * K <= i ? 1 : 0;
+      return i - q * K < seg_cnt[q];
+    }
+    return i < n;
+  };
+  auto position = [&](int i) -> int32_t { return MODE == TK_CAND ? crow_p[i] : base + i; };
+  auto emit = [&](uint32_t pos, int i, uint32_t key) {
+    out[pos] = position(i);
+    if (MODE == TK_SEG) outk[pos] = key;
+  };
+
+  // The thread's keys of the batch at c0 (element c0 + tid + TK_T j in slot
+  // j: each load instruction of a wave reads 64 consecutive keys).  Every
+  // load is unconditional (an index past the elements reads the last one;
+  // valid_at marks the slot), so all of them are in flight together.
+  uint32_t key[TK_E];
+  uint32_t vbits = 0;  // bit j: slot j holds an element of the batch
+  const bool resident = n <= TK_CHUNK;  // one batch: its keys stay in registers through every pass
+  auto load_keys = [&](int c0) {
+    vbits = 0;
+#pragma unroll
+    for (int j = 0; j < TK_E; ++j) vbits |= valid_at(c0 + tid + TK_T * j) ? (1u << j) : 0u;
+    if (MODE == TK_CAND) {
+#pragma unroll
+      for (int j = 0; j < TK_E; ++j) key[j] = crow_k[min(c0 + tid + TK_T * j, n - 1)];
+    } else {
+      float v[TK_E];
+#pragma unroll
+      for (int j = 0; j < TK_E; ++j) v[j] = row[min(c0 + tid + TK_T * j, n - 1)];
+#pragma unroll
+      for (int j = 0; j < TK_E; ++j) key[j] = fkey(v[j]);
+    }
+  };
+
+  if (MODE != TK_CAND && n <= K) {  // every element is taken
+    if (MODE == TK_SEG) {
+      for (int i = tid; i < n; i += TK_T) emit(i, i, fkey(row[i]));
+      if (tid == 0) a.ccount[r * a.segs + seg] = n;
+    } else {
+      for (int i = tid; i < K; i += TK_T) out[i] = i < n ? i : -1;
+      if (tid == 0) a.counts[r] = n;
+    }
     return;
   }
-  uint32_t key[TK_E];
+
+  if (resident) load_keys(0);
+
+  // second stage of a row whose window held at most k keys: every candidate
+  int total = K + 1;
+  if (MODE == TK_CAND) {
+    total = 0;
+    for (int x = 0; x < a.segs; ++x) total += seg_cnt[x];
+  }
+  const bool take_all = total <= K;  // workgroup-uniform
 
   // ---- radix select, 8 bits a pass from the top: the bin [tlo, thi] of
   // keys that holds the k-th largest, and how many of its keys are taken
   // (need; the rest of the k are the keys above thi).  Stops early once
-  // every key of the bin is taken. ----
-  uint32_t prefix = 0, need = (uint32_t)K, tlo = 0, thi = 0xFFFFFFFFu;
-  for (int pass = 0; pass < 4; ++pass) {
+  // every key of the bin is taken.  (Taking every candidate: an empty bin
+  // below every key.) ----
+  uint32_t prefix = 0, need = take_all ? 0u : (uint32_t)K, tlo = take_all ? 1u : 0u, thi = take_all ? 0u : 0xFFFFFFFFu;
+  for (int pass = 0; pass < (take_all ? 0 : 4); ++pass) {
     const int shift = 24 - 8 * pass;
     for (int i = tid; i < TK_SUB * TK_HROW; i += TK_T) hist[i] = 0;
     if (tid == 0) {  // overwritten by the lane that finds the bin
@@ -233,11 +309,11 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(TopkArgs a) {
     __syncthreads();
     uint32_t* hl = hist + (lane & (TK_SUB - 1)) * TK_HROW;
     for (int c0 = 0; c0 < n; c0 += TK_CHUNK) {
-      load_keys(key, row, c0, n, tid);
+      if (!resident) load_keys(c0);
 #pragma unroll
       for (int j = 0; j < TK_E; ++j) {
-        const bool valid = c0 + tid + TK_T * j < n;
-        if (valid && (pass == 0 || (key[j] >> (shift + 8)) == prefix)) atomicAdd(hl + ((key[j] >> shift) & 255u), 1u);
+        if (((vbits >> j) & 1u) && (pass == 0 || (key[j] >> (shift + 8)) == prefix))
+          atomicAdd(hl + ((key[j] >> shift) & 255u), 1u);
       }
     }
     __syncthreads();
@@ -285,10 +361,10 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(TopkArgs a) {
   const uint64_t below = (1ull << lane) - 1;  // lanes before this one
   uint32_t run_gt = 0, run_eq = 0;            // keys above / inside the bin in earlier batches
   for (int c0 = 0; c0 < n; c0 += TK_CHUNK) {
-    load_keys(key, row, c0, n, tid);
+    if (!resident) load_keys(c0);
 #pragma unroll
     for (int j = 0; j < TK_E; ++j) {
-      const bool valid = c0 + tid + TK_T * j < n;
+      const bool valid = (vbits >> j) & 1u;
       const uint64_t bg = __builtin_amdgcn_ballot_w64(valid && key[j] > thi);
       const uint64_t be = __builtin_amdgcn_ballot_w64(valid && key[j] >= tlo && key[j] <= thi);
       if (lane == 0) {
@@ -325,7 +401,7 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(TopkArgs a) {
 #pragma unroll
     for (int j = 0; j < TK_E; ++j) {
       const int i = c0 + tid + TK_T * j;
-      const bool valid = i < n;
+      const bool valid = (vbits >> j) & 1u;
       const bool gt = valid && key[j] > thi, eq = valid && key[j] >= tlo && key[j] <= thi;
       const uint64_t bg = __builtin_amdgcn_ballot_w64(gt);
       const uint64_t be = __builtin_amdgcn_ballot_w64(eq);
@@ -333,20 +409,40 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(TopkArgs a) {
         const uint32_t gt_before = scan[0][j * TK_W + w] + (uint32_t)__builtin_popcountll(bg & below);
         const uint32_t eq_before = scan[1][j * TK_W + w] + (uint32_t)__builtin_popcountll(be & below);
         const uint32_t pos = gt_before + min(eq_before, need);
-        if ((gt || (eq && eq_before < need)) && pos < (uint32_t)K) out[pos] = i;
+        if ((gt || (eq && eq_before < need)) && pos < (uint32_t)K) emit(pos, i, key[j]);
       }
     }
     run_gt += cg;
     run_eq += ce;
     __syncthreads();  // scan read before the next batch writes it
   }
-  if (tid == 0) a.counts[r] = K;
+  if (MODE == TK_CAND && take_all)
+    for (int i = total + tid; i < K; i += TK_T) out[i] = -1;
+  if (tid == 0) {
+    if (MODE == TK_SEG)
+      a.ccount[r * a.segs + seg] = K;
+    else
+      a.counts[r] = take_all ? total : K;
+  }
 }
 
 }  // namespace
 }  // namespace pa
 
 using namespace pa;
+
+namespace pa {
+namespace {
+// First-stage segments per row: enough workgroups for the CUs (about 256)
+// when rows are few, each segment at least 4k keys, at most 16.
+int topk_segments(int rows, int num_kv, int k) {
+  if (rows <= 0) return 1;
+  int s = (256 + rows - 1) / rows;
+  s = std::min(s, std::max(1, num_kv / (4 * k)));
+  return std::max(1, std::min(s, 16));
+}
+}  // namespace
+}  // namespace pa
 
 extern "C" pa_status pa_mqa_logits(float* logits, const uint8_t* q, const uint8_t* kv, const float* kv_scale,
                                    const float* weights, const int32_t* ks, const int32_t* ke, int32_t rows,
@@ -378,16 +474,38 @@ extern "C" pa_status pa_mqa_logits(float* logits, const uint8_t* q, const uint8_
   return PA_OK;
 }
 
+extern "C" pa_status pa_topk_workspace_size(int32_t rows, int32_t num_kv, int32_t k, size_t* bytes) {
+  if (rows < 0 || num_kv < 0 || k < 1 || !bytes) return set_error(PA_ERR_INVALID, "rows, num_kv >= 0, k >= 1 and bytes required");
+  const int segs = topk_segments(rows, num_kv, k);
+  *bytes = segs > 1 ? (size_t)rows * segs * ((size_t)k * 8 + 4) : 0;
+  return PA_OK;
+}
+
 extern "C" pa_status pa_topk(int32_t* indices, int32_t* counts, const float* logits, const int32_t* ks,
                              const int32_t* ke, int32_t rows, int32_t num_kv, int64_t logits_stride, int32_t k,
-                             void* stream) {
+                             void* workspace, size_t workspace_bytes, void* stream) {
   if (rows < 0 || num_kv < 0 || k < 1) return set_error(PA_ERR_INVALID, "rows, num_kv >= 0 and k >= 1 required");
   if (rows == 0) return PA_OK;
   if (!indices || !counts || !ks || !ke || (num_kv > 0 && !logits))
     return set_error(PA_ERR_INVALID, "a pointer argument is NULL");
   if (logits_stride < num_kv) return set_error(PA_ERR_INVALID, "logits_stride must be >= num_kv");
-  TopkArgs a{indices, counts, logits, ks, ke, (long long)logits_stride, rows, num_kv, k};
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)rows), dim3(TK_T), 0, (hipStream_t)stream, a);
+  size_t need = 0;
+  pa_topk_workspace_size(rows, num_kv, k, &need);
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15)))
+    return set_error(PA_ERR_WORKSPACE, "top-k needs a 16-byte aligned workspace of " + std::to_string(need) +
+                                           " bytes (pa_topk_workspace_size)");
+  const int segs = topk_segments(rows, num_kv, k);
+  TopkArgs a{indices, counts, logits, ks, ke, (long long)logits_stride, rows, num_kv, k, segs, nullptr, nullptr,
+             nullptr};
+  if (segs > 1) {
+    a.ckey = (uint32_t*)workspace;
+    a.cpos = (int32_t*)((uint8_t*)workspace + (size_t)rows * segs * k * 4);
+    a.ccount = (int32_t*)((uint8_t*)workspace + (size_t)rows * segs * k * 8);
+    hipLaunchKernelGGL(topk_kernel<TK_SEG>, dim3((unsigned)(rows * segs)), dim3(TK_T), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(topk_kernel<TK_CAND>, dim3((unsigned)rows), dim3(TK_T), 0, (hipStream_t)stream, a);
+  } else {
+    hipLaunchKernelGGL(topk_kernel<TK_ROW>, dim3((unsigned)rows), dim3(TK_T), 0, (hipStream_t)stream, a);
+  }
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(PA_ERR_DEVICE, std::string("top-k launch failed: ") + hipGetErrorString(err));
   return PA_OK;
