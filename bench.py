@@ -478,11 +478,6 @@ def main():
     if args.ceiling:
         ceiling(args, dev)
         return
-    if args.indexer:
-        r = measure_indexer(args.indexer, args.steps, args.warmup, dev)
-        r.update({"workload": args.indexer, "kernel_sha": source_sha()})
-        print(json.dumps(r), flush=True)
-        return
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -492,6 +487,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log(f"calibration copy: {n} bytes read, {n} bytes written")
+    if args.indexer:
+        r = measure_indexer(args.indexer, args.steps, args.warmup, dev)
+        r.update({"workload": args.indexer, "kernel_sha": source_sha()})
+        print(json.dumps(r), flush=True)
+        return
 
     head, inp = measure(args.workload, args.steps, args.warmup, dev)
     p = inp.problem

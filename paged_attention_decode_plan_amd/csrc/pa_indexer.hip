@@ -55,6 +55,11 @@ struct LogitsArgs {
   int rows, num_kv, clean;
 };
 
+// max(x, 0) as one integer max on the bits (a negative float, -0.0
+// included, is a negative int32; a non-negative one keeps its bits): fmaxf
+// would also quieten NaNs first, one more instruction per score.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 template <int H>
 __global__ __launch_bounds__(512) void mqa_logits_kernel(LogitsArgs a) {
   constexpr int D = LG_D;
@@ -136,8 +141,8 @@ __global__ __launch_bounds__(512) void mqa_logits_kernel(LogitsArgs a) {
         acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mb][1], kb[1], acc, 0, 0, 0, 127, 0, 127);
 #pragma unroll
         for (int j = 0; j < 16; j += 2) {
-          part0 += wv[mb][j] * fmaxf(acc[j], 0.f);
-          part1 += wv[mb][j + 1] * fmaxf(acc[j + 1], 0.f);
+          part0 += wv[mb][j] * relu_bits(acc[j]);
+          part1 += wv[mb][j + 1] * relu_bits(acc[j + 1]);
         }
       }
       const float part = part0 + part1;
