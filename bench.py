@@ -43,6 +43,7 @@ PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
 SETTLE_MS = 100.0  # untimed calls before the warm-up steps, so that the GPU clocks have settled
 MERGE = {"reducer": B.MERGE_REDUCER, "in-kernel": B.MERGE_IN_KERNEL}
 merge_mode = B.MERGE_AUTO  # --merge
+settle_ms_target = SETTLE_MS  # --settle-ms
 WORKLOADS = {
     "dense_mtp4_fp8": "dense MTP4 verify, FP8 KV, per-token scales: B32 Hq16/Hkv1 D128 QL4 page128 L~U[16K,32K]",
     "dense_mtp4_bf16": "dense MTP4 verify, BF16 KV: B32 Hq16/Hkv1 D128 QL4 page128 L~U[16K,32K]",
@@ -233,7 +234,7 @@ def measure(workload: str, steps: int, warmup: int, dev):
     # back to back in a fresh process: 102, 54, 59, 61, 59, 57, 56, 55, 54,
     # 53, 52.5, 52, 51.8, 51.4 us).
     settle_ms = 0.0
-    while settle_ms < SETTLE_MS:
+    while settle_ms < settle_ms_target:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for k in range(20):
@@ -333,7 +334,7 @@ def measure_indexer(workload: str, steps: int, warmup: int, dev):
         return e0.elapsed_time(e1) * 1e3 / n
 
     settle_ms = 0.0
-    while settle_ms < SETTLE_MS:
+    while settle_ms < settle_ms_target:
         settle_ms += region(lg, 5) * 5 / 1e3
     for _ in range(warmup):
         lg()
@@ -457,6 +458,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--indexer", choices=sorted(INDEXER_WORKLOADS), default=None,
                     help="measure one indexer workload alone and print its JSON")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="untimed calls of each workload before its warm-up steps, in ms of GPU time")
     ap.add_argument("--merge", choices=sorted(MERGE), default=None,
                     help="merge of multi-partition units (default: the library's choice, the reducer)")
     ap.add_argument("--ceiling", action="store_true",
@@ -472,7 +475,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    global merge_mode
+    global merge_mode, settle_ms_target
+    settle_ms_target = args.settle_ms
     if args.merge:
         merge_mode = MERGE[args.merge]
     if args.ceiling:
