@@ -94,7 +94,9 @@ struct Roles {
 template <int D, bool FP8, int NRT, bool SPARSE>
 struct Smem {
   using R = Roles<D, NRT>;
-  static constexpr int STAGES = (!SPARSE && FP8 && D == 128 && NRT >= 2) ? 4 : 2;
+  // head dim 512: one 128-token FP8 stage is 129 KB, so a single stage (the
+  // tile's loads, then its compute, no overlap inside the workgroup)
+  static constexpr int STAGES = D >= 512 ? 1 : (!SPARSE && FP8 && D == 128 && NRT >= 2) ? 4 : 2;
   static constexpr int STAGE = Tile<D, FP8, Waves<NRT, D>::NT>::STAGE;
   static constexpr int MERGE = NRT * 16 * (D + 4) * 4;  // one O buffer with padded rows
   static constexpr int MAIN = (STAGES * STAGE > MERGE) ? STAGES * STAGE : MERGE;
@@ -334,7 +336,7 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
     // query rows and the staged ids; one wait covers them all (the empty
     // statement makes the compiler take it here), so that the DMA issue and
     // the query split after it wait for nothing else.
-    long pe[NST - 1][3];
+    long pe[NST > 1 ? NST - 1 : 1][3];
 #pragma unroll
     for (int k = 0; k < NST - 1; ++k) tile_entries(tb + k, pe[k]);
     asm volatile("" ::"v"(kscale0), "v"(vscale0));
@@ -823,6 +825,24 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
       }
       // returns false if an overflow stopped the attempt
       auto tiles = [&](auto INc, int from, int to) -> bool {
+        if constexpr (NST == 1) {
+          // one stage: issue the tile, wait for every wave's loads, compute,
+          // and let every wave finish reading before the next issue
+          for (int tile = from; tile < to; ++tile) {
+            issue_tile(tile, stage_base);
+            wait_vmcnt<0>();
+            wait_lgkm0();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if (!scan && *(volatile int*)restart_flag) return false;  // an overflow: stop this attempt
+            compute_tile(PTc, INc, tile, stage_base);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+          }
+          return true;
+        }
         for (int tile = from; tile < to; ++tile) {
           const int cur = (tile - tb) % NST;
           // wait for this tile's loads; the later tiles' loads stay in flight
@@ -832,11 +852,11 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
           if (ahead <= 0) {
             wait_vmcnt<0>();
           } else if (ahead == 1) {
-            if (extra) wait_vmcnt<PER + 1>();
-            else wait_vmcnt<PER>();
+            if (extra) wait_vmcnt<(PER + 1) % 64>();
+            else wait_vmcnt<PER % 64>();
           } else {
-            if (extra) wait_vmcnt<2 * (PER + 1)>();
-            else wait_vmcnt<2 * PER>();
+            if (extra) wait_vmcnt<(2 * (PER + 1)) % 64>();  // (the modulus only for one-stage kernels, which never get here)
+            else wait_vmcnt<(2 * PER) % 64>();
           }
           wait_lgkm0();  // this wave's LDS writes (restart flag) are done
           // all waves' loads of this tile landed and tile-1 compute is done; the
@@ -1217,7 +1237,8 @@ static pa_status launch_one(const KernelArgs& args, int nblocks, hipStream_t str
 
 template <int D, bool FP8, int NRT>
 static pa_status launch_sp(bool sparse, const KernelArgs& args, int n, hipStream_t st) {
-  return sparse ? launch_one<D, FP8, NRT, true>(args, n, st) : launch_one<D, FP8, NRT, false>(args, n, st);
+  if constexpr (D >= 512) return launch_one<D, FP8, NRT, false>(args, n, st);  // dense caches only (validated)
+  else return sparse ? launch_one<D, FP8, NRT, true>(args, n, st) : launch_one<D, FP8, NRT, false>(args, n, st);
 }
 template <int D, bool FP8>
 static pa_status launch_nrt(int nrt, bool sparse, const KernelArgs& args, int n, hipStream_t st) {
@@ -1303,6 +1324,7 @@ static pa_status decode_impl(const pa_plan_t* plan, void* out, const void* q, co
   if (p.kv_dtype == PA_FP8_E4M3FN) {
     if (p.head_dim == 64) return launch_nrt<64, true>(P.nrt, sparse, args, n, st);
     if (p.head_dim == 128) return launch_nrt<128, true>(P.nrt, sparse, args, n, st);
+    if (p.head_dim == 512) return launch_nrt<512, true>(P.nrt, sparse, args, n, st);
     return launch_nrt<256, true>(P.nrt, sparse, args, n, st);
   }
   if (p.head_dim == 64) return launch_nrt<64, false>(P.nrt, sparse, args, n, st);
@@ -1392,10 +1414,13 @@ extern "C" pa_status pa_reduce(const pa_plan_t* plan, void* out, const float* si
   ra.rows_per_group = P.rows_per_group;
   ra.q_fp16 = P.prob.q_dtype == PA_FP16;
   ra.has_sinks = P.prob.has_sinks;
-  const int rr = P.prob.head_dim == 256 ? merge_rows<256>() : P.prob.head_dim == 64 ? merge_rows<64>() : merge_rows<128>();
+  const int D = P.prob.head_dim;
+  const int rr = D == 512 ? merge_rows<512>() : D == 256 ? merge_rows<256>() : D == 64 ? merge_rows<64>() : merge_rows<128>();
   ra.chunks_per_entry = (P.rows_per_group + rr - 1) / rr;
   const unsigned grid = (unsigned)(P.reduce.size() * ra.chunks_per_entry);
-  if (P.prob.head_dim == 256)
+  if (D == 512)
+    hipLaunchKernelGGL(pa_reduce_kernel<512>, dim3(grid), dim3(256), 0, (hipStream_t)stream, ra);
+  else if (P.prob.head_dim == 256)
     hipLaunchKernelGGL(pa_reduce_kernel<256>, dim3(grid), dim3(256), 0, (hipStream_t)stream, ra);
   else if (P.prob.head_dim == 64)
     hipLaunchKernelGGL(pa_reduce_kernel<64>, dim3(grid), dim3(256), 0, (hipStream_t)stream, ra);

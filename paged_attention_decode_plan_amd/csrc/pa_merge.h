@@ -45,7 +45,7 @@ __device__ __forceinline__ void merge_chunk(const MergeArgs& a, const ReduceItem
   constexpr int RR = merge_rows<D>();
   constexpr int Q4 = D / 4;
   constexpr int RCH = 16;  // partitions' loads in flight per round trip
-  static_assert(RR * Q4 == 256 && RR % 4 == 0, "one output per thread");
+  static_assert(RR * Q4 == 256, "one output per thread");
   const int tid = threadIdx.x;
   const bool act = tid < 256;
   const int rpg = a.rows_per_group;
@@ -69,7 +69,7 @@ __device__ __forceinline__ void merge_chunk(const MergeArgs& a, const ReduceItem
   // per-row weights: wave w takes rows w, w + 4, ..., lanes over partitions
   // (p = lane + 64k); the rows' (max, sum) loads are issued together
   if (act) {
-    constexpr int XR = RR / 4;
+    constexpr int XR = (RR + 3) / 4;  // rows per wave (head dim 512: two rows, waves 2 and 3 idle)
     const int wv = tid >> 6, lane = tid & 63;
     float mv[XR][4], lv[XR][4], skv[XR];
 #pragma unroll
@@ -86,7 +86,7 @@ __device__ __forceinline__ void merge_chunk(const MergeArgs& a, const ReduceItem
 #pragma unroll
     for (int x = 0; x < XR; ++x) {
       const int rw = wv + 4 * x;
-      if (r0 + rw >= nrows) continue;  // wave-uniform
+      if (rw >= RR || r0 + rw >= nrows) continue;  // wave-uniform
       float M = -INFINITY;
 #pragma unroll
       for (int k = 0; k < 4; ++k)

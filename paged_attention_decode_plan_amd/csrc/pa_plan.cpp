@@ -71,8 +71,10 @@ pa_status validate_problem(const pa_problem* p) {
   double cache_elems = (double)p->num_pages * p->num_kv_heads * p->page_size * p->head_dim;
   if (cache_elems > (double)(1ull << 40)) return set_error(PA_ERR_INVALID, "cache larger than 2^40 elements");
   // Valid but not implemented here.
-  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
-    return set_error(PA_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256");
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256 && p->head_dim != 512)
+    return set_error(PA_ERR_UNSUPPORTED, "head_dim must be 64, 128, 256 or 512");
+  if (p->head_dim == 512 && (p->kv_dtype != PA_FP8_E4M3FN || p->token_table))
+    return set_error(PA_ERR_UNSUPPORTED, "head_dim 512 needs FP8 caches and page tables");
   if (p->page_size < 16 || p->page_size > 1024 || (p->page_size & (p->page_size - 1)))
     return set_error(PA_ERR_UNSUPPORTED, "page_size must be a power of two from 16 to 1024");
   if (p->token_table && p->page_size > kTileTokens)

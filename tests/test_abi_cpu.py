@@ -51,6 +51,9 @@ def _prob(**kw):
     (dict(scale_mode="none"), NotImplementedError),
     (dict(kv_dtype="bf16"), NotImplementedError),  # BF16 with a scale
     (dict(kv_dtype="bf16", scale_mode="none", head_dim=256), NotImplementedError),
+    (dict(kv_dtype="bf16", scale_mode="none", head_dim=512), NotImplementedError),
+    (dict(head_dim=1024), NotImplementedError),
+    (dict(head_dim=512, token_table=True), NotImplementedError),
     (dict(token_table=True, sliding_window=4), NotImplementedError),
     (dict(token_table=True, query_len=2), NotImplementedError),
     (dict(num_pages=1 << 30, head_dim=256, page_size=128, num_kv_heads=8, num_q_heads=8), ValueError),

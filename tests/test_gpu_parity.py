@@ -91,6 +91,26 @@ def test_d64(kv, scale, page):
         seed += 1
 
 
+@pytest.mark.parametrize("scale", ["tensor", "token"])
+@pytest.mark.parametrize("page", [16, 64, 128, 256])
+def test_d512(scale, page):
+    """Head dim 512 (FP8 caches: the one-stage tile pipeline): 8 to 64 rows
+    per KV head, windows, sinks, plain and transposed V, BF16 and FP16
+    queries, one and several partitions (the reducer at 512 dims)."""
+    seed = 4500 + page + 7 * (scale == "token")
+    lens = [0, 1, 127, 129, 700, 3000]
+    cases = [(1, 8, 1, 0, False, False, "bf16"), (2, 16, 2, 17, True, True, "fp16"), (4, 16, 2, 0, False, True, "bf16"),
+             (4, 16, 1, 257, True, False, "bf16")]
+    for ql, hq, hkv, window, sinks, vt, qd in cases:
+        inp = W.make_dense_case(seed, lens, query_len=ql, num_q_heads=hq, num_kv_heads=hkv, head_dim=512,
+                                page_size=page, q_dtype=qd, v_transposed=vt, scale_mode=scale,
+                                sliding_window=window, has_sinks=sinks)
+        announce(f"d512 {scale} page={page} ql={ql} hq={hq} hkv={hkv} w={window} sinks={sinks} vt={vt} q={qd}")
+        _parity(inp, cu_count=64)
+        _parity(inp, cu_count=4, max_partitions=1, stage_limit=3)
+        seed += 1
+
+
 LARGE_PAGE_CASES = [
     # name, query_len, Hq, Hkv, D, kv dtype, scale mode, window, sinks, transposed V
     ("tile16-fp8", 1, 16, 4, 128, "fp8", "token", 257, True, False),

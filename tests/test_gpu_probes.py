@@ -151,6 +151,13 @@ def test_planted_digits_large_pages(rows, page, vt):
     _dense_probe(ql, hq, 1, 128, page, vt, "token", L=2 * page + 300, seed=390 + rows + page + vt)
 
 
+@pytest.mark.parametrize("ql,page,vt,scale", [(1, 16, False, "tensor"), (4, 64, True, "token"), (2, 128, False, "token"),
+                                            (4, 256, True, "tensor")])
+def test_planted_digits_d512(ql, page, vt, scale):
+    announce(f"planted digits d512 ql={ql} page={page} vt={vt} scale={scale}")
+    _dense_probe(ql, 16, 1, 512, page, vt, scale, seed=395 + ql + page)
+
+
 @pytest.mark.parametrize("kv,scale", [("fp8", "tensor"), ("fp8", "token"), ("bf16", "none")])
 @pytest.mark.parametrize("ql,page,vt", [(1, 16, False), (4, 64, True), (2, 32, False)])
 def test_planted_digits_d64(kv, scale, ql, page, vt):

@@ -101,6 +101,8 @@ CASES = [
     ("d256-token", 1, 8, 1, 256, 16, "fp8", "token", "token"),
     ("bf16-keys", 1, 8, 1, 128, 16, "bf16", "none", "bf16"),
     ("d64-token", 4, 16, 1, 64, 64, "fp8", "token", "token"),
+    ("d512-token", 2, 16, 1, 512, 64, "fp8", "token", "token"),
+    ("d512-stairs", 1, 8, 1, 512, 128, "fp8", "tensor", "stairs"),
     ("d64-bf16-keys", 2, 16, 1, 64, 16, "bf16", "none", "bf16"),
     ("bf16-keys-64rows", 4, 16, 1, 128, 128, "bf16", "none", "bf16"),
 ]
