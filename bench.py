@@ -245,12 +245,17 @@ def measure(workload: str, steps: int, warmup: int, dev):
     for k in range(max(warmup, nc)):
         call(k % nc)
     torch.cuda.synchronize()
-    assert torch.isfinite(out.float()).all(), f"{workload}: non-finite output"
     t_start = time.perf_counter()
     us_warm = region(lambda k: call(0))
     us_cold = region(lambda k: call(k % nc))
     dec_us = region(lambda k: call(k % nc, reduce=False))
     timed_wall = time.perf_counter() - t_start
+    # Checked after the timed regions: the first torch kernels of a process
+    # load their code objects, and the GPU idling meanwhile lowers its clocks
+    # for the next milliseconds (a check placed before the regions cost the
+    # dense MTP4 batch 3-5 us per call in the first measurement of a process).
+    call(0)
+    assert torch.isfinite(out.float()).all(), f"{workload}: non-finite output"
     res = {
         "description": WORKLOADS[workload],
         "kernel": kernel_of(p, info),

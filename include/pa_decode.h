@@ -74,11 +74,12 @@ typedef enum { PA_SCALE_NONE = 0, PA_SCALE_PER_TENSOR = 1, PA_SCALE_PER_TOKEN = 
  *   slot = P % page); positions outside [0, table_stride * page_size) are
  *   clamped to it (never read outside the row; such a position attends the
  *   clamped token).  query_len 1, no window.
- * Built configurations (others: PA_ERR_UNSUPPORTED): head_dim 64, 128 or
- * 256; page_size a power of two from 16 to 1024 (token tables: at most
- * 128; pages above 128 tokens are read as 128-token sub-pages); FP8 e4m3fn
- * caches with a per-tensor or per-token scale at any of those head dims,
- * BF16 caches (no scale, BF16 queries) at head_dim 64 or 128.
+ * Built configurations (others: PA_ERR_UNSUPPORTED): head_dim 64, 128,
+ * 256 or 512; page_size a power of two from 16 to 1024 (token tables: at
+ * most 128; pages above 128 tokens are read as 128-token sub-pages); FP8
+ * e4m3fn caches with a per-tensor or per-token scale at any of those head
+ * dims (512: page tables only, token_table = 0), BF16 caches (no scale,
+ * BF16 queries) at head_dim 64 or 128.
  */
 typedef struct {
   int32_t num_seqs, query_len, num_q_heads, num_kv_heads, head_dim, page_size;
