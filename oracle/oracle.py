@@ -56,6 +56,10 @@ def lib():
             L.orc_bf16.argtypes = [ctypes.c_uint16]
             L.orc_fp16.restype = ctypes.c_double
             L.orc_fp16.argtypes = [ctypes.c_uint16]
+            L.orc_fp4_e2m1.restype = ctypes.c_double
+            L.orc_fp4_e2m1.argtypes = [ctypes.c_uint8]
+            L.orc_e8m0.restype = ctypes.c_double
+            L.orc_e8m0.argtypes = [ctypes.c_uint8]
             vp = ctypes.c_void_p
             L.orc_attend.restype = ctypes.c_int
             L.orc_attend.argtypes = [ctypes.POINTER(OrcProblem), vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -73,6 +77,14 @@ def fp8_value(code: int) -> float:
     return lib().orc_fp8_e4m3fn(code)
 
 
+def fp4_value(code: int) -> float:
+    return lib().orc_fp4_e2m1(code)
+
+
+def e8m0_value(code: int) -> float:
+    return lib().orc_e8m0(code)
+
+
 def bf16_value(bits: int) -> float:
     return lib().orc_bf16(bits)
 
@@ -84,8 +96,8 @@ def fp16_value(bits: int) -> float:
 def _problem(p, held=None) -> OrcProblem:
     return OrcProblem(
         p.num_seqs, p.query_len, p.num_q_heads, p.num_kv_heads, p.head_dim, p.page_size, p.num_pages,
-        p.table_stride, 1 if p.q_dtype == "fp16" else 0, 2 if p.kv_dtype == "fp8" else 0, int(p.v_transposed),
-        {"none": 0, "tensor": 1, "token": 2}[p.scale_mode], int(p.causal), int(p.sliding_window),
+        p.table_stride, 1 if p.q_dtype == "fp16" else 0, {"bf16": 0, "fp8": 2, "mxfp4": 3}[p.kv_dtype],
+        int(p.v_transposed), {"none": 0, "tensor": 1, "token": 2, "mx": 3}[p.scale_mode], int(p.causal), int(p.sliding_window),
         int(p.has_sinks), int(p.token_table), float(p.scale), int(getattr(p, "index_stride", 0)),
         None if held is None else held.topk_ptr,
     )

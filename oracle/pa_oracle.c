@@ -42,6 +42,19 @@
  * The FP8 e4m3fn decoder is written from the OCP 8-bit floating point
  * definition: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits,
  * subnormals at exponent 0, S.1111.111 is NaN, no infinities.
+ *
+ * MXFP4 caches (the MXFP4 K/V of aiter PR #7079's merge of #7056, which
+ * states only that such caches take 256-token partitions; the format is the
+ * OCP Microscaling (MX) one): each token's K or V row is cut into blocks of
+ * 32 consecutive head dims; a block holds 32 FP4 E2M1 codes and one E8M0
+ * scale, and element = fp4(code) * 2^(scale - 127).  FP4 E2M1: 1 sign bit,
+ * 2 exponent bits with bias 1, 1 mantissa bit, subnormal at exponent 0
+ * (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives), no NaN or
+ * infinity.  E8M0: an unsigned exponent, 0xFF is NaN.  Two codes share a
+ * byte, the lower index in the low nibble.  Layouts:
+ *   K  [pages, Hkv, D/32, page, 16 bytes]   (the 32 codes of block d/32)
+ *   V  [pages, Hkv, D, page/2 bytes]        (row d: token 2j low nibble)
+ *   k and v scales: one byte per block, [pages, Hkv, page, D/32].
  */
 #include <math.h>
 #include <pthread.h>
@@ -52,16 +65,18 @@
 #define ORC_BF16 0
 #define ORC_FP16 1
 #define ORC_FP8 2
+#define ORC_MXFP4 3
 
 #define ORC_SCALE_NONE 0
 #define ORC_SCALE_TENSOR 1
 #define ORC_SCALE_TOKEN 2
+#define ORC_SCALE_MX 3
 
 typedef struct {
   int num_seqs, query_len, num_q_heads, num_kv_heads, head_dim, page_size;
   int num_pages, table_stride;
   int q_kind;      /* ORC_BF16 or ORC_FP16 */
-  int kv_kind;     /* ORC_BF16 or ORC_FP8 */
+  int kv_kind;     /* ORC_BF16, ORC_FP8 or ORC_MXFP4 */
   int v_transposed;
   int scale_mode;
   int causal, window, has_sinks, token_table;
@@ -98,6 +113,19 @@ double orc_fp16(uint16_t h) {
   else if (e == 0) v = ldexp((double)m / 1024.0, -14);
   else v = ldexp(1.0 + (double)m / 1024.0, e - 15);
   return sign ? -v : v;
+}
+
+double orc_fp4_e2m1(uint8_t c) {
+  int sign = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+  double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1); /* subnormal: 0.m * 2^(1-1) */
+  return sign ? -v : v;
+}
+
+double orc_e8m0(uint8_t e) { return e == 0xFF ? NAN : ldexp(1.0, (int)e - 127); }
+
+static double orc_nibble(const uint8_t* bytes, long byte_index, int high) {
+  uint8_t b = bytes[byte_index];
+  return orc_fp4_e2m1(high ? (uint8_t)(b >> 4) : (uint8_t)(b & 0xF));
 }
 
 /* ---- addressing ---- */
@@ -142,10 +170,25 @@ static double orc_scale(const orc_problem* p, const float* sc, long page, int g,
   return (double)sc[(page * p->num_kv_heads + g) * p->page_size + slot];
 }
 
+/* block scale of (page, slot, KV head g, block b) of an MXFP4 cache */
+static double orc_mx_scale(const orc_problem* p, const void* sc, long page, int g, int slot, int b) {
+  const uint8_t* e = (const uint8_t*)sc;
+  return orc_e8m0(e[((page * p->num_kv_heads + g) * p->page_size + slot) * (p->head_dim / 32) + b]);
+}
+
 /* dequantised K row of token (page, slot) for KV head g */
 static void orc_k_row(const orc_problem* p, const void* k_cache, const float* k_scale, long page, int slot, int g,
                       double* out) {
   int D = p->head_dim, ps = p->page_size;
+  if (p->kv_kind == ORC_MXFP4) {
+    long base = (page * p->num_kv_heads + g) * (long)(D / 2) * ps;
+    for (int d = 0; d < D; ++d) {
+      int b = d / 32, j = d % 32;
+      out[d] = orc_nibble((const uint8_t*)k_cache, base + ((long)b * ps + slot) * 16 + j / 2, j & 1) *
+               orc_mx_scale(p, k_scale, page, g, slot, b);
+    }
+    return;
+  }
   int x = p->kv_kind == ORC_FP8 ? 16 : 8;
   double sc = orc_scale(p, k_scale, page, g, slot);
   long base = (page * p->num_kv_heads + g) * (long)D * ps;
@@ -158,6 +201,13 @@ static void orc_k_row(const orc_problem* p, const void* k_cache, const float* k_
 static void orc_v_row(const orc_problem* p, const void* v_cache, const float* v_scale, long page, int slot, int g,
                       double* out) {
   int D = p->head_dim, ps = p->page_size;
+  if (p->kv_kind == ORC_MXFP4) {
+    long base = (page * p->num_kv_heads + g) * (long)D * (ps / 2);
+    for (int d = 0; d < D; ++d)
+      out[d] = orc_nibble((const uint8_t*)v_cache, base + (long)d * (ps / 2) + slot / 2, slot & 1) *
+               orc_mx_scale(p, v_scale, page, g, slot, d / 32);
+    return;
+  }
   int x = p->kv_kind == ORC_FP8 ? 16 : 8;
   double sc = orc_scale(p, v_scale, page, g, slot);
   long base = (page * p->num_kv_heads + g) * (long)D * ps;

@@ -14,7 +14,12 @@ aiter PR #6617 "Extend packed D256 PA decode pipe", summary):
 * plain V ``[pages, Hkv, D, page]``; transposed V ``[pages, Hkv, page/x, D, x]``;
 * int32 ``block_tables [num_seqs, table_stride]`` and ``context_lens [num_seqs]``;
 * FP32 scales: one per tensor, or per token ``[pages, Hkv, page]``;
-* FP32 sink logits ``[Hq]``.
+* FP32 sink logits ``[Hq]``;
+* MXFP4 caches (OCP microscaling FP4: 32-dim blocks of E2M1 codes, two per
+  byte with the lower index in the low nibble, one E8M0 scale byte per
+  block): K ``[pages, Hkv, D/32, page, 16]``, V ``[pages, Hkv, D, page/2]``
+  (row d holds the page's tokens in order), scales uint8
+  ``[pages, Hkv, page, D/32]``.
 
 Quantisation to FP8 e4m3fn uses torch's round-to-nearest-even cast after
 clamping to +-448 (the format's largest finite value).  BF16 rounding is
@@ -23,8 +28,13 @@ torch's round-to-nearest-even.
 Positions that no query row can see (tail slots of a sequence's last page,
 slots before a sliding window, pages that are never referenced) are filled
 with poison when ``poison=True``: FP8 byte 0x7F and BF16 0x7FC0 (both NaN),
-and per-token scales of 1e30.  A correct decode never lets them reach the
-output.
+and per-token scales of 1e30; MXFP4 poison is the scale byte 0xFF (NaN).
+A correct decode never lets them reach the output.
+
+MXFP4 quantisation of a 32-dim block: shared exponent e = floor(log2 amax) -
+2 (the largest E2M1 power), clamped into E8M0's range, then each element
+x / 2^e rounded to the nearest E2M1 value (ties to the even code),
+saturating at +-6; an all-zero block takes the scale byte 0.
 """
 
 from __future__ import annotations
@@ -43,9 +53,13 @@ SCALE_POISON = 1.0e30
 
 KV_FP8 = "fp8"
 KV_BF16 = "bf16"
+KV_MXFP4 = "mxfp4"
 SCALE_NONE = "none"
 SCALE_TENSOR = "tensor"
 SCALE_TOKEN = "token"
+SCALE_MX = "mx"
+FP4_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)  # E2M1 magnitudes of codes 0-7
+MX_POISON = 0xFF  # E8M0 NaN
 
 
 @dataclasses.dataclass
@@ -59,9 +73,9 @@ class Problem:
     num_pages: int
     table_stride: int
     q_dtype: str = "bf16"  # "bf16" | "fp16"
-    kv_dtype: str = KV_FP8  # "fp8" | "bf16"
+    kv_dtype: str = KV_FP8  # "fp8" | "bf16" | "mxfp4"
     v_transposed: bool = False
-    scale_mode: str = SCALE_TENSOR  # "none" | "tensor" | "token"
+    scale_mode: str = SCALE_TENSOR  # "none" | "tensor" | "token" | "mx"
     causal: bool = True
     sliding_window: int = 0
     has_sinks: bool = False
@@ -114,6 +128,37 @@ def to_bf16(x: np.ndarray) -> torch.Tensor:
 def to_fp8_bytes(x: torch.Tensor) -> torch.Tensor:
     """float32 tensor -> uint8 e4m3fn codes (RNE, saturating at +-448)."""
     return x.clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def to_mxfp4(x: torch.Tensor):
+    """float32 [..., D] -> (E2M1 codes uint8 [..., D] in 0..15, E8M0 scale
+    bytes uint8 [..., D/32])."""
+    *lead, D = x.shape
+    xb = x.reshape(*lead, D // 32, 32)
+    amax = xb.abs().amax(-1)
+    e = torch.where(amax > 0, torch.floor(torch.log2(amax)) - 2, torch.full_like(amax, -127.0)).clamp(-127, 127)
+    scaled = xb / torch.exp2(e)[..., None]
+    grid = torch.tensor(FP4_GRID, dtype=torch.float32)
+    dist = (scaled.abs().clamp(max=6.0)[..., None] - grid).abs()
+    dist = dist + (torch.arange(8) % 2).to(torch.float32) * 1e-6  # ties to the even code
+    code = dist.argmin(-1).to(torch.uint8)
+    code = torch.where((scaled < 0) & (code > 0), code | 8, code)
+    return code.reshape(*lead, D), (e + 127).to(torch.uint8)
+
+
+def _layout_k_mx(codes: torch.Tensor) -> torch.Tensor:
+    """E2M1 codes [P, H, page, D] -> packed K [P, H, D/32, page, 16] bytes."""
+    P, H, page, D = codes.shape
+    c = codes.reshape(P, H, page, D // 32, 16, 2)
+    b = c[..., 0] | (c[..., 1] << 4)
+    return b.permute(0, 1, 3, 2, 4).contiguous()
+
+
+def _layout_v_mx(codes: torch.Tensor) -> torch.Tensor:
+    """E2M1 codes [P, H, page, D] -> V [P, H, D, page/2] bytes."""
+    P, H, page, D = codes.shape
+    c = codes.permute(0, 1, 3, 2).reshape(P, H, D, page // 2, 2)
+    return (c[..., 0] | (c[..., 1] << 4)).contiguous()
 
 
 def visible_span(L: int, query_len: int, window: int, causal: bool):
@@ -189,6 +234,35 @@ def build_dense(
     vals_v = torch.from_numpy(rkv.standard_normal((nreal, H, page, D), dtype=np.float32)) * kv_amplitude
 
     k_scale = v_scale = None
+    if prob.kv_dtype == KV_MXFP4:
+        qk, ksr = to_mxfp4(vals_k)
+        qv, vsr = to_mxfp4(vals_v)
+        kl = torch.zeros((P, H, page, D), dtype=torch.uint8)
+        vl = torch.zeros((P, H, page, D), dtype=torch.uint8)
+        k_scale = torch.full((P, H, page, D // 32), MX_POISON if poison else 127, dtype=torch.uint8)
+        v_scale = torch.full((P, H, page, D // 32), MX_POISON if poison else 127, dtype=torch.uint8)
+        if nreal:
+            idx = torch.from_numpy(real_pages)
+            kl[idx] = qk
+            vl[idx] = qv
+            k_scale[idx] = ksr
+            v_scale[idx] = vsr
+            if poison:
+                # slots of a real page outside the visible span: NaN scales
+                for pid in real_pages.tolist():
+                    lo_s, hi_s = int(valid_lo[pid]), int(valid_hi[pid])
+                    k_scale[pid, :, :lo_s] = MX_POISON
+                    v_scale[pid, :, :lo_s] = MX_POISON
+                    k_scale[pid, :, hi_s:] = MX_POISON
+                    v_scale[pid, :, hi_s:] = MX_POISON
+        sinks = None
+        if prob.has_sinks:
+            sinks = torch.from_numpy(rs.standard_normal(prob.num_q_heads, dtype=np.float32))
+        return Inputs(
+            problem=prob, q=qt.contiguous(), k_cache=_layout_k_mx(kl), v_cache=_layout_v_mx(vl),
+            block_tables=torch.from_numpy(np.ascontiguousarray(block_tables, dtype=np.int32)),
+            context_lens=torch.from_numpy(np.ascontiguousarray(context_lens, dtype=np.int32)),
+            k_scale=k_scale, v_scale=v_scale, sinks=sinks, name=name)
     if fp8:
         if prob.scale_mode == SCALE_TOKEN:
             ks_real = vals_k.abs().amax(dim=3) / FP8_MAX  # [nreal, H, page]
@@ -314,7 +388,8 @@ def make_dense_case(
         num_seqs=len(lens), query_len=query_len, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
         head_dim=head_dim, page_size=page_size, num_pages=num_pages, table_stride=stride,
         q_dtype=q_dtype, kv_dtype=kv_dtype, v_transposed=v_transposed,
-        scale_mode=scale_mode if kv_dtype == KV_FP8 else SCALE_NONE, causal=causal,
+        scale_mode=scale_mode if kv_dtype == KV_FP8 else (SCALE_MX if kv_dtype == KV_MXFP4 else SCALE_NONE),
+        causal=causal,
         sliding_window=sliding_window, has_sinks=has_sinks,
     )
     return build_dense(prob, lens.astype(np.int32), bt, seed, fill=fill, poison=poison,
@@ -548,8 +623,11 @@ def kv_bytes_visible(inp: Inputs) -> int:
     """Algorithmic KV bytes of one call: K + V (+ per-token K and V scales) of
     the visible-token union of every (sequence, KV head), counted once."""
     p = inp.problem
-    elem = 1 if p.kv_dtype == KV_FP8 else 2
-    per_tok = 2 * p.head_dim * elem + (8 if (p.kv_dtype == KV_FP8 and p.scale_mode == SCALE_TOKEN) else 0)
+    if p.kv_dtype == KV_MXFP4:  # half a byte per element, one scale byte per 32-dim block, K and V
+        per_tok = 2 * (p.head_dim // 2 + p.head_dim // 32)
+    else:
+        elem = 1 if p.kv_dtype == KV_FP8 else 2
+        per_tok = 2 * p.head_dim * elem + (8 if (p.kv_dtype == KV_FP8 and p.scale_mode == SCALE_TOKEN) else 0)
     lens = inp.context_lens.numpy().astype(np.int64)
     tot = 0
     for s in range(p.num_seqs):
