@@ -50,9 +50,9 @@ typedef enum {
   PA_ERR_DEVICE = 4       /* a HIP runtime call failed */
 } pa_status;
 
-typedef enum { PA_BF16 = 0, PA_FP16 = 1, PA_FP8_E4M3FN = 2 } pa_dtype;
+typedef enum { PA_BF16 = 0, PA_FP16 = 1, PA_FP8_E4M3FN = 2, PA_MXFP4 = 3 } pa_dtype;
 typedef enum { PA_V_PLAIN = 0, PA_V_TRANSPOSED = 1 } pa_v_layout;
-typedef enum { PA_SCALE_NONE = 0, PA_SCALE_PER_TENSOR = 1, PA_SCALE_PER_TOKEN = 2 } pa_scale_mode;
+typedef enum { PA_SCALE_NONE = 0, PA_SCALE_PER_TENSOR = 1, PA_SCALE_PER_TOKEN = 2, PA_SCALE_MX = 3 } pa_scale_mode;
 
 /*
  * Problem statement.  Layouts (x = 16 bytes / KV element size: 16 for FP8,
@@ -74,6 +74,23 @@ typedef enum { PA_SCALE_NONE = 0, PA_SCALE_PER_TENSOR = 1, PA_SCALE_PER_TOKEN = 
  *   slot = P % page); positions outside [0, table_stride * page_size) are
  *   clamped to it (never read outside the row; such a position attends the
  *   clamped token).  query_len 1, no window.
+ * MXFP4 caches (kv_dtype PA_MXFP4, scale_mode PA_SCALE_MX; aiter PR #7079,
+ *   merge of #7056, names MXFP4 K/V and its 256-token partitions; the format
+ *   is OCP microscaling FP4): every token's K and V row is cut into blocks
+ *   of 32 head dims, each of 32 E2M1 codes and one E8M0 scale byte e
+ *   (element = code value * 2^(e - 127)); two codes share a byte, the lower
+ *   index in the low nibble.
+ *     k_cache  uint8 [num_pages, num_kv_heads, head_dim/32, page_size, 16]
+ *     v_cache  uint8 [num_pages, num_kv_heads, head_dim, page_size/2]
+ *              (row d: the page's tokens in order, two per byte)
+ *     k/v scales uint8 [num_pages, num_kv_heads, page_size, head_dim/32],
+ *              passed through the k_scale / v_scale pointers, 16-byte
+ *              aligned; a scale byte 0xFF (NaN) of a visible token gives
+ *              unspecified results.
+ *   head_dim 128, page_size 32, 64 or 128, page tables (token_table 0),
+ *   v_layout PA_V_PLAIN; partitions are cut at multiples of 256 tokens of
+ *   the visible span (pa_plan_opts.partition_tokens 0 or 256); plans are
+ *   not refreshable.
  * Built configurations (others: PA_ERR_UNSUPPORTED): head_dim 64, 128,
  * 256 or 512; page_size a power of two from 16 to 1024 (token tables: at
  * most 128; pages above 128 tokens are read as 128-token sub-pages); FP8
@@ -85,9 +102,9 @@ typedef struct {
   int32_t num_seqs, query_len, num_q_heads, num_kv_heads, head_dim, page_size;
   int32_t num_pages, table_stride;
   int32_t q_dtype;    /* pa_dtype: PA_BF16 or PA_FP16 */
-  int32_t kv_dtype;   /* pa_dtype: PA_FP8_E4M3FN or PA_BF16 */
+  int32_t kv_dtype;   /* pa_dtype: PA_FP8_E4M3FN, PA_BF16 or PA_MXFP4 */
   int32_t v_layout;   /* pa_v_layout */
-  int32_t scale_mode; /* pa_scale_mode; FP8 needs PER_TENSOR or PER_TOKEN, BF16 needs NONE */
+  int32_t scale_mode; /* pa_scale_mode; FP8 needs PER_TENSOR or PER_TOKEN, BF16 NONE, MXFP4 MX */
   int32_t causal, sliding_window, has_sinks, token_table;
   float softmax_scale;  /* <= 0: 1/sqrt(head_dim) */
   int32_t index_stride; /* token_table = 2: row stride of the top-k index table (pa_decode_sparse) */

@@ -19,9 +19,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpa.so")
 
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_DEVICE = range(5)
-PA_BF16, PA_FP16, PA_FP8_E4M3FN = range(3)
+PA_BF16, PA_FP16, PA_FP8_E4M3FN, PA_MXFP4 = range(4)
 PA_V_PLAIN, PA_V_TRANSPOSED = range(2)
-PA_SCALE_NONE, PA_SCALE_PER_TENSOR, PA_SCALE_PER_TOKEN = range(3)
+PA_SCALE_NONE, PA_SCALE_PER_TENSOR, PA_SCALE_PER_TOKEN, PA_SCALE_MX = range(4)
 
 EXPORTS = ["pa_plan", "pa_plan_sizes", "pa_plan_info", "pa_plan_work", "pa_plan_upload", "pa_plan_free", "pa_decode",
            "pa_reduce", "pa_plan_refresh", "pa_attend_static", "pa_decode_sparse", "pa_mqa_logits", "pa_topk",
@@ -110,8 +110,8 @@ def _check(st: int):
 def make_problem(num_seqs, query_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages, table_stride,
                  q_dtype="bf16", kv_dtype="fp8", v_transposed=False, scale_mode="tensor", causal=True,
                  sliding_window=0, has_sinks=False, token_table=0, softmax_scale=0.0, index_stride=0) -> PaProblem:
-    dt = {"bf16": PA_BF16, "fp16": PA_FP16, "fp8": PA_FP8_E4M3FN}
-    sm = {"none": PA_SCALE_NONE, "tensor": PA_SCALE_PER_TENSOR, "token": PA_SCALE_PER_TOKEN}
+    dt = {"bf16": PA_BF16, "fp16": PA_FP16, "fp8": PA_FP8_E4M3FN, "mxfp4": PA_MXFP4}
+    sm = {"none": PA_SCALE_NONE, "tensor": PA_SCALE_PER_TENSOR, "token": PA_SCALE_PER_TOKEN, "mx": PA_SCALE_MX}
     return PaProblem(num_seqs, query_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages, table_stride,
                      dt[q_dtype], dt[kv_dtype], PA_V_TRANSPOSED if v_transposed else PA_V_PLAIN, sm[scale_mode],
                      int(causal), int(sliding_window), int(has_sinks), int(token_table), float(softmax_scale),
@@ -246,9 +246,12 @@ def _check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, k_s
         raise ValueError("block_tables and context_lens must be int32")
     if out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must match q in shape and dtype")
-    for name, t in (("k_scale", k_scale), ("v_scale", v_scale), ("sinks", sinks)):
-        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda):
-            raise ValueError(f"{name} must be a contiguous float32 device tensor")
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        # float32 scales, or the E8M0 bytes of MXFP4 caches
+        if t is not None and (t.dtype not in (torch.float32, torch.uint8) or not t.is_contiguous() or not t.is_cuda):
+            raise ValueError(f"{name} must be a contiguous float32 (uint8 for MXFP4) device tensor")
+    if sinks is not None and (sinks.dtype != torch.float32 or not sinks.is_contiguous() or not sinks.is_cuda):
+        raise ValueError("sinks must be a contiguous float32 device tensor")
 
 
 def pa_attend_static(plan: Plan, out, q, k_cache, v_cache, block_tables, context_lens, k_scale=None, v_scale=None,

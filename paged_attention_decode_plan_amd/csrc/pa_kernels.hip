@@ -61,15 +61,19 @@ struct Waves {
   static constexpr int NW = (NRT >= 2 && D <= 128) ? 8 : 4;
   static constexpr int NT = 64 * NW;
 };
-template <int D, bool FP8, int NT>
+// MX: MXFP4 caches (FP4 codes, two per byte, and a scale byte per 32-dim
+// block; FP8 is set as well, the query and probability paths being FP8's).
+template <int D, bool FP8, int NT, bool MX = false>
 struct Tile {
-  static constexpr int E = FP8 ? 1 : 2;      // bytes per KV element
-  static constexpr int X = 16 / E;           // elements per 16-byte chunk
-  static constexpr int KBYTES = D * TT * E;  // K tile: [D/X chunks][TT tokens][16 B]
-  static constexpr int VROW = TT * E;        // V tile: [D rows][TT tokens]
+  static constexpr int E = FP8 ? 1 : 2;      // bytes per KV element (MX: half a byte)
+  static constexpr int X = MX ? 32 : 16 / E;  // elements per 16-byte chunk
+  static constexpr int KBYTES = MX ? D * TT / 2 : D * TT * E;  // K tile: [D/X chunks][TT tokens][16 B]
+  static constexpr int VROW = MX ? TT / 2 : TT * E;             // V tile: [D rows][TT tokens]
   static constexpr int VBYTES = D * VROW;
   static constexpr int VUPR = VROW / 16;     // 16-byte units per V row
-  static constexpr int SBYTES = FP8 ? 2 * TT * 4 : 0;  // per-token k and v scales
+  // per-token k and v scales (FP32), or (MX) the blocks' scale bytes: D/32
+  // per token, which is 4 bytes at head dim 128, laid out alike
+  static constexpr int SBYTES = MX ? 2 * TT * (D / 32) : FP8 ? 2 * TT * 4 : 0;
   static constexpr int STAGE = KBYTES + VBYTES + SBYTES;
   static constexpr int KPT = KBYTES / 16 / NT;  // 16-byte K units per thread per tile
   static constexpr int VPT = VBYTES / 16 / NT;
@@ -91,13 +95,13 @@ struct Roles {
   static_assert(WR * WT == NW && WT <= 4 && NRW * WR == NRT, "wave roles");
 };
 
-template <int D, bool FP8, int NRT, bool SPARSE>
+template <int D, bool FP8, int NRT, bool SPARSE, bool MX = false>
 struct Smem {
   using R = Roles<D, NRT>;
   // head dim 512: one 128-token FP8 stage is 129 KB, so a single stage (the
   // tile's loads, then its compute, no overlap inside the workgroup)
   static constexpr int STAGES = D >= 512 ? 1 : (!SPARSE && FP8 && D == 128 && NRT >= 2) ? 4 : 2;
-  static constexpr int STAGE = Tile<D, FP8, Waves<NRT, D>::NT>::STAGE;
+  static constexpr int STAGE = Tile<D, FP8, Waves<NRT, D>::NT, MX>::STAGE;
   static constexpr int MERGE = NRT * 16 * (D + 4) * 4;  // one O buffer with padded rows
   static constexpr int MAIN = (STAGES * STAGE > MERGE) ? STAGES * STAGE : MERGE;
   static constexpr int IDS = kStageCap * 4;
@@ -113,12 +117,13 @@ struct Staged {
   u32x4 s;
 };
 
-template <int D, bool FP8, int NRT, bool SPARSE>
+template <int D, bool FP8, int NRT, bool SPARSE, bool MX = false>
 __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelArgs a) {
+  static_assert(!MX || (FP8 && D == 128 && !SPARSE), "MXFP4: head dim 128, page tables");
   constexpr int NTHREADS = Waves<NRT, D>::NT;
   constexpr int NWAVES = Waves<NRT, D>::NW;
-  using T = Tile<D, FP8, NTHREADS>;
-  using S = Smem<D, FP8, NRT, SPARSE>;
+  using T = Tile<D, FP8, NTHREADS, MX>;
+  using S = Smem<D, FP8, NRT, SPARSE, MX>;
   using R = Roles<D, NRT>;
   constexpr int NST = S::STAGES;
   constexpr int NRW = R::NRW;
@@ -233,11 +238,18 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
     const uint16_t* qrow = (const uint16_t*)a.q + (((long)s * a.QL + i) * a.Hq + (long)kvh * a.G + hl) * D;
 #pragma unroll
     for (int x = 0; x < NQR; ++x)
-      qraw[rt][x] = FP8 ? (32 * g < D ? *(const u32x4*)(qrow + 128 * (x / 4) + 32 * g + 8 * (x % 4))
+      // MX: the FP4 form of the QK MFMA pairs nibble j of A lane group g
+      // (dim 32g + j of its scale block) with B element 64(g&1) + 16(g>>1) +
+      // 32(j>>4) + (j&15), so B lane group g holds dims 16g .. 16g+15, then
+      // 64+16g .. 64+16g+15
+      qraw[rt][x] = MX    ? *(const u32x4*)(qrow + 64 * (x / 2) + 16 * g + 8 * (x % 2))
+                    : FP8 ? (32 * g < D ? *(const u32x4*)(qrow + 128 * (x / 4) + 32 * g + 8 * (x % 4))
                                       : u32x4{0, 0, 0, 0})  // head dim 64: lane groups 2, 3 hold no dims
                         : *(const u32x4*)(qrow + 32 * x + 8 * g);
   }
-  const bool per_token = FP8 && a.scale_mode == PA_SCALE_PER_TOKEN;
+  // MX block scales take the per-token path (scales staged with each tile,
+  // V scales folded into P against a reference)
+  const bool per_token = FP8 && (MX || a.scale_mode == PA_SCALE_PER_TOKEN);
   const float kscale0 = (FP8 && !per_token) ? a.k_scale[0] : 1.0f;  // per-tensor scales
   const float vscale0 = (FP8 && !per_token) ? a.v_scale[0] : 1.0f;
   const uint8_t* kbase = a.k_cache + (long long)kvh * a.head_stride;
@@ -260,13 +272,14 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   const int v_tok = ((tid % T::VUPR) ^ (v_row & (T::VUPR - 1))) * T::X;  // first token of the unit
   const int v_pg = v_tok / ps;
   const int v_sx = (v_tok % ps) / T::X;
-  const long v_off = a.v_transposed ? ((long)v_sx * D + v_row) * 16 : (long)v_row * pps * T::E + v_sx * 16;
-  const long v_step = a.v_transposed ? (long)VRS * 16 : (long)VRS * pps * T::E;
+  const long vrow_bytes = MX ? (long)pps / 2 : (long)pps * T::E;  // a V row of one page
+  const long v_off = a.v_transposed ? ((long)v_sx * D + v_row) * 16 : (long)v_row * vrow_bytes + v_sx * 16;
+  const long v_step = a.v_transposed ? (long)VRS * 16 : (long)VRS * vrow_bytes;
   // Byte offsets of a (sub-)page id inside its cache / scale array: the
   // page's block plus the sub-page's place in it (K: token offset in every
   // chunk; plain V: column offset in every row; transposed V: its 16-token
   // blocks; scales: token offset).
-  const long vsub_bytes = a.v_transposed ? (long)(ps / T::X) * D * 16 : (long)ps * T::E;
+  const long vsub_bytes = a.v_transposed ? (long)(ps / T::X) * D * 16 : MX ? (long)ps / 2 : (long)ps * T::E;
   const long msk = (1L << psub) - 1;
   auto kpage = [&](long id) { return (id >> psub) * a.page_stride + (id & msk) * ps * 16; };
   auto vpage = [&](long id) { return (id >> psub) * a.page_stride + (id & msk) * vsub_bytes; };
@@ -448,6 +461,14 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   }
   if (per_token) vs_ref = 0.f;
   float inv_ref = per_token ? 0.f : 1.0f;
+  // MX: one V-scale reference per 32-dim block (blocks of one token may lie
+  // binades apart; a shared reference would push the FP16 products of the
+  // smaller blocks into subnormals), O of block b holding sum p*v / vrb[b]
+  constexpr int NVB = MX ? D / 32 : 1;
+  float vrb[NVB], vib[NVB], vhb[NVB];
+#pragma unroll
+  for (int b4 = 0; b4 < NVB; ++b4) vrb[b4] = vib[b4] = vhb[b4] = 0.f;
+  if (MX) vs_ref = inv_ref = 1.0f;
 
   // ---- online softmax state (lane holds row (wr*NRW+rt)*16+c) ----
   // Probabilities are exp2(score - m_ref) with m_ref a reference maximum set
@@ -623,7 +644,23 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
       __builtin_amdgcn_sched_barrier(0);
       const int tok = 32 * tg + 8 * (c >> 2) + 4 * b + (c & 3);
       const uint8_t* krow = kl + kswz(tok) * 16;
-      if constexpr (FP8) {
+      if constexpr (MX) {
+        // K as FP4 (A operand, the low four registers): lane group g holds
+        // block g (dims 32g .. 32g+31) of token tok, which the MFMA scales
+        // by the block's E8M0 byte
+        const u32x4 k4 = *(const u32x4*)(krow + g * TT * 16);
+        const i32x8 kf = i32x8{(int)k4[0], (int)k4[1], (int)k4[2], (int)k4[3], 0, 0, 0, 0};
+        const int kse = (int)((*(const uint32_t*)((const uint8_t*)sl + tok * 4) >> (8 * g)) & 0xFF);
+#pragma unroll
+        for (int rt = 0; rt < NRW; ++rt) {
+          sacc[rt][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf[rt][0][0], sacc[rt][b], 4, 0, 0, kse,
+                                                                         0, 127);
+          sacc[rt][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf[rt][0][1], sacc[rt][b], 4, 0, 0, kse,
+                                                                         0, 123);
+          sacc[rt][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf[rt][0][2], sacc[rt][b], 4, 0, 0, kse,
+                                                                         0, 119);
+        }
+      } else if constexpr (FP8) {
 #pragma unroll
         for (int kk = 0; kk < NQ; ++kk) {
           // head dim 64: lane groups 2, 3 would read past the K tile; their
@@ -664,7 +701,41 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
       vb = min(max(hi_u - tv, 0), 8);
     }
     float ks[8], vsr[8];
-    if constexpr (PT) {
+    float vmx[MX ? D / 32 : 1][8];  // MX: V block scales of the lane's tokens, per block
+    if constexpr (MX) {
+      // scale bytes of tokens tl .. tl+7, D/32 per token (one 32-bit word at D128)
+      const uint8_t* vsb = (const uint8_t*)(sl + TT) + tl * 4;
+      const u32x4 w0 = *(const u32x4*)vsb, w1 = *(const u32x4*)(vsb + 16);
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const uint32_t wd = p < 4 ? w0[p] : w1[p - 4];
+#pragma unroll
+        for (int b4 = 0; b4 < D / 32; ++b4) {
+          const uint32_t e = (wd >> (8 * b4)) & 0xFF;  // E8M0: 2^(e - 127); e = 0 is the subnormal 2^-127
+          float f = __uint_as_float(e == 0 ? 0x00400000u : e << 23);
+          if constexpr (!IN) f = (p >= va && p < vb) ? f : 0.f;  // scales outside the span are not read
+          vmx[b4][p] = f;
+        }
+      }
+#pragma unroll
+      for (int b4 = 0; b4 < D / 32; ++b4) {
+        float vmax = vmx[b4][0];
+#pragma unroll
+        for (int p = 1; p < 8; ++p) vmax = fmaxf(vmax, vmx[b4][p]);
+        vmax = group_max(vmax);  // wave-uniform
+        if (vrb[b4] == 0.f) {
+          if (vmax > 0.f) {
+            vrb[b4] = vmax;
+            vib[b4] = __builtin_amdgcn_rcpf(vmax);
+          }
+        } else if (vmax > vrb[b4] * VS_BAND) {
+          ovf = true;
+          vhb[b4] = fmaxf(vhb[b4], vmax);
+        }
+#pragma unroll
+        for (int p = 0; p < 8; ++p) vmx[b4][p] *= vib[b4];
+      }
+    } else if constexpr (PT) {
       f4 k0 = *(const f4*)(sl + tl), k1 = *(const f4*)(sl + tl + 4);
       f4 v0 = *(const f4*)(sl + TT + tl), v1 = *(const f4*)(sl + TT + tl + 4);
 #pragma unroll
@@ -703,7 +774,7 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
         float v = sacc[rt][p >> 2][p & 3];
-        if constexpr (PT) v *= ks[p];
+        if constexpr (PT && !MX) v *= ks[p];  // MX: the K scales are inside the MFMA
         if constexpr (!IN) {
           const int t = tv + p;
           v = (t >= lo_r[rt] && t <= hi_r[rt]) ? v : -INFINITY;
@@ -726,6 +797,7 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
     using PFrag = typename std::conditional<FP8, half8, bf16x8>::type;
     PFrag pf[NRW];
     PFrag pl[NRW];  // BF16 caches: low part of a two-term split of P
+    half8 pfx[MX ? D / 32 : 1][NRW];  // MX: P times each V block's relative scale
 #pragma unroll
     for (int rt = 0; rt < NRW; ++rt) {
       const float nm = m_ref[rt] == -INFINITY ? 0.f : -m_ref[rt];
@@ -734,9 +806,18 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
       for (int p = 0; p < 8; ++p) {
         pr[p] = __builtin_amdgcn_exp2f(__builtin_fmaf(y[rt][p], crow[rt], nm));  // exp2(-inf) = 0
         l_part[rt] += pr[p];
-        if constexpr (PT) pr[p] *= vsr[p];
+        if constexpr (PT && !MX) pr[p] *= vsr[p];
       }
-      if constexpr (FP8) {
+      if constexpr (MX) {
+#pragma unroll
+        for (int b4 = 0; b4 < D / 32; ++b4)
+#pragma unroll
+          for (int p = 0; p < 8; p += 2) {
+            h2 hp = __builtin_convertvector(f2{pr[p] * vmx[b4][p], pr[p + 1] * vmx[b4][p + 1]}, h2);
+            pfx[b4][rt][p] = hp[0];
+            pfx[b4][rt][p + 1] = hp[1];
+          }
+      } else if constexpr (FP8) {
 #pragma unroll
         for (int p = 0; p < 8; p += 2) {
           h2 hp = __builtin_convertvector(f2{pr[p], pr[p + 1]}, h2);
@@ -768,7 +849,21 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
       if (dt % (NDT / 4) == 0) __builtin_amdgcn_sched_barrier(0);
       const int d = 16 * dt + c;
       const uint8_t* vrow = vl + d * T::VROW;
-      if constexpr (FP8) {
+      if constexpr (MX) {
+        // row d of the tile: 32-token units with the unit index swizzled by
+        // d mod 4; the lane's tokens 8g .. 8g+7 of step tg are 4 bytes of
+        // unit tg.  FP4 has no NaN: masked tokens need no V mask (their P is
+        // 0 and their scale factor 0).
+        const uint32_t raw = *(const uint32_t*)(vrow + ((tg ^ (d & (T::VUPR - 1))) * 16) + 4 * g);
+        const h2 h0 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw, 1.0f, 0));
+        const h2 h1 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw, 1.0f, 1));
+        const h2 h2_ = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw, 1.0f, 2));
+        const h2 h3 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw, 1.0f, 3));
+        const half8 vf = half8{h0[0], h0[1], h1[0], h1[1], h2_[0], h2_[1], h3[0], h3[1]};
+#pragma unroll
+        for (int rt = 0; rt < NRW; ++rt)
+          o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pfx[dt / 2][rt], o[rt][dt], 0, 0, 0);
+      } else if constexpr (FP8) {
         const int q = (2 * tg + (g >> 1)) ^ (d & 7);
         u32x2 raw = *(const u32x2*)(vrow + q * 16 + (g & 1) * 8);
         if constexpr (!IN) {
@@ -942,11 +1037,19 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
         vs_ref = vs_hi;
         inv_ref = 1.0f / vs_ref;
       }
+#pragma unroll
+      for (int b4 = 0; b4 < NVB; ++b4)
+        if (vhb[b4] > vrb[b4]) {
+          vrb[b4] = vhb[b4];
+          vib[b4] = 1.0f / vrb[b4];
+        }
       ovf = false;
       __syncthreads();
     }
   };
-  if constexpr (FP8) {
+  if constexpr (MX) {
+    run(std::true_type{});
+  } else if constexpr (FP8) {
     if (per_token)
       run(std::true_type{});
     else
@@ -1025,7 +1128,7 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           f4* dst = (f4*)(obuf + ((wr * NRW + rt) * 16 + c) * OROW + 16 * dt + 4 * g);
-          const f4 v = o[rt][dt] * fw[rt];
+          const f4 v = o[rt][dt] * (MX ? fw[rt] * vrb[dt / 2] : fw[rt]);
           *dst = (k == 0) ? v : *dst + v;
         }
     }
@@ -1233,20 +1336,20 @@ __global__ __launch_bounds__(REF_T) void pa_refresh_kernel(RefreshArgs a) {
 // ---------------------------------------------------------------------------
 // Launch selection
 // ---------------------------------------------------------------------------
-template <int D, bool FP8, int NRT, bool SPARSE>
+template <int D, bool FP8, int NRT, bool SPARSE, bool MX = false>
 static pa_status launch_one(const KernelArgs& args, int nblocks, hipStream_t stream) {
-  constexpr int bytes = Smem<D, FP8, NRT, SPARSE>::TOTAL;
+  constexpr int bytes = Smem<D, FP8, NRT, SPARSE, MX>::TOTAL;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   static bool configured = false;
   if (!configured) {
-    if (hipFuncSetAttribute((const void*)pa_decode_kernel<D, FP8, NRT, SPARSE>,
+    if (hipFuncSetAttribute((const void*)pa_decode_kernel<D, FP8, NRT, SPARSE, MX>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess) {
       (void)hipGetLastError();
       return set_error(PA_ERR_DEVICE, "hipFuncSetAttribute failed");
     }
     configured = true;
   }
-  hipLaunchKernelGGL((pa_decode_kernel<D, FP8, NRT, SPARSE>), dim3(nblocks), dim3((Waves<NRT, D>::NT)), bytes, stream,
+  hipLaunchKernelGGL((pa_decode_kernel<D, FP8, NRT, SPARSE, MX>), dim3(nblocks), dim3((Waves<NRT, D>::NT)), bytes, stream,
                      args);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(PA_ERR_DEVICE, std::string("decode launch failed: ") + hipGetErrorString(err));
@@ -1284,10 +1387,10 @@ static pa_status decode_impl(const pa_plan_t* plan, void* out, const void* q, co
     return set_error(PA_ERR_INVALID, "a required device pointer is NULL");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return set_error(PA_ERR_INVALID, "q, out, k_cache and v_cache must be 16-byte aligned");
-  if (p.kv_dtype == PA_FP8_E4M3FN) {
-    if (!k_scale || !v_scale) return set_error(PA_ERR_INVALID, "FP8 caches need k_scale and v_scale");
-    if (p.scale_mode == PA_SCALE_PER_TOKEN && (!aligned16(k_scale) || !aligned16(v_scale)))
-      return set_error(PA_ERR_INVALID, "per-token scales must be 16-byte aligned");
+  if (p.kv_dtype == PA_FP8_E4M3FN || p.kv_dtype == PA_MXFP4) {
+    if (!k_scale || !v_scale) return set_error(PA_ERR_INVALID, "FP8 and MXFP4 caches need k_scale and v_scale");
+    if (p.scale_mode != PA_SCALE_PER_TENSOR && (!aligned16(k_scale) || !aligned16(v_scale)))
+      return set_error(PA_ERR_INVALID, "per-token and block scales must be 16-byte aligned");
   }
   if (p.has_sinks && !sinks) return set_error(PA_ERR_INVALID, "has_sinks set but sinks is NULL");
   if (!meta_dev) return set_error(PA_ERR_WORKSPACE, "meta_dev is NULL");
@@ -1295,7 +1398,9 @@ static pa_status decode_impl(const pa_plan_t* plan, void* out, const void* q, co
     return set_error(PA_ERR_WORKSPACE, "meta_dev does not hold this plan's metadata: call pa_plan_upload first");
   if (P.num_slots > 0 && !workspace_dev) return set_error(PA_ERR_WORKSPACE, "workspace_dev is NULL");
   hipStream_t st = (hipStream_t)stream;
-  const int elem = p.kv_dtype == PA_FP8_E4M3FN ? 1 : 2;
+  // bytes of head_dim * page_size elements of one KV head's page
+  const long long head_bytes = (long long)p.head_dim * p.page_size *
+                               (p.kv_dtype == PA_BF16 ? 2 : 1) / (p.kv_dtype == PA_MXFP4 ? 2 : 1);
   KernelArgs args;
   args.out = out;
   args.q = q;
@@ -1314,7 +1419,7 @@ static pa_status decode_impl(const pa_plan_t* plan, void* out, const void* q, co
   args.tag_hi = (uint32_t)(P.serial >> 32);
   args.workspace = (float*)workspace_dev;
   args.merge_ctr = P.in_kernel_merge ? (int*)((uint8_t*)meta_dev + P.counters_offset()) : nullptr;
-  args.head_stride = (long long)p.head_dim * p.page_size * elem;
+  args.head_stride = head_bytes;
   args.page_stride = args.head_stride * p.num_kv_heads;
   args.QL = p.query_len;
   args.Hq = p.num_q_heads;
@@ -1339,6 +1444,11 @@ static pa_status decode_impl(const pa_plan_t* plan, void* out, const void* q, co
   const int n = (int)P.items.size();
   const bool sparse = p.token_table != 0;
   if (stream_kernel_applies(P)) return launch_stream(P, args, n, st);
+  if (p.kv_dtype == PA_MXFP4) {  // head dim 128, page tables (validated)
+    if (P.nrt == 1) return launch_one<128, true, 1, false, true>(args, n, st);
+    if (P.nrt == 2) return launch_one<128, true, 2, false, true>(args, n, st);
+    return launch_one<128, true, 4, false, true>(args, n, st);
+  }
   if (p.kv_dtype == PA_FP8_E4M3FN) {
     if (p.head_dim == 64) return launch_nrt<64, true>(P.nrt, sparse, args, n, st);
     if (p.head_dim == 128) return launch_nrt<128, true>(P.nrt, sparse, args, n, st);

@@ -59,10 +59,10 @@ pa_status validate_problem(const pa_problem* p) {
   if (p->num_seqs > 0 && p->table_stride < 1) return set_error(PA_ERR_INVALID, "table_stride < 1");
   if (p->sliding_window < 0) return set_error(PA_ERR_INVALID, "sliding_window < 0");
   if (p->q_dtype != PA_BF16 && p->q_dtype != PA_FP16) return set_error(PA_ERR_INVALID, "q_dtype must be BF16 or FP16");
-  if (p->kv_dtype != PA_FP8_E4M3FN && p->kv_dtype != PA_BF16)
-    return set_error(PA_ERR_INVALID, "kv_dtype must be FP8_E4M3FN or BF16");
+  if (p->kv_dtype != PA_FP8_E4M3FN && p->kv_dtype != PA_BF16 && p->kv_dtype != PA_MXFP4)
+    return set_error(PA_ERR_INVALID, "kv_dtype must be FP8_E4M3FN, BF16 or MXFP4");
   if (p->v_layout != PA_V_PLAIN && p->v_layout != PA_V_TRANSPOSED) return set_error(PA_ERR_INVALID, "bad v_layout");
-  if (p->scale_mode < PA_SCALE_NONE || p->scale_mode > PA_SCALE_PER_TOKEN)
+  if (p->scale_mode < PA_SCALE_NONE || p->scale_mode > PA_SCALE_MX)
     return set_error(PA_ERR_INVALID, "bad scale_mode");
   if ((p->causal | p->has_sinks) & ~1) return set_error(PA_ERR_INVALID, "flags must be 0 or 1");
   if (p->token_table < 0 || p->token_table > 2) return set_error(PA_ERR_INVALID, "token_table must be 0, 1 or 2");
@@ -89,6 +89,13 @@ pa_status validate_problem(const pa_problem* p) {
     return set_error(PA_ERR_UNSUPPORTED, "BF16 caches need BF16 queries");
   if (p->token_table && (p->sliding_window > 0 || p->query_len != 1))
     return set_error(PA_ERR_UNSUPPORTED, "token tables need query_len 1 and no sliding window");
+  if ((p->kv_dtype == PA_MXFP4) != (p->scale_mode == PA_SCALE_MX))
+    return set_error(PA_ERR_UNSUPPORTED, "MXFP4 caches take (only) the MX block scales");
+  if (p->kv_dtype == PA_MXFP4 &&
+      (p->head_dim != 128 || p->page_size < 32 || p->page_size > kTileTokens || p->token_table ||
+       p->v_layout != PA_V_PLAIN))
+    return set_error(PA_ERR_UNSUPPORTED,
+                     "MXFP4 caches: head_dim 128, page_size 32 to 128, page tables and the plain V layout");
   return PA_OK;
 }
 
@@ -121,6 +128,10 @@ extern "C" pa_status pa_plan(const pa_problem* problem, const int32_t* context_l
     return set_error(PA_ERR_INVALID, "plan options must be >= 0");
   if (o.refreshable & ~1) return set_error(PA_ERR_INVALID, "refreshable must be 0 or 1");
   const pa_problem& p = *problem;
+  // MXFP4 caches take 256-token partitions (aiter PR #7079, merge of #7056)
+  const bool mx = p.kv_dtype == PA_MXFP4;
+  if (mx && (o.refreshable || (o.partition_tokens != 0 && o.partition_tokens != 2 * kTileTokens)))
+    return set_error(PA_ERR_UNSUPPORTED, "MXFP4 plans take 256-token partitions and are not refreshable");
 
   int cu = o.cu_count;
   if (cu == 0) {
@@ -167,6 +178,11 @@ extern "C" pa_status pa_plan(const pa_problem* problem, const int32_t* context_l
     long t0 = p.token_table ? 0 : (lo / vps) * vps;
     seq_tiles[s] = hi > lo ? (int)ceil_div(hi - t0, kTileTokens) : 0;
   }
+  // Partitions are cut at multiples of gran tiles of the span (MXFP4: 256
+  // tokens); the choices below count in those units.
+  const int gran = mx ? 2 : 1;
+  std::vector<int> seq_units(p.num_seqs, 0);
+  for (int s = 0; s < p.num_seqs; ++s) seq_units[s] = (int)ceil_div(seq_tiles[s], gran);
 
   // Units: (sequence, KV head, row group).  Choose partition counts.
   const int units_per_seq = p.num_kv_heads * P.row_groups;
@@ -175,15 +191,15 @@ extern "C" pa_status pa_plan(const pa_problem* problem, const int32_t* context_l
   const int occ = resident_per_cu(p, P.nrt);
   const long slots_budget = std::max<long>((long)cu * occ, nunits);
   if (o.partition_tokens > 0) {
-    int tiles_per_part = (int)ceil_div(o.partition_tokens, kTileTokens);
+    int units_per_part = (int)ceil_div(ceil_div(o.partition_tokens, kTileTokens), gran);
     for (int s = 0; s < p.num_seqs; ++s)
-      parts[s] = std::max(1, std::min<int>({(int)ceil_div(seq_tiles[s], tiles_per_part), maxp,
-                                            std::max(seq_tiles[s], 1)}));
+      parts[s] = std::max(1, std::min<int>({(int)ceil_div(seq_units[s], units_per_part), maxp,
+                                            std::max(seq_units[s], 1)}));
   } else {
     // Greedy: split the sequence with the longest work item while the shorter
     // makespan outweighs the added partial traffic and the budget allows.
-    const double elem = p.kv_dtype == PA_FP8_E4M3FN ? 1.0 : 2.0;
-    const double tile_bytes = kTileTokens * (2.0 * p.head_dim * elem + 8.0);
+    const double elem = p.kv_dtype == PA_FP8_E4M3FN ? 1.0 : mx ? 0.5 : 2.0;
+    const double tile_bytes = gran * kTileTokens * (2.0 * p.head_dim * elem + 8.0);  // of one unit
     const double partial_bytes = P.rows_per_group * (p.head_dim + 2.0) * 4.0;
     const double cost_per_item = 2.0 * partial_bytes / (tile_bytes * cu);  // in tile-times
     // The reducer takes a unit's partitions eight at a time, one memory
@@ -197,18 +213,18 @@ extern "C" pa_status pa_plan(const pa_problem* problem, const int32_t* context_l
       using E = std::pair<long, int>;  // (current longest item tiles, seq)
       std::priority_queue<E> pq;
       for (int s = 0; s < p.num_seqs; ++s)
-        if (seq_tiles[s] > 1) pq.push({seq_tiles[s], s});
+        if (seq_units[s] > 1) pq.push({seq_units[s], s});
       while (!pq.empty()) {
         auto [len, s] = pq.top();
         pq.pop();
         if (len <= 1) continue;
         // the smallest partition count that shortens this sequence's longest
         // item (one more partition may not, when the tiles do not divide)
-        const int np = (int)ceil_div(seq_tiles[s], len - 1);
-        if (np > maxp || np > seq_tiles[s]) continue;
+        const int np = (int)ceil_div(seq_units[s], len - 1);
+        if (np > maxp || np > seq_units[s]) continue;
         const long add = (long)(np - pr[s]) * units_per_seq;
         if (items + add > budget) break;
-        long newlen = ceil_div(seq_tiles[s], np);
+        long newlen = ceil_div(seq_units[s], np);
         // the first split of a sequence also creates its first partial slots
         double added = cost_per_item * units_per_seq * ((np - pr[s]) + (pr[s] == 1 ? 1 : 0)) +
                        reduce_per_part * (np - pr[s]);
@@ -233,7 +249,7 @@ extern "C" pa_status pa_plan(const pa_problem* problem, const int32_t* context_l
       auto makespan = [&](const std::vector<int>& pr) {
         std::vector<double> len;
         for (int s = 0; s < p.num_seqs; ++s) {
-          const int nt = seq_tiles[s], np = pr[s];
+          const int nt = seq_units[s], np = pr[s];
           for (int part = 0; part < np; ++part) {
             const int t = nt / np + (part < nt % np ? 1 : 0);
             for (int u = 0; u < units_per_seq; ++u)
@@ -270,7 +286,7 @@ extern "C" pa_status pa_plan(const pa_problem* problem, const int32_t* context_l
   P.total_tiles = 0;
   for (int s = 0; s < p.num_seqs; ++s) {
     int np = parts[s];
-    int nt = seq_tiles[s];
+    int nt = seq_units[s];
     P.max_parts = std::max(P.max_parts, np);
     for (int g = 0; g < p.num_kv_heads; ++g)
       for (int rg = 0; rg < P.row_groups; ++rg) {
@@ -286,6 +302,8 @@ extern "C" pa_status pa_plan(const pa_problem* problem, const int32_t* context_l
           int base = nt / np, extra = nt % np;
           int b = part * base + std::min(part, extra);
           int e = b + base + (part < extra ? 1 : 0);
+          b *= gran;
+          e = std::min(e * gran, seq_tiles[s]);
           WorkItem w{s, g, rg, b, part == np - 1 ? -1 : e, np > 1 ? first + part : -1, part, np};
           P.items.push_back(w);
           P.total_tiles += e - b;

@@ -31,11 +31,11 @@ def to_device(inp, device="cuda"):
 def check_shapes(inp, dev):
     """Host-side check that the tensors match the problem before any launch."""
     p = inp.problem
-    elem = 1 if p.kv_dtype == "fp8" else 2
     per_page = p.num_kv_heads * p.head_dim * p.page_size
+    cache_bytes = {"fp8": per_page, "bf16": 2 * per_page, "mxfp4": per_page // 2}[p.kv_dtype] * p.num_pages
     assert dev["q"].shape == (p.rows, p.num_q_heads, p.head_dim)
-    assert dev["k_cache"].numel() * dev["k_cache"].element_size() == p.num_pages * per_page * elem
-    assert dev["v_cache"].numel() * dev["v_cache"].element_size() == p.num_pages * per_page * elem
+    assert dev["k_cache"].numel() * dev["k_cache"].element_size() == cache_bytes
+    assert dev["v_cache"].numel() * dev["v_cache"].element_size() == cache_bytes
     assert dev["block_tables"].shape == (p.num_seqs, p.table_stride)
     assert dev["context_lens"].shape == (p.num_seqs,)
     bt = inp.block_tables.cpu().numpy()
@@ -51,6 +51,9 @@ def check_shapes(inp, dev):
         assert (used >= 0).all() and (used < lim).all(), "table entry out of range"
     if p.kv_dtype == "fp8" and p.scale_mode == "token":
         assert dev["k_scale"].shape == (p.num_pages, p.num_kv_heads, p.page_size)
+    if p.kv_dtype == "mxfp4":
+        for t in (dev["k_scale"], dev["v_scale"]):
+            assert t.dtype == torch.uint8 and t.shape == (p.num_pages, p.num_kv_heads, p.page_size, p.head_dim // 32)
 
 
 def run(inp, dev=None, plan=None, lens_for_plan=None, **plan_kw):
