@@ -48,6 +48,8 @@ WORKLOADS = {
     "dense_mtp4_fp8": "dense MTP4 verify, FP8 KV, per-token scales: B32 Hq16/Hkv1 D128 QL4 page128 L~U[16K,32K]",
     "dense_mtp4_bf16": "dense MTP4 verify, BF16 KV: B32 Hq16/Hkv1 D128 QL4 page128 L~U[16K,32K]",
     "dense_mtp2_fp8": "supplementary: the dense MTP4 FP8 batch with QL2 (32 rows per KV head), same caches and tables",
+    "dense_mtp4_mxfp4": "supplementary: the dense MTP4 batch with MXFP4 KV (E2M1 codes, an E8M0 scale per 32 dims), "
+                        "256-token partitions",
     "long_mtp4_c200k": "supplementary: the pages' MI355X shape: B200 QL4 Hq16/Hkv1 D128 page128, every context "
                        "200000, FP8 per-token, plain V; 5 partitions per sequence (the pages' best NP)",
     "long_d256": "long-context D256: B4 Hkv2 GQA8 QL4 page64 L=131072 window 8193, transposed V, per-tensor",
@@ -60,13 +62,13 @@ WORKLOADS = {
 }
 # Measured after the headline line by default, into its "workloads" object.
 EXTRA_WORKLOADS = ["tiny", "sparse", "sparse_topk", "long_d256", "long_d256_nowindow", "ragged", "dense_mtp4_bf16",
-                   "dense_mtp2_fp8", "long_mtp4_c200k"]
+                   "dense_mtp2_fp8", "dense_mtp4_mxfp4", "long_mtp4_c200k"]
 # Shapes whose time is HBM streaming of the KV bytes (a roofline claim); the
 # tiny and ragged batches are latency-bound and the sparse batches gather
 # from a pool that stays in the 256 MB Infinity Cache: for those the
 # bandwidth figure is an effective rate, not a roofline fraction.
-ROOFLINE_CLAIM = {"dense_mtp4_fp8", "dense_mtp4_bf16", "dense_mtp2_fp8", "long_d256", "long_d256_nowindow",
-                  "long_mtp4_c200k"}
+ROOFLINE_CLAIM = {"dense_mtp4_fp8", "dense_mtp4_bf16", "dense_mtp2_fp8", "dense_mtp4_mxfp4", "long_d256",
+                  "long_d256_nowindow", "long_mtp4_c200k"}
 
 
 # The pages' own MI355X figure for a workload, where they give one: the
@@ -131,6 +133,8 @@ def make_inputs(workload: str):
         return W.config_ragged(), {}
     if workload == "dense_mtp4_bf16":
         return W.config_dense_mtp4("bf16"), {}
+    if workload == "dense_mtp4_mxfp4":
+        return W.config_dense_mtp4("mxfp4"), {}
     if workload == "dense_mtp2_fp8":
         return W.config_dense_mtp4("fp8", query_len=2), {}
     if workload == "long_mtp4_c200k":  # drawn on the device: 10.56 GB of KV

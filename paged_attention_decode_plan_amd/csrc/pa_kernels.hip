@@ -120,6 +120,7 @@ struct Staged {
 template <int D, bool FP8, int NRT, bool SPARSE, bool MX = false>
 __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelArgs a) {
   static_assert(!MX || (FP8 && D == 128 && !SPARSE), "MXFP4: head dim 128, page tables");
+  static_assert(!MX || Roles<D, NRT>::NRW == 1, "MXFP4: one row tile per wave (per-step scale references)");
   constexpr int NTHREADS = Waves<NRT, D>::NT;
   constexpr int NWAVES = Waves<NRT, D>::NW;
   using T = Tile<D, FP8, NTHREADS, MX>;
@@ -461,13 +462,14 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   }
   if (per_token) vs_ref = 0.f;
   float inv_ref = per_token ? 0.f : 1.0f;
-  // MX: one V-scale reference per 32-dim block (blocks of one token may lie
-  // binades apart; a shared reference would push the FP16 products of the
-  // smaller blocks into subnormals), O of block b holding sum p*v / vrb[b]
+  // MX: one V-scale reference exponent per 32-dim block (blocks of one token
+  // may lie binades apart; a shared reference would push the FP16 products
+  // of the smaller blocks into subnormals); O of block b holds
+  // sum p * v * 2^(e - erb[b]); -1: no visible token yet
   constexpr int NVB = MX ? D / 32 : 1;
-  float vrb[NVB], vib[NVB], vhb[NVB];
+  int erb[NVB], ehb[NVB];
 #pragma unroll
-  for (int b4 = 0; b4 < NVB; ++b4) vrb[b4] = vib[b4] = vhb[b4] = 0.f;
+  for (int b4 = 0; b4 < NVB; ++b4) erb[b4] = ehb[b4] = -1;
   if (MX) vs_ref = inv_ref = 1.0f;
 
   // ---- online softmax state (lane holds row (wr*NRW+rt)*16+c) ----
@@ -701,40 +703,11 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
       vb = min(max(hi_u - tv, 0), 8);
     }
     float ks[8], vsr[8];
-    float vmx[MX ? D / 32 : 1][8];  // MX: V block scales of the lane's tokens, per block
+    u32x4 vsw[2];  // MX: the V scale bytes of the lane's tokens tl .. tl+7 (one word per token at D128)
     if constexpr (MX) {
-      // scale bytes of tokens tl .. tl+7, D/32 per token (one 32-bit word at D128)
       const uint8_t* vsb = (const uint8_t*)(sl + TT) + tl * 4;
-      const u32x4 w0 = *(const u32x4*)vsb, w1 = *(const u32x4*)(vsb + 16);
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const uint32_t wd = p < 4 ? w0[p] : w1[p - 4];
-#pragma unroll
-        for (int b4 = 0; b4 < D / 32; ++b4) {
-          const uint32_t e = (wd >> (8 * b4)) & 0xFF;  // E8M0: 2^(e - 127); e = 0 is the subnormal 2^-127
-          float f = __uint_as_float(e == 0 ? 0x00400000u : e << 23);
-          if constexpr (!IN) f = (p >= va && p < vb) ? f : 0.f;  // scales outside the span are not read
-          vmx[b4][p] = f;
-        }
-      }
-#pragma unroll
-      for (int b4 = 0; b4 < D / 32; ++b4) {
-        float vmax = vmx[b4][0];
-#pragma unroll
-        for (int p = 1; p < 8; ++p) vmax = fmaxf(vmax, vmx[b4][p]);
-        vmax = group_max(vmax);  // wave-uniform
-        if (vrb[b4] == 0.f) {
-          if (vmax > 0.f) {
-            vrb[b4] = vmax;
-            vib[b4] = __builtin_amdgcn_rcpf(vmax);
-          }
-        } else if (vmax > vrb[b4] * VS_BAND) {
-          ovf = true;
-          vhb[b4] = fmaxf(vhb[b4], vmax);
-        }
-#pragma unroll
-        for (int p = 0; p < 8; ++p) vmx[b4][p] *= vib[b4];
-      }
+      vsw[0] = *(const u32x4*)vsb;
+      vsw[1] = *(const u32x4*)(vsb + 16);
     } else if constexpr (PT) {
       f4 k0 = *(const f4*)(sl + tl), k1 = *(const f4*)(sl + tl + 4);
       f4 v0 = *(const f4*)(sl + TT + tl), v1 = *(const f4*)(sl + TT + tl + 4);
@@ -809,14 +782,36 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
         if constexpr (PT && !MX) pr[p] *= vsr[p];
       }
       if constexpr (MX) {
+        // per block: the lane's largest visible scale exponent checks the
+        // block's reference (2^3 band; above it the lane marks a restart and
+        // records the exponent), and each token's factor 2^(e - erb) goes
+        // into P as an exponent add (exact).  The reference is wave-uniform:
+        // set from the whole wave's step at its first visible tokens.
 #pragma unroll
-        for (int b4 = 0; b4 < D / 32; ++b4)
+        for (int b4 = 0; b4 < D / 32; ++b4) {
+          int ev[8];
+          int emx = -1;
+#pragma unroll
+          for (int p = 0; p < 8; ++p) {
+            ev[p] = (int)((vsw[p >> 2][p & 3] >> (8 * b4)) & 0xFF);
+            if constexpr (!IN) ev[p] = (p >= va && p < vb) ? ev[p] : -1;  // scales outside the span are not read
+            emx = max(emx, ev[p]);
+          }
+          if (erb[b4] < 0) {
+            erb[b4] = (int)group_max((float)emx);
+          } else if (emx > erb[b4] + 3) {
+            ovf = true;
+            ehb[b4] = max(ehb[b4], emx);
+          }
 #pragma unroll
           for (int p = 0; p < 8; p += 2) {
-            h2 hp = __builtin_convertvector(f2{pr[p] * vmx[b4][p], pr[p + 1] * vmx[b4][p + 1]}, h2);
+            const float p0 = __builtin_amdgcn_ldexpf(pr[p], ev[p] - erb[b4]);  // pr = 0 for masked tokens
+            const float p1 = __builtin_amdgcn_ldexpf(pr[p + 1], ev[p + 1] - erb[b4]);
+            h2 hp = __builtin_convertvector(f2{p0, p1}, h2);
             pfx[b4][rt][p] = hp[0];
             pfx[b4][rt][p + 1] = hp[1];
           }
+        }
       } else if constexpr (FP8) {
 #pragma unroll
         for (int p = 0; p < 8; p += 2) {
@@ -1038,11 +1033,7 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
         inv_ref = 1.0f / vs_ref;
       }
 #pragma unroll
-      for (int b4 = 0; b4 < NVB; ++b4)
-        if (vhb[b4] > vrb[b4]) {
-          vrb[b4] = vhb[b4];
-          vib[b4] = 1.0f / vrb[b4];
-        }
+      for (int b4 = 0; b4 < NVB; ++b4) erb[b4] = (int)group_max((float)max(erb[b4], ehb[b4]));  // wave-uniform
       ovf = false;
       __syncthreads();
     }
@@ -1128,7 +1119,7 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           f4* dst = (f4*)(obuf + ((wr * NRW + rt) * 16 + c) * OROW + 16 * dt + 4 * g);
-          const f4 v = o[rt][dt] * (MX ? fw[rt] * vrb[dt / 2] : fw[rt]);
+          const f4 v = o[rt][dt] * (MX ? fw[rt] * __builtin_amdgcn_ldexpf(1.0f, erb[dt / 2] - 127) : fw[rt]);
           *dst = (k == 0) ? v : *dst + v;
         }
     }

@@ -138,10 +138,12 @@ def to_mxfp4(x: torch.Tensor):
     amax = xb.abs().amax(-1)
     e = torch.where(amax > 0, torch.floor(torch.log2(amax)) - 2, torch.full_like(amax, -127.0)).clamp(-127, 127)
     scaled = xb / torch.exp2(e)[..., None]
-    grid = torch.tensor(FP4_GRID, dtype=torch.float32)
-    dist = (scaled.abs().clamp(max=6.0)[..., None] - grid).abs()
-    dist = dist + (torch.arange(8) % 2).to(torch.float32) * 1e-6  # ties to the even code
-    code = dist.argmin(-1).to(torch.uint8)
+    mag = scaled.abs()
+    # nearest magnitude: count the midpoints below; a tie goes to the even code
+    code = torch.zeros(mag.shape, dtype=torch.uint8)
+    for c in range(7):
+        mid = 0.5 * (FP4_GRID[c] + FP4_GRID[c + 1])
+        code += (mag > mid if c % 2 == 0 else mag >= mid).to(torch.uint8)
     code = torch.where((scaled < 0) & (code > 0), code | 8, code)
     return code.reshape(*lead, D), (e + 127).to(torch.uint8)
 
@@ -444,7 +446,7 @@ def config_dense_mtp4(kv_dtype: str = KV_FP8, poison: bool = True, num_seqs: int
     bt = disjoint_tables(rng[0], lens_pages, num_pages, stride)
     prob = Problem(num_seqs=num_seqs, query_len=query_len, num_q_heads=16, num_kv_heads=1, head_dim=128,
                    page_size=128, num_pages=num_pages, table_stride=stride, kv_dtype=kv_dtype,
-                   scale_mode=SCALE_TOKEN if kv_dtype == KV_FP8 else SCALE_NONE)
+                   scale_mode={KV_FP8: SCALE_TOKEN, KV_MXFP4: SCALE_MX}.get(kv_dtype, SCALE_NONE))
     return build_dense(prob, lens, bt, seed, fill="context", poison=poison, name=f"dense_mtp{query_len}_{kv_dtype}")
 
 
