@@ -988,16 +988,23 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
         load_sparse(tb, st);
         store_sparse(st, stage_base);
       }
+      // The gather's issue is bound by the vector memory unit's address
+      // processing (a tile's byte gathers take several times its compute),
+      // and a wave issuing loads cannot compute meanwhile.  Half the waves
+      // issue their share of the next tile before computing this one, the
+      // other half after, so the unit is kept busy through the compute.
+      const bool early = w >= NWAVES / 2;
       for (int tile = tb; tile < te; ++tile) {
         __syncthreads();
         if (!scan && *(volatile int*)restart_flag) break;
         const int cur = (tile - tb) & 1;
         const bool more = tile + 1 < te;
-        if (more) load_sparse(tile + 1, st);
+        if (more && early) load_sparse(tile + 1, st);
         if (tile >= ti0 && tile < ti1)
           compute_tile(PTc, std::true_type{}, tile, stage_base + cur * T::STAGE);
         else
           compute_tile(PTc, std::false_type{}, tile, stage_base + cur * T::STAGE);
+        if (more && !early) load_sparse(tile + 1, st);
         if (more) store_sparse(st, stage_base + (cur ^ 1) * T::STAGE);
       }
     }
