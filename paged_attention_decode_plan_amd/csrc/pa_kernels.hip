@@ -382,7 +382,11 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
   // is 32m + 8g + p.
   constexpr int NQ = FP8 ? (D + 127) / 128 : NM;  // QK k-steps (head dim 64: one, half of it zero)
   using QFrag = typename std::conditional<FP8, i32x8, bf16x8>::type;
-  QFrag qf[NRW][NQ][FP8 ? 3 : 1];
+  // query terms: three (about 12 significant bits), two at head dim 512
+  // (about 8: hi + mid/16), whose fragments and O accumulator would not fit
+  // the registers with three
+  constexpr int NQT = FP8 ? (D >= 512 ? 2 : 3) : 1;
+  QFrag qf[NRW][NQ][NQT];
   float crow[NRW];  // log2-domain score scale of the row (incl. the query scale)
 #pragma unroll
   for (int rt = 0; rt < NRW; ++rt) {
@@ -442,7 +446,7 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
           w2 = __builtin_amdgcn_cvt_pk_fp8_f32(r1[2], r1[3], w2, true);
           qf[rt][kk][0][j4] = w0;
           qf[rt][kk][1][j4] = w1;
-          qf[rt][kk][2][j4] = w2;
+          if constexpr (NQT > 2) qf[rt][kk][2][j4] = w2;
         }
       }
       crow[rt] = a.scale_log2 * qs;
@@ -678,8 +682,9 @@ __global__ __launch_bounds__((Waves<NRT, D>::NT)) void pa_decode_kernel(KernelAr
                                                                            127, 0, 127);
             sacc[rt][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf[rt][kk][1], sacc[rt][b], 0, 0, 0,
                                                                            127, 0, 123);
-            sacc[rt][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf[rt][kk][2], sacc[rt][b], 0, 0, 0,
-                                                                           127, 0, 119);
+            if constexpr (NQT > 2)
+              sacc[rt][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf[rt][kk][NQT - 1], sacc[rt][b], 0,
+                                                                             0, 0, 127, 0, 119);
           }
         }
       } else {
