@@ -23,10 +23,15 @@
 //  * QK^T is computed as S^T = K Q^T: FP8 caches run
 //    v_mfma_scale_f32_16x16x128_f8f6f4 with K as stored against three FP8
 //    terms of the query (hi, then two residuals, each with its own E8M0 block
-//    scale), BF16 caches run v_mfma_f32_16x16x32_bf16 with the BF16 query;
+//    scale; two terms at head dim 512), BF16 caches run
+//    v_mfma_f32_16x16x32_bf16 with the BF16 query, MXFP4 caches the scaled
+//    MFMA with FP4 K and each lane's block scale as the A scale (the query
+//    permuted to the FP4 operand's lane order);
 //  * PV is computed as O^T = V^T P^T: FP8 V converts exactly to FP16 in
 //    registers (v_cvt_scalef32_pk_f16_fp8) against FP16 probabilities on
-//    v_mfma_f32_16x16x32_f16; BF16 V runs against a two-term BF16 split of
+//    v_mfma_f32_16x16x32_f16 (MXFP4: FP4 V converts exactly as well, its
+//    block scales folded into the probabilities per 32-dim block as exponent
+//    adds against per-block references); BF16 V runs against a two-term BF16 split of
 //    the probabilities; probabilities go from the QK accumulator to the PV
 //    operand in registers (the QK rows are read in the token order PV
 //    contracts);
