@@ -10,6 +10,9 @@
            instruction counts -> MFMA busy fraction of the kernel (busy cycles
            summed over SIMDs / (GPU-active cycles x SIMDs), GRBM_GUI_ACTIVE
            being summed over the XCDs) and MFMA / VALU instructions per launch
+  counters any counter CSVs (one per rocprofv3 pass) -> per-dispatch means of
+           a kernel's counters, per CU, and per CU and GPU-active cycle where
+           a pass also holds GRBM_GUI_ACTIVE
 
 The counters report KiB per dispatch; the copy calibration turns them into
 bytes whatever request granularity the counter assumes.
@@ -140,6 +143,35 @@ def cmd_mfma(a):
     print(text)
 
 
+def cmd_counters(a):
+    means, active = {}, None
+    for path in a.csv:
+        rows = [r for r in _rows(path) if re.search(a.kernel, r["Kernel_Name"])]
+        if not rows:
+            raise SystemExit(f"no dispatches of {a.kernel!r} in {path}")
+        per = {}
+        for r in rows:
+            per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        for k, v in per.items():
+            means[k] = statistics.mean(v[-a.last:] if a.last > 0 else v)
+    if "GRBM_GUI_ACTIVE" in means:
+        active = means["GRBM_GUI_ACTIVE"] / a.xcds
+    res = {"kernel": a.kernel, "workload": a.workload, "kernel_sha": source_sha(), "commands": a.command,
+           "counters_per_dispatch": means,
+           "per_cu": {k: v / a.cu_count for k, v in means.items() if k != "GRBM_GUI_ACTIVE"}}
+    if active:
+        res["active_cycles"] = active
+        res["per_cu_per_active_cycle"] = {k: v / a.cu_count / active for k, v in means.items()
+                                          if k != "GRBM_GUI_ACTIVE"}
+    if a.note:
+        res["note"] = a.note
+    text = json.dumps(res, indent=1)
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text + "\n")
+    print(text)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(prog="python -m paged_attention_decode_plan_amd.profiling")
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -173,6 +205,17 @@ def main(argv=None):
     m.add_argument("--command", default="")
     m.add_argument("--out")
     m.set_defaults(fn=cmd_mfma)
+    c = sub.add_parser("counters")
+    c.add_argument("--csv", required=True, nargs="+", help="counter_collection.csv of each counter pass")
+    c.add_argument("--kernel", default="pa_stream_kernel|pa_decode_kernel")
+    c.add_argument("--last", type=int, default=0, help="mean over the last N dispatches of each pass")
+    c.add_argument("--cu-count", type=int, default=256)
+    c.add_argument("--xcds", type=int, default=8)
+    c.add_argument("--workload", default="")
+    c.add_argument("--command", nargs="*", default=[])
+    c.add_argument("--note", default="")
+    c.add_argument("--out")
+    c.set_defaults(fn=cmd_counters)
     a = ap.parse_args(argv)
     a.fn(a)
 
