@@ -41,6 +41,9 @@ def _case(kind):
     if kind == "bf16":
         return W.make_dense_case(505, lens, query_len=4, num_q_heads=16, num_kv_heads=1, page_size=128,
                                  kv_dtype="bf16"), dict(cu_count=64)
+    if kind == "mxfp4":  # MXFP4 caches: 256-token partitions, 64 rows (8-wave tile kernel)
+        return W.make_dense_case(506, lens, query_len=4, num_q_heads=16, num_kv_heads=1, page_size=64,
+                                 kv_dtype="mxfp4", has_sinks=True), dict(cu_count=64)
     if kind == "sparse":  # the sparse decode shape: 4 partitions of 512 slots per row
         return W.config_sparse(num_rows=8, selected=2048, pool_pages=256), dict(partition_tokens=512)
     if kind == "sparse_topk":
@@ -48,7 +51,7 @@ def _case(kind):
     raise ValueError(kind)
 
 
-KINDS = ["tile16", "stream64", "stream32", "d256", "bf16", "sparse", "sparse_topk"]
+KINDS = ["tile16", "stream64", "stream32", "d256", "bf16", "mxfp4", "sparse", "sparse_topk"]
 
 
 def _with_queries(inp, k):

@@ -72,3 +72,23 @@ def test_static_scratch_matches_caller_buffers():
                        d["k_scale"], d["v_scale"], d["sinks"])
     torch.cuda.synchronize()
     assert np.array_equal(out.float().cpu().numpy(), e1)
+
+
+@pytest.mark.gpu
+def test_static_scratch_mxfp4_plans():
+    """MXFP4 caches (tile kernel, 256-token partitions): a multi-partition
+    plan, then a smaller one, each bit-identical to the caller-buffer path."""
+    big = W.make_dense_case(193, [7000, 3000, 300, 0], query_len=4, num_q_heads=16, num_kv_heads=1,
+                            page_size=64, kv_dtype="mxfp4", has_sinks=True)
+    small = W.make_dense_case(194, [700, 33], query_len=2, num_q_heads=8, num_kv_heads=1, page_size=32,
+                              kv_dtype="mxfp4", sliding_window=300)
+    announce("static scratch: MXFP4 multi-partition plan")
+    s1, e1, p1 = _run_both(big, cu_count=64)
+    assert p1.info().num_slots > 0
+    assert np.array_equal(s1, e1)
+    compare(s1, O.attend(big), "static scratch MXFP4, first call")
+    announce("static scratch: smaller MXFP4 plan")
+    s2, e2, p2 = _run_both(small, cu_count=64)
+    assert p2.meta_bytes + p2.workspace_bytes < p1.meta_bytes + p1.workspace_bytes
+    assert np.array_equal(s2, e2)
+    compare(s2, O.attend(small), "static scratch MXFP4, second call")
