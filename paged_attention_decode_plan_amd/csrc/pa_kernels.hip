@@ -1211,7 +1211,7 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(ReduceArgs a) {
   if (e.nparts < 2) return;  // a unit with one partition wrote its rows itself
   const MergeArgs ma{a.out, a.workspace, a.sinks, a.QL, a.Hq, a.G, a.rows_total, a.rows_per_group, a.q_fp16,
                      a.has_sinks};
-  merge_chunk<D>(ma, e, blockIdx.x % a.chunks_per_entry, wgt, rowf);
+  merge_chunk_any<D>(ma, e, blockIdx.x % a.chunks_per_entry, wgt, rowf);
 }
 
 // ---------------------------------------------------------------------------

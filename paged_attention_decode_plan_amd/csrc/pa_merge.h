@@ -15,6 +15,13 @@
 
 namespace pa {
 
+// acc + w * v per component as one fused multiply-add, whatever the code
+// around it: every merge variant rounds each partition's term the same way.
+__device__ __forceinline__ f4 merge_term(f4 acc, float w, const f4& v) {
+  return f4{__builtin_fmaf(w, v[0], acc[0]), __builtin_fmaf(w, v[1], acc[1]), __builtin_fmaf(w, v[2], acc[2]),
+            __builtin_fmaf(w, v[3], acc[3])};
+}
+
 struct MergeArgs {
   void* out;
   const float* workspace;
@@ -39,12 +46,16 @@ constexpr int merge_lds_bytes() { return (merge_wgt_floats<D>() + 64 + 4) * 4; }
 // Merges rows [chunk * RR, chunk * RR + RR) of unit e.  Every thread of the
 // workgroup must call it (it holds one barrier); threads 256 and up only take
 // part in the barrier.  wgt: RR * kMaxPartitions floats of LDS, rowf: RR.
-template <int D>
+// RCH: partitions whose loads are in flight per round trip.  The order of
+// the operations on each output does not depend on it.
+template <int D, int RCH>
 __device__ __forceinline__ void merge_chunk(const MergeArgs& a, const ReduceItem& e, int chunk, float* wgt,
                                             float* rowf) {
+  // no contraction of a*b+c into FMAs at the compiler's choice, which
+  // differs with the surrounding code: the fused operations are explicit
+#pragma clang fp contract(off)
   constexpr int RR = merge_rows<D>();
   constexpr int Q4 = D / 4;
-  constexpr int RCH = 16;  // partitions' loads in flight per round trip
   static_assert(RR * Q4 == 256, "one output per thread");
   const int tid = threadIdx.x;
   const bool act = tid < 256;
@@ -99,7 +110,7 @@ __device__ __forceinline__ void merge_chunk(const MergeArgs& a, const ReduceItem
         if (p < np) {
           const float wp = lv[x][k] > 0.f ? __builtin_amdgcn_exp2f(mv[x][k] - M) : 0.f;
           wgt[rw * kMaxPartitions + p] = wp;
-          den += wp * lv[x][k];
+          den = __builtin_fmaf(wp, lv[x][k], den);
         }
       }
       den = wave_sum(den);  // fixed-order sum of the denominator terms
@@ -110,7 +121,7 @@ __device__ __forceinline__ void merge_chunk(const MergeArgs& a, const ReduceItem
             const float sk = skv[x] * LOG2E;
             const float M2 = fmaxf(M, sk);
             const float sc = __builtin_amdgcn_exp2f(M - M2);
-            f = sc / (den * sc + __builtin_amdgcn_exp2f(sk - M2));
+            f = sc / __builtin_fmaf(den, sc, __builtin_amdgcn_exp2f(sk - M2));  // fused in every caller
           } else {
             f = 1.0f / den;
           }
@@ -139,7 +150,7 @@ __device__ __forceinline__ void merge_chunk(const MergeArgs& a, const ReduceItem
 #pragma unroll
       for (int j = 0; j < RCH; ++j) {
         const float wp = p0 + j < np ? wgt[rr * kMaxPartitions + p0 + j] : 0.f;
-        if (wp != 0.f) acc += wp * v[j];
+        if (wp != 0.f) acc = merge_term(acc, wp, v[j]);
       }
     }
   }
@@ -159,6 +170,17 @@ __device__ __forceinline__ void merge_chunk(const MergeArgs& a, const ReduceItem
       u32x2{(uint32_t)hv[0] | ((uint32_t)hv[1] << 16), (uint32_t)hv[2] | ((uint32_t)hv[3] << 16)};
 }
 
+// merge_chunk with the round-trip width chosen by the partition count (a
+// unit of up to 32 partitions in one round trip): the reducer's choice.
+template <int D>
+__device__ __forceinline__ void merge_chunk_any(const MergeArgs& a, const ReduceItem& e, int chunk, float* wgt,
+                                                float* rowf) {
+  if (e.nparts <= 16)
+    merge_chunk<D, 16>(a, e, chunk, wgt, rowf);
+  else
+    merge_chunk<D, 32>(a, e, chunk, wgt, rowf);
+}
+
 // The whole unit in one round trip to memory, for units of at most 64
 // partitions whose partial O fits SMALL_LOADS 16-byte loads per thread:
 // every thread loads all partitions of its outputs (output o = tid + 256 j,
@@ -173,6 +195,7 @@ __device__ __forceinline__ bool merge_fits_small(int nrows, int np) {
 }
 template <int D>
 __device__ __forceinline__ void merge_small(const MergeArgs& a, const ReduceItem& e, float* wgt, float* rowf) {
+#pragma clang fp contract(off)  // as in merge_chunk
   constexpr int Q4 = D / 4;
   const int tid = threadIdx.x;
   const bool act = tid < 256;
@@ -215,7 +238,7 @@ __device__ __forceinline__ void merge_small(const MergeArgs& a, const ReduceItem
       if (lane < np) {
         const float wp = lv[x] > 0.f ? __builtin_amdgcn_exp2f(mv[x] - M) : 0.f;
         wgt[rw * 64 + lane] = wp;
-        den += wp * lv[x];
+        den = __builtin_fmaf(wp, lv[x], den);
       }
       den = wave_sum(den);  // fixed-order sum of the denominator terms
       if (lane == 0) {
@@ -225,7 +248,7 @@ __device__ __forceinline__ void merge_small(const MergeArgs& a, const ReduceItem
             const float sk = skv[x] * LOG2E;
             const float M2 = fmaxf(M, sk);
             const float sc = __builtin_amdgcn_exp2f(M - M2);
-            f = sc / (den * sc + __builtin_amdgcn_exp2f(sk - M2));
+            f = sc / __builtin_fmaf(den, sc, __builtin_amdgcn_exp2f(sk - M2));  // fused in every caller
           } else {
             f = 1.0f / den;
           }
@@ -248,7 +271,7 @@ __device__ __forceinline__ void merge_small(const MergeArgs& a, const ReduceItem
       for (int k = 0; k < SMALL_LOADS; ++k) {
         if (k / np == j) {
           const float wp = wgt[r * 64 + k % np];
-          if (wp != 0.f) acc += wp * v[k];
+          if (wp != 0.f) acc = merge_term(acc, wp, v[k]);
         }
       }
     }
@@ -313,7 +336,7 @@ __device__ __forceinline__ void arrive_and_merge(const MergeArgs& ma, int* count
   }
   const int nchunks = (nrows + merge_rows<D>() - 1) / merge_rows<D>();
   for (int ch = 0; ch < nchunks; ++ch) {
-    merge_chunk<D>(ma, e, ch, wgt, rowf);
+    merge_chunk<D, 16>(ma, e, ch, wgt, rowf);
     __syncthreads();  // the chunk's weights read before the next chunk writes them
   }
 }

@@ -44,6 +44,9 @@ def _case(kind):
     if kind == "mxfp4":  # MXFP4 caches: 256-token partitions, 64 rows (8-wave tile kernel)
         return W.make_dense_case(506, lens, query_len=4, num_q_heads=16, num_kv_heads=1, page_size=64,
                                  kv_dtype="mxfp4", has_sinks=True), dict(cu_count=64)
+    if kind == "many_parts":  # a unit of 79 partitions: several round trips of the wider loads
+        return W.make_dense_case(507, [20000, 3000, 0], query_len=4, num_q_heads=16, num_kv_heads=1, page_size=128,
+                                 scale_mode="token", has_sinks=True), dict(partition_tokens=256, cu_count=256)
     if kind == "sparse":  # the sparse decode shape: 4 partitions of 512 slots per row
         return W.config_sparse(num_rows=8, selected=2048, pool_pages=256), dict(partition_tokens=512)
     if kind == "sparse_topk":
@@ -51,7 +54,7 @@ def _case(kind):
     raise ValueError(kind)
 
 
-KINDS = ["tile16", "stream64", "stream32", "d256", "bf16", "mxfp4", "sparse", "sparse_topk"]
+KINDS = ["tile16", "stream64", "stream32", "d256", "bf16", "mxfp4", "many_parts", "sparse", "sparse_topk"]
 
 
 def _with_queries(inp, k):
@@ -68,7 +71,7 @@ def test_in_kernel_merge_bit_exact(kind):
     inp, kw = _case(kind)
     red = B.Plan(B.problem_of(inp.problem), inp.context_lens, merge=B.MERGE_REDUCER, **kw).allocate("cuda")
     ikm = B.Plan(B.problem_of(inp.problem), inp.context_lens, merge=B.MERGE_IN_KERNEL, **kw).allocate("cuda")
-    assert ikm.info().max_parts > 1, "the case must have multi-partition units"
+    assert ikm.info().max_parts > (32 if kind == "many_parts" else 1), "the case must have multi-partition units"
     for k in range(3):
         case = _with_queries(inp, k)
         announce(f"in-kernel merge {kind} call {k}")
