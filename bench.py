@@ -432,9 +432,10 @@ def ceiling(args, dev):
     K = args.steps
     res = {"metric": "read bandwidth of the decode's KV access pattern (ceiling probes)", "workload": "dense_mtp4_fp8",
            "kv_bytes_per_call": kv_bytes, "work_items": n, "steps": K, "kernel_sha": source_sha()}
-    rounds = {"registers": [], "lds_ring": [], "decode": []}
+    rounds = {"registers": [], "registers_full_rows": [], "lds_ring": [], "decode": []}
     for _ in range(3):  # interleaved rounds, best of three
         rounds["registers"].append(region(lambda c: probe(0, c), K))
+        rounds["registers_full_rows"].append(region(lambda c: probe(2, c), K))
         rounds["lds_ring"].append(region(lambda c: probe(1, c), K))
         rounds["decode"].append(region(decode, K))
     for name, v in rounds.items():

@@ -14,6 +14,10 @@
 //   mode 1  an LDS ring: the workgroup copies each tile (K, V, scales) into
 //           one of three LDS stages with global_load_lds_dwordx4, waits for
 //           the oldest stage, reads it back from LDS;
+//   mode 2  mode 0 with V read as whole 128-byte rows: the same bytes per
+//           tile and per wave, but each V load instruction covers 8 full
+//           rows of the page instead of a 32-byte piece of 32 rows (in mode 0
+//           the four waves each read a quarter of every V row);
 // and pa_ceiling_read streams a contiguous buffer (the plain-read rate).
 #include <hip/hip_runtime.h>
 
@@ -60,6 +64,7 @@ struct Step {
   float sc;
 };
 
+template <bool FULL_ROWS>
 __global__ __launch_bounds__(256) void probe_registers(ProbeArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
   const Item it = item_of(a);
@@ -84,7 +89,12 @@ __global__ __launch_bounds__(256) void probe_registers(ProbeArgs a) {
       s.k[3] = *(const u32x4*)(kp + 5 * kcs);
       const uint8_t* vp = vb + pid * a.page_stride + slot + 16 * h;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) s.v[db] = *(const u32x4*)(vp + (32 * db + c32) * ps);
+      for (int db = 0; db < 4; ++db) {
+        if (FULL_ROWS)  // rows 32w + 8db .. +7 of the page, 16 bytes per lane
+          s.v[db] = *(const u32x4*)(vb + pid * a.page_stride + (32 * w + 8 * db + (lane >> 3)) * ps + 16 * (lane & 7));
+        else
+          s.v[db] = *(const u32x4*)(vp + (32 * db + c32) * ps);
+      }
       s.sc = sb[(pid * a.Hkv + it.kvh) * ps + slot + c32];
     };
     auto use = [&](const Step& s) {
@@ -221,7 +231,9 @@ extern "C" int pa_ceiling_gather(int mode, const void* k_cache, const void* v_ca
   a.page_size = page_size;
   a.table_stride = table_stride;
   if (mode == 0) {
-    hipLaunchKernelGGL(probe_registers, dim3(num_items), dim3(256), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(probe_registers<false>, dim3(num_items), dim3(256), 0, (hipStream_t)stream, a);
+  } else if (mode == 2) {
+    hipLaunchKernelGGL(probe_registers<true>, dim3(num_items), dim3(256), 0, (hipStream_t)stream, a);
   } else if (mode == 1) {
     static bool configured = false;
     if (!configured) {
