@@ -11,7 +11,8 @@
  *     L = context_lens[s];  pos = L - QL + i (causal) or L - 1;
  *     visible tokens t: 0 <= t < L, t <= pos, and t > pos - W when W > 0;
  *     out[s*QL+i, h, :] = softmax_t(softmax_scale * q . k_t  [+ sink_h]) v_t
- *   with k_t, v_t dequantised from paged caches (FP8 code * scale, or BF16),
+ *   with k_t, v_t dequantised from paged caches (FP8 code * scale, MXFP4
+ *   code * the power-of-two scale of its 32-element block, or BF16),
  *   a per-head sink logit joining the denominator only, and 0 for a row that
  *   sees no token.
  *

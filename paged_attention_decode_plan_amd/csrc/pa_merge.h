@@ -7,8 +7,10 @@
 //
 // One code path for both callers: the reducer kernel (one workgroup per
 // chunk of rows) and the last-arriving work item of a decode launch with the
-// in-kernel merge (the unit's chunks in turn).  Same threads, same order,
-// same operations: the two give bit-identical outputs.
+// in-kernel merge (the unit's chunks in turn, or a small unit at once).
+// Each output gets the same operations in the same order from either (how
+// many partitions' loads share a round trip differs, which changes no
+// value): the two give bit-identical outputs.
 #pragma once
 
 #include "pa_device.h"
