@@ -177,8 +177,11 @@ def cpu_baseline(inp, budget_s: float = 12.0):
 
 def kernel_of(p, info) -> str:
     """Which decode kernel the library launches for a plan (its dispatch rule)."""
-    if (p.kv_dtype == "fp8" and not p.token_table and info.rows_per_group > 16
-            and (p.head_dim == 128 or (p.head_dim == 256 and info.rows_per_group <= 32))):
+    if p.token_table or info.rows_per_group <= 16:
+        return "pa_decode_kernel"
+    if p.kv_dtype == "bf16" and p.head_dim == 128 and p.page_size >= 32:
+        return "pa_stream_kernel"
+    if p.kv_dtype == "fp8" and (p.head_dim == 128 or (p.head_dim == 256 and info.rows_per_group <= 32)):
         return "pa_stream_kernel"
     return "pa_decode_kernel"
 

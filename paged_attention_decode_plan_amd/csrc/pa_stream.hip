@@ -39,6 +39,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -73,11 +74,15 @@ struct StreamSmem {
 };
 
 // Step data of one wave, loaded NB - 1 steps ahead.
-template <int D>
+//   FP8:  k[ks] (64 dims): K chunks 4ks + 2h, 4ks + 2h + 1 (dims 64ks + 32h
+//         .. +31) of token kt; v[db]: V dim 32db + c32, tokens 16h .. 16h+15;
+//   BF16: k[ks] (16 dims): K chunk 2ks + h (dims 16ks + 8h .. +7) of token
+//         kt; v[2db + kb]: V dim 32db + c32, tokens 16h + 8kb .. +7.
+template <int D, bool BF>
 struct StepData {
-  i32x8 k[D / 64];  // k-step ks: K chunks 4ks + 2h, 4ks + 2h + 1 (dims 64ks + 32h .. +31) of token kt
-  u32x4 v[D / 32];  // V dim 32db + c32, tokens 16h .. 16h+15 of the step
-  float sc;         // lanes 0-31: k scale of token c32; lanes 32-63: v scale of token c32
+  typename std::conditional<BF, u32x4, i32x8>::type k[BF ? D / 16 : D / 64];
+  u32x4 v[BF ? D / 16 : D / 32];
+  float sc;  // lanes 0-31: k scale of token c32; lanes 32-63: v scale of token c32
 };
 
 
@@ -87,18 +92,22 @@ __device__ __forceinline__ i32x8 load32(const uint8_t* p0, const uint8_t* p1) {
 }
 
 // BIG: page size >= 32 (the 32 tokens of a step share one page).
-template <int D, int RB, bool PT, bool BIG>
+// BF: BF16 caches (head dim 128, pages of 32 tokens or more, no scales): QK
+// on v_mfma_f32_32x32x16_bf16 with the BF16 query and K as stored, PV on the
+// same instruction with V as stored against a two-term BF16 split of P.
+template <int D, int RB, bool PT, bool BIG, bool BF = false>
 __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   constexpr int TT = kTileTokens;
   using S = StreamSmem<D, RB>;
-  constexpr int NKS = D / 64;  // QK k-steps (64 dims each)
-  constexpr int NDB = D / 32;  // 32-dim blocks of V and O
-  // Load buffers per wave: three at head dim 128; two at 256, whose steps
-  // are twice the bytes (the same bytes in flight) and whose O accumulator
-  // is twice the registers.
-  constexpr int NB = D == 128 ? 3 : 2;
+  constexpr int NKS = BF ? D / 16 : D / 64;  // QK k-steps (64 dims each; BF16: 16)
+  constexpr int NDB = D / 32;                // 32-dim blocks of V and O
+  // Load buffers per wave: three at head dim 128 (FP8); two at 256 and for
+  // BF16 caches, whose steps are twice the bytes (the same bytes in flight)
+  // and, at 256, whose O accumulator is twice the registers.
+  constexpr int NB = (D == 128 && !BF) ? 3 : 2;
   static_assert(D == 128 || (D == 256 && RB == 1), "head dim 256 takes one 32-row block");
-  using SD = StepData<D>;
+  static_assert(!BF || (D == 128 && !PT && BIG), "BF16: head dim 128, no scales, pages of 32 tokens or more");
+  using SD = StepData<D, BF>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   float* obuf = (float*)smem;
   static_assert(merge_lds_bytes<D>() <= S::MERGE, "the in-kernel merge reuses the O buffers");
@@ -214,21 +223,27 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   };
   // Lane-constant parts of the addresses (page >= 32: a step lies in one page)
   const int slot_k = (32 * w + kt) & (ps - 1);
-  const uint32_t koff = (uint32_t)((2 * h * pps + slot_k) * 16);
+  // the lane's first K chunk: 2h (FP8: chunks 2h, 2h+1 of every 64 dims), h (BF16: chunk h of every 16 dims)
+  const uint32_t koff = (uint32_t)(((BF ? 1 : 2) * h * pps + slot_k) * 16);
   const uint32_t kcs = (uint32_t)pps * 16;  // K chunk stride
   const int slot_v = (32 * w + 16 * h) & (ps - 1);
+  // V: the lane's 16 tokens of dim 32db + c32 (BF16: two 16-byte halves,
+  // vkb apart)
+  constexpr int X = BF ? 8 : 16;  // tokens per 16-byte unit of transposed V
   uint32_t voff[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     const int dd = 32 * db + c32;
-    voff[db] = a.v_transposed ? (uint32_t)(((slot_v >> 4) * D + dd) * 16) : (uint32_t)(dd * pps + slot_v);
+    voff[db] = a.v_transposed ? (uint32_t)(((slot_v / X) * D + dd) * 16)
+                              : (uint32_t)((dd * pps + slot_v) * (BF ? 2 : 1));
   }
+  const uint32_t vkb = a.v_transposed ? (uint32_t)D * 16 : 16u;
   const uint32_t soff = (uint32_t)((kvh * pps + ((32 * w + c32) & (ps - 1))) * 4);
   // A (sub-)page id's place in the caches and scales: its page's block plus
   // the sub-page's offset (K: tokens in every chunk; plain V: columns of
   // every row; transposed V: its 16-token blocks; scales: tokens).
   const long msk = (1L << psub) - 1;
-  const long vsub_bytes = a.v_transposed ? (long)(ps >> 4) * D * 16 : (long)ps;
+  const long vsub_bytes = a.v_transposed ? (long)(ps / X) * D * 16 : (long)ps * (BF ? 2 : 1);
   auto kpage = [&](long id) { return (id >> psub) * a.page_stride + (id & msk) * ps * 16; };
   auto vpage = [&](long id) { return (id >> psub) * a.page_stride + (id & msk) * vsub_bytes; };
   const float* sbase = h ? a.v_scale : a.k_scale;
@@ -239,7 +254,11 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     long a, b;
   };
   auto load_k = [&](SD& d, StepPages id) {
-    if constexpr (BIG) {
+    if constexpr (BF) {
+      const uint8_t* kp = kbase + kpage(id.a);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) d.k[ks] = *(const u32x4*)(kp + koff + 2 * ks * kcs);
+    } else if constexpr (BIG) {
       const uint8_t* kp = kbase + kpage(id.a);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) d.k[ks] = load32(kp + koff + 4 * ks * kcs, kp + koff + (4 * ks + 1) * kcs);
@@ -259,7 +278,13 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     if constexpr (!PT) d.sc = 0.f;
   };
   auto load_v = [&](SD& d, StepPages id) {
-    if constexpr (BIG) {
+    if constexpr (BF) {
+      const uint8_t* vp = vbase + vpage(id.a);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) d.v[2 * db + kb] = *(const u32x4*)(vp + voff[db] + kb * vkb);
+    } else if constexpr (BIG) {
       const uint8_t* vp = vbase + vpage(id.a);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) d.v[db] = *(const u32x4*)(vp + voff[db]);
@@ -313,9 +338,24 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   // of k-step ks holds dims 64ks + 32h .. +31, the same dims as its K
   // operand; every wave then keeps all of the item's fragments in
   // accumulator registers.
+  // BF16 caches: the BF16 query as given, laid out alike in LDS ([RB][NKS
+  // ks][64 lanes][16 B]: lane half h of k-step ks holds dims 16ks + 8h ..
+  // +7, the same dims as its K operand); softmax_scale * log2(e) multiplies
+  // the accumulator.
   uint8_t* qlds = smem;  // [RB][NKS ks][2 terms][64 lanes][32 B]; the merge buffers reuse it after the loop
   int* qexp = (int*)(smem + RB * NKS * 2 * 64 * 32);  // [ROWS] E8M0 of the hi term
-  {
+  if constexpr (BF) {
+    const int r = q_r, qq = q_qq;
+    if (r < S::ROWS) {
+      const int rb = r >> 5;
+#pragma unroll
+      for (int part = 0; part < 4; ++part) {
+        const int ks = 2 * qq + (part >> 1), hh = part & 1;
+        *(u32x4*)(qlds + ((size_t)(rb * NKS + ks) * 64 + 32 * hh + (r & 31)) * 16) =
+            q_valid ? qraw[part] : u32x4{0, 0, 0, 0};
+      }
+    }
+  } else {
     const float cbase = a.scale_log2 * (PT ? 1.0f : a.k_scale[0]);
     const int r = q_r, qq = q_qq;
     float qv[32];
@@ -378,19 +418,29 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   }
   __syncthreads();
   int qsc[RB];
-  i32x8 qf[RB][NKS][2];
+  i32x8 qf[RB][BF ? 1 : NKS][2];
+  u32x4 qfb[RB][BF ? NKS : 1];  // BF16 query fragments
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    qsc[rb] = qexp[32 * rb + c32];
+    if constexpr (BF) {
+      qsc[rb] = 0;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const uint8_t* src = qlds + ((size_t)((rb * NKS + ks) * 2 + t) * 64 + lane) * 32;
-        const u32x4 lo = *(const u32x4*)src, hi = *(const u32x4*)(src + 16);
-        qf[rb][ks][t] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        asm volatile("" : "+a"(qf[rb][ks][t]));  // kept in accumulator registers for the whole loop
+      for (int ks = 0; ks < NKS; ++ks) {
+        qfb[rb][ks] = *(const u32x4*)(qlds + ((size_t)(rb * NKS + ks) * 64 + lane) * 16);
+        asm volatile("" : "+a"(qfb[rb][ks]));  // kept in accumulator registers for the whole loop
       }
+    } else {
+      qsc[rb] = qexp[32 * rb + c32];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint8_t* src = qlds + ((size_t)((rb * NKS + ks) * 2 + t) * 64 + lane) * 32;
+          const u32x4 lo = *(const u32x4*)src, hi = *(const u32x4*)(src + 16);
+          qf[rb][ks][t] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          asm volatile("" : "+a"(qf[rb][ks][t]));  // kept in accumulator registers for the whole loop
+        }
+    }
   }
 
   // ---- page ids of the item into LDS (the loop needs them from its fourth
@@ -411,7 +461,8 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     m_ref[rb] = valid[rb] ? -INFINITY : 0.f;
     m_hi[rb] = -INFINITY;
   }
-  const float vs_out = PT ? 1.0f : a.v_scale[0];
+  const float vs_out = (PT || BF) ? 1.0f : a.v_scale[0];
+  const float cbf = a.scale_log2;  // BF16: the score scale, applied to the accumulator
 
   float* ssl = sbuf + w * 64;  // this wave's scale slot
 
@@ -498,21 +549,35 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
 
     // V of the step; tokens outside the visible span get zero V (their bytes
     // may be anything, and 0 * NaN would reach O)
-    u32x4 vv[NDB];
+    constexpr int NVU = BF ? 2 * NDB : NDB;  // 16-byte V units of the lane
+    u32x4 vv[NVU];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) vv[db] = cur.v[db];
+    for (int u = 0; u < NVU; ++u) vv[u] = cur.v[u];
     if constexpr (gen) {
       const int va = min(max(span_lo - tl, 0), 16), vb = min(max(span_hi - tl, 0), 16);
+      if constexpr (BF) {
+        // unit 2db + kb, word q: tokens 8kb + 2q (low half) and 8kb + 2q + 1
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t m = 0;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int t = 4 * q + b;
-          if (t >= va && t < vb) m |= 0xFFu << (8 * b);
+          for (int q = 0; q < 4; ++q) {
+            const int t = 8 * kb + 2 * q;
+            const uint32_t m = ((t >= va && t < vb) ? 0xFFFFu : 0u) | ((t + 1 >= va && t + 1 < vb) ? 0xFFFF0000u : 0u);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) vv[2 * db + kb][q] &= m;
+          }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t m = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int t = 4 * q + b;
+            if (t >= va && t < vb) m |= 0xFFu << (8 * b);
+          }
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) vv[db][q] &= m;
         }
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) vv[db][q] &= m;
       }
     }
 
@@ -520,17 +585,25 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     // terms, each k-step with its own E8M0 scale
     auto qk = [&](int rb) {
       f32x16 acc = {};
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
+      if constexpr (BF) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
-          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.k[ks], qf[rb][ks][t], acc, 0, 0, 0, 127, 0,
-                                                                qsc[rb] - 4 * t);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cur.k[ks]),
+                                                        __builtin_bit_cast(bf16x8, qfb[rb][ks]), acc, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.k[ks], qf[rb][ks][t], acc, 0, 0, 0, 127, 0,
+                                                                  qsc[rb] - 4 * t);
+      }
       return acc;
     };
     // V in FP16 (times 2^E): k-block kb of dim 32db + c32 = tokens 16h + 8kb .. +7
     half8 vb[NDB][2];
     auto vcvt = [&]() {
+      if constexpr (BF) return;  // BF16 V enters the MFMA as stored
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -563,11 +636,15 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
 
     // probabilities of one row block -> PV operand (FP16); branch-free so
     // that the MFMAs of the other row block can be interleaved with it
-    auto probs = [&](int rb, const f32x16& sa, half8 (&pb)[2]) {
+    // PV operand: FP16 P (FP8 caches), or the two BF16 terms of P, hi in
+    // [0, 2) and lo in [2, 4) (BF16 caches)
+    using PF = typename std::conditional<BF, bf16x8, half8>::type;
+    constexpr int NPF = BF ? 4 : 2;
+    auto probs = [&](int rb, const f32x16& sa, PF (&pb)[NPF]) {
       float y[16];
       if constexpr (gen) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) y[i] = PT ? sa[i] * ks16[i] : sa[i];
+        for (int i = 0; i < 16; ++i) y[i] = BF ? sa[i] * cbf : PT ? sa[i] * ks16[i] : sa[i];
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -595,7 +672,7 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if constexpr (gen) y[i] = y[i] + nm;
-        else y[i] = PT ? __builtin_fmaf(sa[i], ks16[i], nm) : sa[i] + nm;
+        else y[i] = BF ? __builtin_fmaf(sa[i], cbf, nm) : PT ? __builtin_fmaf(sa[i], ks16[i], nm) : sa[i] + nm;
         y[i] = __builtin_amdgcn_exp2f(y[i]);  // exp2(-inf) = 0
       }
       float t8[8];
@@ -618,20 +695,39 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) y[i] *= vs16[i];
       }
+      if constexpr (BF) {
+        // P = hi + lo, each rounded to BF16 (about 16 significant bits)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        h2 c[4];
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int x = 0; x < 4; ++x) c[x] = __builtin_convertvector(f2{y[8 * kb + 2 * x], y[8 * kb + 2 * x + 1]}, h2);
-        pb[kb] = half8{c[0][0], c[0][1], c[1][0], c[1][1], c[2][0], c[2][1], c[3][0], c[3][1]};
+          for (int x = 0; x < 8; ++x) {
+            const __bf16 hi = (__bf16)y[8 * kb + x];
+            pb[kb][x] = hi;
+            pb[2 + kb][x] = (__bf16)(y[8 * kb + x] - (float)hi);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          h2 c[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) c[x] = __builtin_convertvector(f2{y[8 * kb + 2 * x], y[8 * kb + 2 * x + 1]}, h2);
+          pb[kb] = half8{c[0][0], c[0][1], c[1][0], c[1][1], c[2][0], c[2][1], c[3][0], c[3][1]};
+        }
       }
     };
-    auto pv = [&](int rb, const half8 (&pb)[2]) {
+    auto pv = [&](int rb, const PF (&pb)[NPF]) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[db][kb], pb[kb], o[rb][db], 0, 0, 0);
+        for (int kb = 0; kb < 2; ++kb) {
+          if constexpr (BF) {
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, vv[2 * db + kb]);
+            o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kb], o[rb][db], 0, 0, 0);
+            o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[2 + kb], o[rb][db], 0, 0, 0);
+          } else {
+            o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[db][kb], pb[kb], o[rb][db], 0, 0, 0);
+          }
+        }
     };
 
     // Schedule (one wave per SIMD, so the overlap has to come from within
@@ -645,13 +741,13 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
     // compiler interleaves the MFMAs with the VALU work (an interleave pinned
     // by hand, one MFMA per 8-16 VALU, measured 2 % slower).
     static_assert(RB == 1 || RB == 2, "one or two row blocks");
-    half8 p0[2];
+    PF p0[NPF];
     const f32x16 s0 = qk(0);
     vcvt();
     __builtin_amdgcn_sched_barrier(0);
-    load_v(cur, nid);  // this step's V is converted
+    load_v(cur, nid);  // this step's V is converted (BF16: copied to vv)
     if constexpr (RB == 2) {
-      half8 p1[2];
+      PF p1[NPF];
       const f32x16 s1 = qk(1);
       scales();
       probs(0, s0, p0);
@@ -875,20 +971,20 @@ __global__ __launch_bounds__(256) void pa_stream_kernel(KernelArgs a) {
   }
 }
 
-template <int D, int RB, bool PT, bool BIG>
+template <int D, int RB, bool PT, bool BIG, bool BF = false>
 static pa_status launch_stream_t(const KernelArgs& args, int nblocks, hipStream_t stream) {
   constexpr int bytes = StreamSmem<D, RB>::LAUNCH;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   static bool configured = false;
   if (!configured) {
-    if (hipFuncSetAttribute((const void*)pa_stream_kernel<D, RB, PT, BIG>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    if (hipFuncSetAttribute((const void*)pa_stream_kernel<D, RB, PT, BIG, BF>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             bytes) != hipSuccess) {
       (void)hipGetLastError();
       return set_error(PA_ERR_DEVICE, "hipFuncSetAttribute failed");
     }
     configured = true;
   }
-  hipLaunchKernelGGL((pa_stream_kernel<D, RB, PT, BIG>), dim3(nblocks), dim3(256), bytes, stream, args);
+  hipLaunchKernelGGL((pa_stream_kernel<D, RB, PT, BIG, BF>), dim3(nblocks), dim3(256), bytes, stream, args);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(PA_ERR_DEVICE, std::string("decode launch failed: ") + hipGetErrorString(err));
   return PA_OK;
@@ -896,12 +992,16 @@ static pa_status launch_stream_t(const KernelArgs& args, int nblocks, hipStream_
 
 bool stream_kernel_applies(const Plan& P) {
   const pa_problem& p = P.prob;
-  return p.kv_dtype == PA_FP8_E4M3FN && !p.token_table && P.rows_per_group > 16 && p.num_pages > 0 &&
-         (p.head_dim == 128 || (p.head_dim == 256 && P.rows_per_group <= 32));
+  if (p.token_table || P.rows_per_group <= 16 || p.num_pages <= 0) return false;
+  if (p.kv_dtype == PA_BF16) return p.head_dim == 128 && p.page_size >= 32;
+  return p.kv_dtype == PA_FP8_E4M3FN && (p.head_dim == 128 || (p.head_dim == 256 && P.rows_per_group <= 32));
 }
 
 template <int D, int RB>
 static pa_status launch_stream_rb(const Plan& P, const KernelArgs& args, int nblocks, hipStream_t stream) {
+  if constexpr (D == 128) {
+    if (P.prob.kv_dtype == PA_BF16) return launch_stream_t<D, RB, false, true, true>(args, nblocks, stream);
+  }
   const bool pt = P.prob.scale_mode == PA_SCALE_PER_TOKEN;
   if (P.prob.page_size >= 32)
     return pt ? launch_stream_t<D, RB, true, true>(args, nblocks, stream)
