@@ -1,12 +1,14 @@
-// gfx950 streaming decode kernel for FP8 caches, page tables, and work items
-// of 17..64 query rows (multi-token (MTP) verify rows times a GQA group):
-// head dim 128 with one 32-row block (RB = 1) or two (RB = 2), head dim 256
-// with one.
+// gfx950 streaming decode kernel for page tables and work items of 17..64
+// query rows (multi-token (MTP) verify rows times a GQA group): FP8 caches at
+// head dim 128 with one 32-row block (RB = 1) or two (RB = 2) and at head dim
+// 256 with one; BF16 caches at head dim 128 with pages of 32 tokens or more
+// (BF, at the end of this comment).
 //
 // Same method as the tile kernel (online softmax per partition, partials
-// merged by the reducer in a fixed order: aiter PR #4332 "Add paged-attention
-// Tile kernel" and aiter PR #7079, "Launch and reducer latency"; scale before
-// mask: aiter PR #6617), laid out differently for bandwidth:
+// merged in a fixed order by the reducer or by the unit's last-arriving work
+// item: aiter PR #4332 "Add paged-attention Tile kernel" and aiter PR #7079,
+// "Launch and reducer latency" and "Partition merges"; scale before mask:
+// aiter PR #6617), laid out differently for bandwidth:
 //
 //  * a workgroup has 4 waves and owns one work item; each 128-token tile of
 //    the item is cut into four 32-token steps and wave w takes step w of every
@@ -34,7 +36,11 @@
 //    largest V scale sets a power of two 2^E; V converts exactly to FP16 as
 //    v * 2^E, and each probability times its token's V scale * 2^-E (at most
 //    1 unless E hit its clamp) is rounded once to FP16 (11 significant bits);
-//    an operand that would reach 2^15 makes the wave restart.
+//    an operand that would reach 2^15 makes the wave restart;
+//  * BF16 caches: QK on v_mfma_f32_32x32x16_bf16 with K as stored against
+//    the BF16 query (staged once in LDS in the operand's lane order), PV on
+//    the same instruction with V as stored against a two-term BF16 split of
+//    the probabilities (hi, then the residual), two load buffers per wave.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
