@@ -247,9 +247,8 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(TopkArgs a) {
     }
     return i < n;
   };
-  auto position = [&](int i) -> int32_t { return MODE == TK_CAND ? crow_p[i] : base + i; };
-  auto emit = [&](uint32_t pos, int i, uint32_t key) {
-    out[pos] = position(i);
+  auto emit = [&](uint32_t pos, int32_t position, uint32_t key) {
+    out[pos] = position;
     if (MODE == TK_SEG) outk[pos] = key;
   };
 
@@ -258,6 +257,7 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(TopkArgs a) {
   // load is unconditional (an index past the elements reads the last one;
   // valid_at marks the slot), so all of them are in flight together.
   uint32_t key[TK_E];
+  int32_t cpos[MODE == TK_CAND ? TK_E : 1];  // candidates: their positions, loaded with the keys
   uint32_t vbits = 0;  // bit j: slot j holds an element of the batch
   const bool resident = n <= TK_CHUNK;  // one batch: its keys stay in registers through every pass
   auto load_keys = [&](int c0) {
@@ -267,6 +267,10 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(TopkArgs a) {
     if (MODE == TK_CAND) {
 #pragma unroll
       for (int j = 0; j < TK_E; ++j) key[j] = crow_k[min(c0 + tid + TK_T * j, n - 1)];
+      // the positions now, so that writing a selected candidate waits for
+      // no load of its own
+#pragma unroll
+      for (int j = 0; j < (MODE == TK_CAND ? TK_E : 0); ++j) cpos[j] = crow_p[min(c0 + tid + TK_T * j, n - 1)];
     } else {
       float v[TK_E];
 #pragma unroll
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(TopkArgs a) {
 
   if (MODE != TK_CAND && n <= K) {  // every element is taken
     if (MODE == TK_SEG) {
-      for (int i = tid; i < n; i += TK_T) emit(i, i, fkey(row[i]));
+      for (int i = tid; i < n; i += TK_T) emit(i, base + i, fkey(row[i]));
       if (tid == 0) a.ccount[r * a.segs + seg] = n;
     } else {
       for (int i = tid; i < K; i += TK_T) out[i] = i < n ? i : -1;
@@ -414,7 +418,7 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(TopkArgs a) {
         const uint32_t gt_before = scan[0][j * TK_W + w] + (uint32_t)__builtin_popcountll(bg & below);
         const uint32_t eq_before = scan[1][j * TK_W + w] + (uint32_t)__builtin_popcountll(be & below);
         const uint32_t pos = gt_before + min(eq_before, need);
-        if ((gt || (eq && eq_before < need)) && pos < (uint32_t)K) emit(pos, i, key[j]);
+        if ((gt || (eq && eq_before < need)) && pos < (uint32_t)K) emit(pos, MODE == TK_CAND ? cpos[j % (MODE == TK_CAND ? TK_E : 1)] : base + i, key[j]);
       }
     }
     run_gt += cg;
