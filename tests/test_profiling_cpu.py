@@ -92,3 +92,17 @@ def test_counters_per_cu_and_cycle(tmp_path):
     assert r["active_cycles"] == pytest.approx(500.0)
     # 64000 busy cycles over 256 CUs and 500 active cycles: half the time
     assert r["per_cu_per_active_cycle"]["TA_TA_BUSY_sum"] == pytest.approx(0.5)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 ends with a message before
+    any device work."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 1
+    assert "one GPU" in r.stderr and r.stdout == ""
