@@ -3,7 +3,7 @@ small synthetic CSVs whose answers are worked out by hand: the kernel-trace
 table and the mean over the last dispatches of the focus kernel, the
 copy-calibrated HBM traffic, the MFMA busy fraction and the per-CU counter
 rates.  These are the numbers the committed summaries and the bench line's
-traffic figure are made of."""
+traffic figure are made of.  Also: bench.py's refusal of more than one GPU."""
 
 from __future__ import annotations
 
